@@ -310,4 +310,5 @@ def layer_bwd(p: LayerParams, c: dict, dy, d: LayerDims):
     dx_norm, g["g_attn"] = rmsnorm_bwd(dxn, c["x"], p.g_attn, c["r1"])
     g["dx"] = R(dh + dx_norm)
     g["dqkv"] = dqkv
+    g["dh"] = dh
     return g

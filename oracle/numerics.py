@@ -10,10 +10,15 @@
   three GEMMs; linlog.top article, "吞吐量优化": torch._scaled_mm with dynamic tensorwise scales].
   The pages name the scheme, not its constants; the constants below are the reading taken:
     amax      = max |x| over the whole tensor
-    scale     = fl32(448 / max(amax, fl32(1e-12)))     (IEEE fp32 division)
+    ratio     = fl32(448 / max(amax, fl32(1e-12)))     (IEEE fp32 division)
+    scale     = 2^floor(log2(ratio))                   (the largest power of two <= ratio)
     q         = e4m3_RNE(clamp(fl32(x * scale), -448, 448))
-    inv_scale = fl32(1 / scale)
+    inv_scale = 1 / scale                              (exact)
   and a GEMM of quantised operands is dequantised as (sum of exact products) * inv_a * inv_b.
+  A power-of-two scale makes x * scale exact and keeps the scale unchanged when amax moves by a
+  rounding error (it changes only when amax crosses a power of two); an unrounded 448 / amax
+  would re-grid every element of the tensor whenever its single largest element changes by one
+  bf16 ulp.
 
 All arithmetic is float64; a float64 result of one fp32 op on fp32 operands, rounded once to
 fp32, is the correctly rounded fp32 result (53 >= 2*24 + 2), so the fp32 steps above are exact.
@@ -116,8 +121,10 @@ def quantize_tensorwise(x):
     """
     x = np.asarray(x, dtype=np.float64)
     amax = float(np.max(np.abs(x))) if x.size else 0.0
-    scale = float(f32(E4M3_MAX / max(amax, AMAX_FLOOR)))
-    inv_scale = float(f32(1.0 / scale))
+    ratio = float(f32(E4M3_MAX / max(amax, AMAX_FLOOR)))
+    _, e = np.frexp(ratio)                        # ratio = m * 2^e, 0.5 <= m < 1
+    scale = float(np.ldexp(1.0, int(e) - 1))
+    inv_scale = float(np.ldexp(1.0, 1 - int(e)))
     y = f32(x * scale)
     y = np.clip(y, -E4M3_MAX, E4M3_MAX)
     vals = e4m3_round(y)

@@ -105,7 +105,9 @@ def test_quantizer_golden_example():
 def _torch_quant(x32: np.ndarray):
     t = torch.from_numpy(x32)
     amax = t.abs().max()
-    scale = torch.tensor(448.0, dtype=torch.float32) / torch.clamp(amax, min=torch.tensor(1e-12, dtype=torch.float32))
+    ratio = torch.tensor(448.0, dtype=torch.float32) / torch.clamp(amax, min=torch.tensor(1e-12, dtype=torch.float32))
+    _, e = torch.frexp(ratio)
+    scale = torch.ldexp(torch.tensor(1.0), e - 1)
     q = (t * scale).clamp(-448, 448).to(torch.float8_e4m3fn)
     return q, scale.item(), (1.0 / scale).item()
 
@@ -124,10 +126,15 @@ def test_quantizer_matches_torch(std):
 def test_quantizer_degenerate_inputs():
     codes, vals, scale, inv = nu.quantize_tensorwise(np.zeros((4, 4)))
     assert np.all(codes == 0)
-    assert scale == float(np.float32(448.0 / np.float32(1e-12)))
-    # a single element equal to amax maps exactly to +-448
+    assert scale == 2.0 ** 48                        # 448 / 1e-12 = 4.48e14 in [2^48, 2^49)
+    # amax a power of two times 448/2^k maps exactly onto +-448; otherwise into [224, 448]
+    codes, vals, scale, inv = nu.quantize_tensorwise(np.array([[-3.5, 1.0, 2.0]]))
+    assert scale == 128.0 and vals[0, 0] == -448.0
     codes, vals, scale, inv = nu.quantize_tensorwise(np.array([[-3.0, 1.0, 2.0]]))
-    assert vals[0, 0] == -448.0
+    assert scale == 128.0 and vals[0, 0] == -384.0 and inv == 1.0 / 128
+    for amax in np.geomspace(1e-6, 1e6, 97):
+        _, v, sc, iv = nu.quantize_tensorwise(np.array([amax, -amax / 3]))
+        assert 224.0 <= v[0] <= 448.0 and sc * iv == 1.0 and np.log2(sc) == np.floor(np.log2(sc))
 
 
 def test_fp8_gemm_matches_torch_scaled_mm():
