@@ -1,0 +1,169 @@
+/*
+ * ll.h — C ABI of the little-lm training-step hot path on AMD Instinct MI355X (gfx950).
+ *
+ * One decoder layer of the little-lm 3.8B model, forward and backward, its FP8 e4m3 tensorwise
+ * quantiser, and the fused linear cross-entropy LM-head loss. The model is stated on the
+ * "hn.213312.xyz translation" page (section 设置 / Setup: RMSNorm, RoPE, GQA 24 query / 8 KV
+ * heads, relu^2 MLP, QK-norm, logit softcap, per-layer learnable residual scalars, ResFormer-style
+ * value embeddings) and on the "youdonthavefriends cost analysis" page (section "config
+ * appendix": hidden 3072, intermediate 12288 non-gated, head_dim 128, rope_theta 10000,
+ * rms_norm_eps 1e-6, vocab padded 50257 -> 50304, bf16, FP8 on, loss
+ * LigerFusedLinearCrossEntropyLoss(softcap=15.0)).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers to caller-owned memory, 16-byte aligned, row-major,
+ *     densely packed unless a leading dimension is given. The library never allocates device
+ *     memory and keeps no state between calls other than the text of the last error.
+ *   - `stream` is a hipStream_t (NULL = the default stream). All work is enqueued on it with no
+ *     host synchronisation; outputs are valid once the stream has reached the enqueued work.
+ *   - Every call validates its arguments before enqueuing anything and returns an ll_status.
+ *     A failed validation enqueues nothing. A launch failure returns LL_ERR_HIP; the HIP error
+ *     text is then in ll_last_error().
+ *   - Values that are not finite in the inputs, or token ids / targets out of range, give
+ *     unspecified results (they are not checked on the device).
+ *   - Calls that share a workspace, `saved` buffer or output on one stream run in order; the
+ *     caller must not run two calls that share such memory on different streams at once.
+ */
+#ifndef LL_H_
+#define LL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LL_OK = 0,
+  LL_ERR_INVALID_ARG = 1,   /* null pointer, bad shape or leading dimension, misaligned pointer */
+  LL_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. fp8 with fp32, head_dim not 64/128) */
+  LL_ERR_WORKSPACE = 3,     /* workspace or saved buffer smaller than the size query returns */
+  LL_ERR_HIP = 4            /* HIP launch/runtime error; see ll_last_error() */
+} ll_status;
+
+typedef enum { LL_F32 = 0, LL_BF16 = 1 } ll_dtype;
+
+/* Static shape and precision of one decoder layer. */
+typedef struct {
+  int32_t dtype;            /* ll_dtype of activations and weight matrices */
+  int32_t fp8_mlp;          /* 1: the three GEMMs of each MLP linear take e4m3 operands (LL_BF16 only) */
+  int64_t batch, seq;       /* tokens = batch * seq; positions restart at 0 in every batch row */
+  int32_t d_model;          /* D */
+  int32_t n_q_heads;        /* Hq */
+  int32_t n_kv_heads;       /* Hkv; Hq must be a multiple of Hkv (q head h reads kv head h / (Hq/Hkv)) */
+  int32_t head_dim;         /* Dh: 64 or 128 */
+  int32_t d_ff;             /* F (4 * D in the model) */
+  float rms_eps;            /* 1e-6: block RMSNorms and QK-norm */
+  float rope_theta;         /* 10000 */
+  int32_t has_value_embed;  /* 1 on value-embedding layers (v += ve_table[token_ids]) */
+  int64_t ve_rows;          /* rows of ve_table (padded vocabulary, 50304) */
+} ll_layer_cfg;
+
+/* Parameters of one layer (read only). Matrices are in cfg.dtype; gains and scalars are fp32. */
+typedef struct {
+  const void* attn_norm_w;   /* fp32 [D]: gain of the pre-attention RMSNorm */
+  const void* w_qkv;         /* [(Hq + 2 Hkv) * Dh, D]: q rows, then k rows, then v rows, head-major */
+  const void* w_o;           /* [D, Hq * Dh] */
+  const void* mlp_norm_w;    /* fp32 [D]: gain of the pre-MLP RMSNorm */
+  const void* w_fc;          /* [F, D] */
+  const void* w_proj;        /* [D, F] */
+  const void* ve_table;      /* [ve_rows, Hkv * Dh] in cfg.dtype, or NULL when !has_value_embed */
+  const float* resid_attn;   /* device fp32 scalar a_attn:  h = x + a_attn * attention branch */
+  const float* resid_mlp;    /* device fp32 scalar a_mlp:   y = h + a_mlp * MLP branch */
+} ll_layer_params;
+
+/* Gradients of one layer. Matrices are written (overwritten) in cfg.dtype; gains and scalars are
+ * written in fp32; ve_table is ACCUMULATED into (fp32, the caller zeroes it once per step). */
+typedef struct {
+  void* attn_norm_w;   /* fp32 [D] */
+  void* w_qkv;
+  void* w_o;
+  void* mlp_norm_w;    /* fp32 [D] */
+  void* w_fc;
+  void* w_proj;
+  float* ve_table;     /* fp32 [ve_rows, Hkv * Dh] or NULL */
+  float* resid_attn;   /* fp32 scalar */
+  float* resid_mlp;    /* fp32 scalar */
+} ll_layer_grads;
+
+/* Bytes of the opaque `saved` buffer that ll_layer_fwd fills and ll_layer_bwd reads, and of the
+ * scratch workspace either call needs. Return 0 if cfg is invalid. */
+size_t ll_layer_saved_bytes(const ll_layer_cfg* cfg);
+size_t ll_layer_workspace_bytes(const ll_layer_cfg* cfg);
+
+/* Forward of one decoder layer [hn.213312.xyz translation, 设置 / Setup; youdonthavefriends cost
+ * analysis, "config appendix"]:
+ *   xn = RMSNorm(x) g1;  [q|k|v] = xn W_qkv^T;  v += ve_table[token_ids] (value-embedding layers);
+ *   q^ = RoPE(QKnorm(q)), k^ = RoPE(QKnorm(k));  o = causal softmax(q^ k^T / sqrt(Dh)) v (GQA);
+ *   h = x + a_attn (o W_o^T);  hn = RMSNorm(h) g2;  y = h + a_mlp (relu(hn W_fc^T)^2 W_proj^T),
+ * with the MLP GEMMs on dynamically quantised e4m3 operands when cfg.fp8_mlp.
+ *   x, y: [batch * seq, D] in cfg.dtype (y must not alias x).  token_ids: int32 [batch * seq]
+ *   (required on value-embedding layers, else may be NULL).  saved: >= ll_layer_saved_bytes.
+ *   ws: >= ll_layer_workspace_bytes. */
+int ll_layer_fwd(const ll_layer_cfg* cfg, const ll_layer_params* p, const void* x,
+                 const int32_t* token_ids, void* y, void* saved, size_t saved_bytes, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/* Backward of one decoder layer, given dy = dL/dy [batch * seq, D] (cfg.dtype) and the `saved`
+ * buffer of the matching ll_layer_fwd call (same cfg, params, x and token_ids). Writes
+ * dx = dL/dx [batch * seq, D] (must not alias dy or x) and the gradients in `g`. The FP8 path
+ * quantises dL/dm and dL/du and runs the two backward GEMMs of each MLP linear (input gradient,
+ * weight gradient) on e4m3 operands, straight-through [hn.213312.xyz translation, 提升吞吐量 /
+ * Increasing throughput: three FP8 GEMMs, one forward and two backward]. */
+int ll_layer_bwd(const ll_layer_cfg* cfg, const ll_layer_params* p, const void* x,
+                 const int32_t* token_ids, const void* saved, size_t saved_bytes, const void* dy,
+                 void* dx, const ll_layer_grads* g, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of ll_fused_lce_fwd_bwd for these sizes (0 if invalid). */
+size_t ll_fused_lce_workspace_bytes(int32_t dtype, int64_t n, int32_t d, int64_t v, int64_t token_chunk);
+
+/* Fused linear cross-entropy with tanh logit softcap [youdonthavefriends cost analysis,
+ * "Increasing throughput" and "config appendix"; hn.213312.xyz translation, 提升吞吐量: the LM
+ * head matmul is chunked inside the loss and the (n, v) logits are never materialised]:
+ *   z = hidden weight^T, c = softcap tanh(z / softcap), lse_i = log sum_j exp(c_ij),
+ *   loss = mean over rows with targets_i != ignore_index of (lse_i - c_{i, targets_i}),
+ *   dz = grad_scale / n_valid (softmax(c) - onehot) (1 - (c / softcap)^2),
+ *   d_hidden = dz weight, d_weight = dz^T hidden.
+ *   dtype: LL_F32 or LL_BF16 for hidden, weight, d_hidden, d_weight.
+ *   hidden [n, d], weight [v, d] (all v rows take part in the softmax, padded rows included),
+ *   targets int32 [n] in [0, v) or == ignore_index.  token_chunk: rows per chunk (memory of the
+ *   per-chunk logits is token_chunk * v * 6 bytes of ws); 0 picks a default.
+ *   loss: device fp32 scalar (0 if no row is valid).  lse: device fp32 [n] or NULL.
+ *   d_hidden [n, d] and d_weight [v, d]: both NULL (forward only) or both non-NULL (overwritten).
+ *   Requires d % 64 == 0 (bf16) / d % 32 == 0 (fp32), v % 8 == 0. */
+int ll_fused_lce_fwd_bwd(int32_t dtype, const void* hidden, const void* weight,
+                         const int32_t* targets, int64_t n, int32_t d, int64_t v, float softcap,
+                         int32_t ignore_index, float grad_scale, int64_t token_chunk, float* loss,
+                         float* lse, void* d_hidden, void* d_weight, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Workspace bytes of ll_fp8_quant_tensorwise (a few bytes for the amax). */
+size_t ll_fp8_quant_workspace_bytes(void);
+
+/* Dynamic tensorwise e4m3fn quantisation of x [rows, cols] (leading dimension ld >= cols, a
+ * multiple of 8; cols a multiple of 16; elements of in_dtype) [linlog.top article, 吞吐量优化:
+ * torch._scaled_mm with dynamic tensorwise scaling; the constants are this library's reading]:
+ *   amax = max|x|;  scale = 2^floor(log2(fl32(448 / max(amax, 1e-12))));  inv_scale = 1 / scale;
+ *   q = e4m3fn_round_nearest_even(clamp(fl32(x * scale), -448, 448)).
+ * The power-of-two scale keeps x * scale exact and does not move when amax changes by a rounding
+ * error, so two implementations that agree up to rounding pick the same scale.
+ * q: uint8 [rows, cols] or NULL; q_t: uint8 [cols, rows] (the transpose) or NULL; scale and
+ * inv_scale: device fp32 scalars. Results are bit-exact and independent of launch order. */
+int ll_fp8_quant_tensorwise(int32_t in_dtype, const void* x, int64_t rows, int64_t cols,
+                            int64_t ld, uint8_t* q, uint8_t* q_t, float* scale, float* inv_scale,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Text of a status code, and a description of the last error raised by this library in the
+ * calling thread (empty if none). */
+const char* ll_status_string(int status);
+const char* ll_last_error(void);
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int ll_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LL_H_ */

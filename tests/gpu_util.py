@@ -1,0 +1,54 @@
+"""Helpers of the GPU parity tests: device upload/download and tolerance checks."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_train_step_amd as ll
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ll._lib.lib()          # raises if libll.so is missing: no fallback
+
+
+def dev(a, dtype="bf16"):
+    """numpy (float32 values already representable in dtype, or ints) -> device tensor."""
+    a = np.ascontiguousarray(a)
+    if a.dtype.kind in "iu":
+        return torch.from_numpy(a).cuda()
+    t = torch.from_numpy(a.astype(np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.cuda()
+
+
+def host(t) -> np.ndarray:
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.float()
+    return t.detach().cpu().numpy().astype(np.float64) if t.is_floating_point() else t.detach().cpu().numpy()
+
+
+def rel_err(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def assert_close(got, ref, rtol, name="", elem_rtol=None):
+    """Norm-wise relative error <= rtol, and elementwise |got - ref| <= k*rtol*(|ref| + rms(ref))."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    e = rel_err(got, ref)
+    assert e <= rtol, f"{name}: norm-wise relative error {e:.3e} > {rtol:.1e}"
+    k = elem_rtol if elem_rtol is not None else 10 * rtol
+    rms = np.sqrt(np.mean(ref * ref)) if ref.size else 0.0
+    bad = np.abs(got - ref) > k * (np.abs(ref) + rms)
+    assert not np.any(bad), (f"{name}: {int(bad.sum())} elements beyond {k:.1e} x (|ref| + rms); "
+                             f"first at {np.argwhere(bad)[0]}: got {got[tuple(np.argwhere(bad)[0])]}, "
+                             f"ref {ref[tuple(np.argwhere(bad)[0])]}")

@@ -1,0 +1,122 @@
+"""GPU parity of the whole decoder layer (ll_layer_fwd / ll_layer_bwd) and of the fused linear
+cross-entropy (ll_fused_lce_fwd_bwd) against the oracle, on seeded synthetic inputs.
+
+Tolerances (norm-wise relative error per tensor): 1e-5 for the fp32 tiny configuration, 2e-2 for
+bf16 / FP8 configurations. The residual-scalar gradients are sums of N*D products that cancel, so
+their bound is 2 * rtol * |a| |b| (the error a norm-wise rtol in each factor can cause)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import lce as olce
+from tests.gpu_util import assert_close, need_gpu
+from tests.layer_cases import GRAD_KEYS, run_gpu, run_oracle
+from transformer_train_step_amd.ops import FusedLCE
+
+pytestmark = pytest.mark.gpu
+
+
+def _compare(gpu, ref, rtol, elem_rtol):
+    for k in ("y", "dx") + GRAD_KEYS + ("d_head",):
+        if k not in ref:
+            continue
+        if k == "ve_table":
+            # sparse: only rows named by the token ids receive gradient; the rest stay exactly 0
+            rows = np.unique(gpu["ids"])
+            untouched = np.ones(ref[k].shape[0], bool)
+            untouched[rows] = False
+            assert not np.any(gpu[k][untouched]), "value-embedding rows without a token were written"
+            assert_close(gpu[k][rows], ref[k][rows], rtol, k, elem_rtol=elem_rtol)
+        elif isinstance(ref[k], float):
+            # a_attn = sum(dh * attn_out), a_mlp = sum(dy * m) cancel heavily; their error is bounded
+            # by |d(a)| <= |da|.|b| + |a|.|db| <= 2 rtol |a||b| when a, b agree to rtol norm-wise
+            scale = ref["scale_" + k]
+            assert abs(gpu[k] - ref[k]) <= 2 * rtol * scale, (k, gpu[k], ref[k], scale)
+        else:
+            assert_close(gpu[k], ref[k], rtol, k, elem_rtol=elem_rtol)
+    if "loss" in ref:
+        assert abs(gpu["loss"] - ref["loss"]) <= rtol * abs(ref["loss"]), (gpu["loss"], ref["loss"])
+
+
+def test_tiny_fp32_layer_chained_into_lce():
+    """The tiny fp32 configuration (d 256, 4q/2kv x 64, F 1024, VE 512 x 128, vocab 512, 2 x 128
+    tokens): layer -> fused LCE (softcap 15) -> layer backward, everything at 1e-5."""
+    need_gpu()
+    s = synth.TINY_FP32
+    inp = synth.layer_inputs(s, seed=0, perturb=True)
+    w_head = synth.normal((s.vocab, s.d_model), 0.02, 0, synth.K_WHEAD, "fp32")
+    targets = synth.uniform_ints((s.tokens,), s.real_vocab, 0, synth.K_TARGETS)
+    print("tiny fp32 layer + LCE", flush=True)
+    gpu = run_gpu(inp, lce_head=(w_head, targets))
+    ref = run_oracle(inp, lce_head=(w_head, targets))
+    _compare(gpu, ref, 1e-5, 1e-3)
+
+
+@pytest.mark.parametrize("batch,seq,fp8,ve,seed", [
+    (2, 200, True, True, 1),        # ragged: 400 tokens, T not a multiple of 64
+    (1, 130, False, False, 2),      # bf16 MLP without FP8
+    (3, 64, True, False, 3),
+])
+def test_layer_bf16_real_dims(batch, seq, fp8, ve, seed):
+    """d_model 3072, 24q/8kv x 128, F 12288 (the 3.8B layer) at a few hundred tokens."""
+    need_gpu()
+    s = synth.LayerShape(batch=batch, seq=seq, fp8_mlp=fp8, value_embed=ve)
+    inp = synth.layer_inputs(s, seed=seed, perturb=True)
+    print(f"layer bf16 B={batch} T={seq} fp8={fp8} ve={ve}", flush=True)
+    gpu = run_gpu(inp)
+    ref = run_oracle(inp)
+    _compare(gpu, ref, 2e-2, 0.5)
+
+
+def test_tiny_fp32_layer_ragged_and_single_token():
+    need_gpu()
+    for b, t in ((3, 37), (1, 1)):
+        s = synth.LayerShape(batch=b, seq=t, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, d_ff=1024,
+                             vocab=512, real_vocab=512, dtype="fp32", fp8_mlp=False, value_embed=True)
+        inp = synth.layer_inputs(s, seed=5, perturb=True)
+        print(f"tiny fp32 B={b} T={t}", flush=True)
+        _compare(run_gpu(inp), run_oracle(inp), 1e-5, 1e-3)
+
+
+# ------------------------------------------------------------------ fused linear cross-entropy
+@pytest.mark.parametrize("n,d,v,chunk,dtype,ignored", [
+    (300, 3072, 50304, 128, "bf16", 7),     # LM-head shape, 3 chunks with a ragged last chunk
+    (256, 256, 512, 0, "fp32", 0),
+    (97, 256, 520, 40, "fp32", 3),
+])
+def test_fused_lce_parity(n, d, v, chunk, dtype, ignored):
+    need_gpu()
+    inp = synth.lce_inputs(n, d, v, min(v, 50257), dtype=dtype, seed=n, n_ignored=ignored)
+    print(f"lce n={n} d={d} v={v} chunk={chunk} {dtype}", flush=True)
+    lce = FusedLCE(dtype, n, d, v, chunk)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    H = torch.from_numpy(inp.hidden).to(tdt).cuda()
+    W = torch.from_numpy(inp.weight).to(tdt).cuda()
+    y = torch.from_numpy(inp.targets).cuda()
+    lse = torch.empty(n, dtype=torch.float32, device="cuda")
+    loss, dh, dw = lce(H, W, y, grad_scale=0.5, lse=lse)
+    torch.cuda.synchronize()
+    ref = olce.lce_fwd_bwd(inp.hidden, inp.weight, inp.targets, grad_scale=0.5, mode=dtype)
+    rtol = 1e-5 if dtype == "fp32" else 2e-2
+    assert abs(loss.item() - ref["loss"]) <= (1e-5 if dtype == "fp32" else 1e-4) * abs(ref["loss"])
+    assert_close(lse.cpu().numpy(), ref["lse"], 1e-6 if dtype == "fp32" else 1e-5, "lse", elem_rtol=1e-4)
+    assert_close(dh.float().cpu().numpy(), ref["dh"], rtol, "d_hidden", elem_rtol=max(10 * rtol, 1e-3))
+    assert_close(dw.float().cpu().numpy(), ref["dw"], rtol, "d_weight", elem_rtol=max(10 * rtol, 1e-3))
+
+
+def test_fused_lce_forward_only_and_empty():
+    need_gpu()
+    inp = synth.lce_inputs(64, 256, 512, 512, dtype="fp32", seed=9)
+    lce = FusedLCE("fp32", 64, 256, 512)
+    loss, _, _ = lce(torch.from_numpy(inp.hidden).cuda(), torch.from_numpy(inp.weight).cuda(),
+                     torch.from_numpy(inp.targets).cuda(), grads=False)
+    ref = olce.lce_fwd_bwd(inp.hidden, inp.weight, inp.targets, mode="fp32", need_grads=False)
+    assert math.isclose(loss.item(), ref["loss"], rel_tol=1e-5)
+    # all rows ignored: loss 0 and zero gradients
+    y = torch.full((64,), -100, dtype=torch.int32, device="cuda")
+    loss, dh, dw = lce(torch.from_numpy(inp.hidden).cuda(), torch.from_numpy(inp.weight).cuda(), y)
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0 and not dh.any().item() and not dw.any().item()

@@ -1,0 +1,121 @@
+// Shared device helpers of the gfx950 kernels: bf16 and e4m3fn conversions, 16-byte vector
+// types, wave reductions and small launch utilities. Internal to libll.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ll {
+
+// ------------------------------------------------------------------ element types
+struct bf16 { uint16_t u; };          // storage type of bf16 tensors
+typedef uint8_t fp8;                   // e4m3fn byte
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Round a finite fp32 to the nearest bf16, ties to even.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float round_bf(float f) { return bf2f(f2bf(f)); }
+
+// Load / store one element of a storage type as fp32; store rounds (RNE) for bf16.
+template <class T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr bool kIsBf16 = false;
+  __device__ __forceinline__ static float ld(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void st(float* p, int64_t i, float v) { p[i] = v; }
+  __device__ __forceinline__ static float rnd(float v) { return v; }
+};
+template <> struct Elem<bf16> {
+  static constexpr bool kIsBf16 = true;
+  __device__ __forceinline__ static float ld(const bf16* p, int64_t i) { return bf2f(p[i].u); }
+  __device__ __forceinline__ static void st(bf16* p, int64_t i, float v) { p[i].u = f2bf(v); }
+  __device__ __forceinline__ static float rnd(float v) { return round_bf(v); }
+};
+
+// 8 consecutive elements <-> 8 floats (16 B for bf16, 32 B for fp32).
+template <class T> struct Vec8;
+template <> struct Vec8<bf16> {
+  __device__ __forceinline__ static void load(const bf16* p, float (&v)[8]) {
+    uint4 r = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = __uint_as_float(w[i] << 16); v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u); }
+  }
+  __device__ __forceinline__ static void store(bf16* p, const float (&v)[8]) {
+    uint4 r;
+    r.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    r.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    r.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+    r.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+    *reinterpret_cast<uint4*>(p) = r;
+  }
+};
+template <> struct Vec8<float> {
+  __device__ __forceinline__ static void load(const float* p, float (&v)[8]) {
+    float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ static void store(float* p, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+// ------------------------------------------------------------------ e4m3fn
+// Round a finite fp32 with |v| <= 448 to the nearest e4m3fn code, ties to even. Written from the
+// OCP E4M3 definition: bias 7, 3 mantissa bits, subnormal quantum 2^-9, largest finite 448.
+// For |v| >= 2^-6 the code is the fp32 pattern rebiased (exponent -120) with the mantissa
+// rounded from 23 to 3 bits; below 2^-6 it is |v| / 2^-9 rounded to an integer 0..8 (8 being
+// the smallest normal 2^-6, code 0x08).
+__device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x3C800000u) {                      // |v| >= 2^-6: normal
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);  // RNE at mantissa bit 20
+    code = ((r >> 20) - (120u << 3)) & 0x7Fu;       // exponent 127 -> 7
+  } else {                                     // subnormal: k = rne(|v| * 2^9), 0 <= k <= 8
+    float s = __uint_as_float(a) * 512.0f;     // exact (power-of-two scaling, |v| < 2^-6)
+    code = (uint32_t)__builtin_rintf(s);       // rintf: ties to even
+  }
+  return (uint8_t)(sign | code);
+}
+
+// Decode an e4m3fn code (finite codes only) to fp32.
+__device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
+  uint32_t e = (c >> 3) & 0xF, m = c & 7;
+  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80) ? -mag : mag;
+}
+
+// ------------------------------------------------------------------ reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// atomic max of a non-negative float through its bit pattern (monotone for v >= 0)
+__device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
+  atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+}
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Blocks are dispatched round-robin over the 8 XCDs of MI355X (block b runs on XCD b % 8), each
+// XCD with its own L2. Renumber so that consecutive logical tiles land on the same XCD.
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+  const int x = b & 7, i = b >> 3, q = nb >> 3, r = nb & 7;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
+}  // namespace ll

@@ -1,0 +1,470 @@
+// ll_layer_fwd / ll_layer_bwd: one little-lm decoder layer [hn.213312.xyz translation, 设置 /
+// Setup; youdonthavefriends cost analysis, "config appendix"], as a fixed sequence of launches on
+// the caller's stream. Every GEMM is C = A B^T with both operands K-contiguous; the operands a
+// GEMM needs K-contiguous along the token axis (weight gradients) are produced transposed by their
+// producer (the e4m3 quantiser) or by a transpose kernel, with the token axis padded to a
+// multiple of 128 and zero-filled.
+#include "api.h"
+#include "attn.h"
+#include "gemm.h"
+#include "norm.h"
+#include "quant.h"
+
+using namespace ll;
+
+namespace {
+
+struct Dims {
+  int64_t B, T, N, Np, Tp;
+  int D, Hq, Hkv, DH, F, QD, KVD, QKVD, vcol0;
+  bool fp8, bf, ve;
+  int es;
+  float eps, theta;
+};
+
+int make_dims(const ll_layer_cfg* c, Dims& d) {
+  LL_CHECK(c, LL_ERR_INVALID_ARG, "cfg must not be null");
+  LL_CHECK(c->dtype == LL_F32 || c->dtype == LL_BF16, LL_ERR_INVALID_ARG, "cfg.dtype must be LL_F32 or LL_BF16");
+  LL_CHECK(c->batch >= 0 && c->seq >= 0, LL_ERR_INVALID_ARG, "batch and seq must be >= 0");
+  LL_CHECK(c->d_model > 0 && c->n_q_heads > 0 && c->n_kv_heads > 0 && c->head_dim > 0 && c->d_ff > 0,
+           LL_ERR_INVALID_ARG, "dimensions must be positive");
+  LL_CHECK(c->n_q_heads % c->n_kv_heads == 0, LL_ERR_INVALID_ARG, "n_q_heads must be a multiple of n_kv_heads");
+  LL_CHECK(!(c->fp8_mlp && c->dtype != LL_BF16), LL_ERR_UNSUPPORTED, "fp8_mlp requires LL_BF16");
+  LL_CHECK(c->head_dim == (c->dtype == LL_BF16 ? 128 : 64), LL_ERR_UNSUPPORTED,
+           "head_dim must be 128 (bf16) or 64 (fp32)");
+  LL_CHECK(c->d_model % 128 == 0 && c->d_ff % 128 == 0 && c->d_model <= 4096, LL_ERR_UNSUPPORTED,
+           "d_model and d_ff must be multiples of 128, d_model <= 4096");
+  LL_CHECK((int64_t)c->n_q_heads * c->head_dim % 32 == 0, LL_ERR_UNSUPPORTED, "n_q_heads * head_dim % 32 != 0");
+  LL_CHECK(c->rms_eps >= 0.f && c->rope_theta > 0.f, LL_ERR_INVALID_ARG, "rms_eps >= 0, rope_theta > 0");
+  LL_CHECK(!c->has_value_embed || c->ve_rows > 0, LL_ERR_INVALID_ARG, "ve_rows must be > 0 on value-embedding layers");
+  LL_CHECK(c->batch * c->seq < ((int64_t)1 << 31) / 64, LL_ERR_UNSUPPORTED, "too many tokens");
+  d.B = c->batch; d.T = c->seq; d.N = d.B * d.T;
+  d.Np = round_up(d.N, 128); d.Tp = round_up(d.T, 64);
+  d.D = c->d_model; d.Hq = c->n_q_heads; d.Hkv = c->n_kv_heads; d.DH = c->head_dim; d.F = c->d_ff;
+  d.QD = d.Hq * d.DH; d.KVD = d.Hkv * d.DH; d.QKVD = d.QD + 2 * d.KVD; d.vcol0 = d.QD + d.KVD;
+  d.fp8 = c->fp8_mlp != 0; d.bf = c->dtype == LL_BF16; d.ve = c->has_value_embed != 0;
+  d.es = d.bf ? 2 : 4; d.eps = c->rms_eps; d.theta = c->rope_theta;
+  return LL_OK;
+}
+
+// ---------------------------------------------------------------- saved (fwd -> bwd)
+struct Saved {
+  void *xn, *qkv, *qh, *kh, *o, *attn_out, *h, *u, *m, *hn, *r;
+  float *r1, *r2, *rq, *rk, *lse;
+  uint8_t *hn8, *hn8t, *r8t, *w18, *w18t, *w28, *w28t;
+  QScale* qs;          // [4]: hn, w1, r, w2
+};
+enum { QS_HN = 0, QS_W1 = 1, QS_R = 2, QS_W2 = 3 };
+
+size_t carve_saved(void* base, const Dims& d, Saved& s) {
+  Carver c(base);
+  const size_t e = d.es;
+  s.qs = c.take<QScale>(4);
+  s.xn = c.take<char>(d.N * d.D * e);
+  s.r1 = c.take<float>(d.N);
+  s.r2 = c.take<float>(d.N);
+  s.qkv = c.take<char>(d.N * d.QKVD * e);
+  s.qh = c.take<char>(d.N * d.QD * e);
+  s.kh = c.take<char>(d.N * d.KVD * e);
+  s.rq = c.take<float>(d.N * d.Hq);
+  s.rk = c.take<float>(d.N * d.Hkv);
+  s.o = c.take<char>(d.N * d.QD * e);
+  s.lse = c.take<float>(d.N * d.Hq);
+  s.attn_out = c.take<char>(d.N * d.D * e);
+  s.h = c.take<char>(d.N * d.D * e);
+  s.u = c.take<char>(d.N * d.F * e);
+  s.m = c.take<char>(d.N * d.D * e);
+  s.hn = s.r = nullptr;
+  s.hn8 = s.hn8t = s.r8t = s.w18 = s.w18t = s.w28 = s.w28t = nullptr;
+  if (d.fp8) {
+    s.hn8 = c.take<uint8_t>(d.N * d.D);
+    s.hn8t = c.take<uint8_t>((int64_t)d.D * d.Np);
+    s.r8t = c.take<uint8_t>((int64_t)d.F * d.Np);
+    s.w18 = c.take<uint8_t>((int64_t)d.F * d.D);
+    s.w18t = c.take<uint8_t>((int64_t)d.D * d.F);
+    s.w28 = c.take<uint8_t>((int64_t)d.D * d.F);
+    s.w28t = c.take<uint8_t>((int64_t)d.F * d.D);
+  } else {
+    s.hn = c.take<char>(d.N * d.D * e);
+    s.r = c.take<char>(d.N * d.F * e);
+  }
+  return c.bytes();
+}
+
+// ---------------------------------------------------------------- forward workspace
+struct FwdWs {
+  float2* cs;
+  void *vt, *hn, *r;
+  uint8_t* r8;
+};
+size_t carve_fwd(void* base, const Dims& d, FwdWs& w) {
+  Carver c(base);
+  w.cs = c.take<float2>(d.T * (d.DH / 2) + 1);
+  w.vt = c.take<char>(d.B * d.KVD * d.Tp * d.es);
+  w.hn = w.r = nullptr;
+  w.r8 = nullptr;
+  if (d.fp8) {
+    w.hn = c.take<char>(d.N * d.D * d.es);
+    w.r = c.take<char>(d.N * d.F * d.es);
+    w.r8 = c.take<uint8_t>(d.N * d.F);
+  }
+  return c.bytes();
+}
+
+// ---------------------------------------------------------------- backward workspace
+struct BwdWs {
+  float2* cs;
+  QScale* qs;            // [2]: dm, du
+  void *dm, *du, *dhn, *dh, *dattn, *dout, *dattnT, *oT, *woT, *qt, *kt, *dot, *dqkv, *dqkvT, *xnT, *wqkvT, *dxn;
+  void *w2T, *w1T, *dmT, *rT, *duT, *hnT;
+  uint8_t *dm8, *dm8t, *du8, *du8t;
+  float *delta, *dqh, *dkh, *dgp;
+};
+size_t carve_bwd(void* base, const Dims& d, BwdWs& w) {
+  Carver c(base);
+  const size_t e = d.es;
+  w.cs = c.take<float2>(d.T * (d.DH / 2) + 1);
+  w.qs = c.take<QScale>(2);
+  w.dm = c.take<char>(d.N * d.D * e);
+  w.du = c.take<char>(d.N * d.F * e);
+  w.dhn = c.take<char>(d.N * d.D * e);
+  w.dh = c.take<char>(d.N * d.D * e);
+  w.dattn = c.take<char>(d.N * d.D * e);
+  w.dout = c.take<char>(d.N * d.QD * e);
+  w.dattnT = c.take<char>((int64_t)d.D * d.Np * e);
+  w.oT = c.take<char>((int64_t)d.QD * d.Np * e);
+  w.woT = c.take<char>((int64_t)d.QD * d.D * e);
+  w.qt = c.take<char>(d.B * d.QD * d.Tp * e);
+  w.kt = c.take<char>(d.B * d.KVD * d.Tp * e);
+  w.dot = c.take<char>(d.B * d.QD * d.Tp * e);
+  w.delta = c.take<float>(d.N * d.Hq);
+  w.dqh = c.take<float>(d.N * d.QD);
+  w.dkh = c.take<float>(d.N * d.KVD);
+  w.dqkv = c.take<char>(d.N * d.QKVD * e);
+  w.dqkvT = c.take<char>((int64_t)d.QKVD * d.Np * e);
+  w.xnT = c.take<char>((int64_t)d.D * d.Np * e);
+  w.wqkvT = c.take<char>((int64_t)d.D * d.QKVD * e);
+  w.dxn = c.take<char>(d.N * d.D * e);
+  w.dgp = c.take<float>(rmsnorm_bwd_partials(d.N) * d.D + 1);
+  w.w2T = w.w1T = w.dmT = w.rT = w.duT = w.hnT = nullptr;
+  w.dm8 = w.dm8t = w.du8 = w.du8t = nullptr;
+  if (d.fp8) {
+    w.dm8 = c.take<uint8_t>(d.N * d.D);
+    w.dm8t = c.take<uint8_t>((int64_t)d.D * d.Np);
+    w.du8 = c.take<uint8_t>(d.N * d.F);
+    w.du8t = c.take<uint8_t>((int64_t)d.F * d.Np);
+  } else {
+    w.w2T = c.take<char>((int64_t)d.F * d.D * e);
+    w.w1T = c.take<char>((int64_t)d.D * d.F * e);
+    w.dmT = c.take<char>((int64_t)d.D * d.Np * e);
+    w.rT = c.take<char>((int64_t)d.F * d.Np * e);
+    w.duT = c.take<char>((int64_t)d.F * d.Np * e);
+    w.hnT = c.take<char>((int64_t)d.D * d.Np * e);
+  }
+  return c.bytes();
+}
+
+template <class T> T* P(void* p) { return static_cast<T*>(p); }
+template <class T> const T* CP(const void* p) { return static_cast<const T*>(p); }
+
+int check_ptrs(std::initializer_list<const void*> ps, const char* what) {
+  for (const void* p : ps) {
+    LL_CHECK(p, LL_ERR_INVALID_ARG, std::string(what) + ": null pointer");
+    LL_CHECK(aligned16(p), LL_ERR_INVALID_ARG, std::string(what) + ": pointer not 16-byte aligned");
+  }
+  return LL_OK;
+}
+
+hipError_t rope_table(float2* cs, const Dims& d, hipStream_t s) {
+  const int64_t n = d.T * (d.DH / 2);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 4096)), dim3(256), 0, s, cs,
+                     (int)d.T, d.DH / 2, (double)d.theta);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------ fwd
+template <class T, int DH>
+int layer_fwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32_t* ids, T* y, const Saved& sv,
+                const FwdWs& w, hipStream_t s) {
+  const int64_t N = d.N;
+  const float* g1 = CP<float>(p->attn_norm_w);
+  const float* g2 = CP<float>(p->mlp_norm_w);
+  LL_HIP(rope_table(w.cs, d, s));
+  LL_HIP(fill_f32(reinterpret_cast<float*>(sv.qs), 0.f, 4 * 4, s));
+  // attention block
+  LL_HIP(launch_rmsnorm_fwd(x, g1, P<T>(sv.xn), sv.r1, N, d.D, d.eps, (float*)nullptr, s));
+  {
+    EpiQkv<T> e{P<T>(sv.qkv), d.QKVD, d.ve ? CP<T>(p->ve_table) : nullptr, d.KVD, ids, d.vcol0};
+    LL_HIP(launch_gemm_nt(CP<T>(sv.xn), d.D, CP<T>(p->w_qkv), d.D, (int)N, d.QKVD, d.D, e, s));
+  }
+  if (N > 0) {
+    const int64_t threads = N * (d.Hq + d.Hkv) * (DH / 2);
+    hipLaunchKernelGGL((qk_prep_kernel<T, DH>), dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, s, CP<T>(sv.qkv),
+                       (int64_t)d.QKVD, w.cs, P<T>(sv.qh), P<T>(sv.kh), sv.rq, sv.rk, N, (int)d.T, d.Hq, d.Hkv, d.eps);
+    LL_HIP(hipGetLastError());
+    LL_HIP(launch_transpose(CP<T>(sv.qkv) + d.vcol0, d.T, DH, (int64_t)d.QKVD, P<T>(w.vt), d.Tp, d.Tp,
+                            (int)(d.B * d.Hkv), d.Hkv, d.T * d.QKVD, (int64_t)DH, (int64_t)DH * d.Tp, s));
+    const int nqb = (int)cdiv(d.T, 128);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nqb)), dim3(256), 0, s, CP<T>(sv.qh),
+                       CP<T>(sv.kh), CP<T>(w.vt), P<T>(sv.o), sv.lse, (int)d.B, (int)d.T, (int)d.Tp, d.Hq, d.Hkv);
+    LL_HIP(hipGetLastError());
+  }
+  {
+    EpiResidual<T> e{P<T>(sv.h), x, P<T>(sv.attn_out), (int64_t)d.D, p->resid_attn, Deq{nullptr, nullptr}};
+    LL_HIP(launch_gemm_nt(CP<T>(sv.o), d.QD, CP<T>(p->w_o), d.QD, (int)N, d.D, d.QD, e, s));
+  }
+  // MLP block
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (d.fp8) {
+      QScale* q = sv.qs;
+      LL_HIP(launch_rmsnorm_fwd(CP<T>(sv.h), g2, P<T>(w.hn), sv.r2, N, d.D, d.eps, &q[QS_HN].amax, s));
+      LL_HIP(launch_amax(CP<T>(p->w_fc), d.F, d.D, d.D, &q[QS_W1].amax, s));
+      LL_HIP(launch_amax(CP<T>(p->w_proj), d.D, d.F, d.F, &q[QS_W2].amax, s));
+      LL_HIP(launch_cast_e4m3(CP<T>(p->w_fc), d.F, d.D, d.D, &q[QS_W1], sv.w18, d.D, sv.w18t, d.F, d.F,
+                              (float*)nullptr, (float*)nullptr, s));
+      LL_HIP(launch_cast_e4m3(CP<T>(p->w_proj), d.D, d.F, d.F, &q[QS_W2], sv.w28, d.F, sv.w28t, d.D, d.D,
+                              (float*)nullptr, (float*)nullptr, s));
+      LL_HIP(launch_cast_e4m3(CP<T>(w.hn), N, d.D, d.D, &q[QS_HN], sv.hn8, d.D, sv.hn8t, d.Np, d.Np,
+                              (float*)nullptr, (float*)nullptr, s));
+      {
+        EpiRelu2<T> e{P<T>(sv.u), P<T>(w.r), (int64_t)d.F, Deq{&q[QS_HN].inv_scale, &q[QS_W1].inv_scale},
+                      &q[QS_R].amax};
+        LL_HIP(launch_gemm_nt(sv.hn8, d.D, sv.w18, d.D, (int)N, d.F, d.D, e, s));
+      }
+      LL_HIP(launch_cast_e4m3(CP<T>(w.r), N, d.F, d.F, &q[QS_R], w.r8, d.F, sv.r8t, d.Np, d.Np,
+                              (float*)nullptr, (float*)nullptr, s));
+      {
+        EpiResidual<T> e{y, CP<T>(sv.h), P<T>(sv.m), (int64_t)d.D, p->resid_mlp,
+                         Deq{&q[QS_R].inv_scale, &q[QS_W2].inv_scale}};
+        LL_HIP(launch_gemm_nt(w.r8, d.F, sv.w28, d.F, (int)N, d.D, d.F, e, s));
+      }
+      return LL_OK;
+    }
+  }
+  LL_HIP(launch_rmsnorm_fwd(CP<T>(sv.h), g2, P<T>(sv.hn), sv.r2, N, d.D, d.eps, (float*)nullptr, s));
+  {
+    EpiRelu2<T> e{P<T>(sv.u), P<T>(sv.r), (int64_t)d.F, Deq{nullptr, nullptr}, &sv.qs[QS_R].amax};
+    LL_HIP(launch_gemm_nt(CP<T>(sv.hn), d.D, CP<T>(p->w_fc), d.D, (int)N, d.F, d.D, e, s));
+  }
+  {
+    EpiResidual<T> e{y, CP<T>(sv.h), P<T>(sv.m), (int64_t)d.D, p->resid_mlp, Deq{nullptr, nullptr}};
+    LL_HIP(launch_gemm_nt(CP<T>(sv.r), d.F, CP<T>(p->w_proj), d.F, (int)N, d.D, d.F, e, s));
+  }
+  return LL_OK;
+}
+
+// ------------------------------------------------------------------------------------------ bwd
+template <class T, int DH>
+int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32_t* ids, const Saved& sv,
+                const T* dy, T* dx, const ll_layer_grads* g, const BwdWs& w, hipStream_t s) {
+  const int64_t N = d.N, Np = d.Np;
+  const float* g1 = CP<float>(p->attn_norm_w);
+  const float* g2 = CP<float>(p->mlp_norm_w);
+  LL_HIP(rope_table(w.cs, d, s));
+  LL_HIP(fill_f32(reinterpret_cast<float*>(w.qs), 0.f, 2 * 4, s));
+  LL_HIP(fill_f32(g->resid_mlp, 0.f, 1, s));
+  LL_HIP(fill_f32(g->resid_attn, 0.f, 1, s));
+  // MLP residual branch: dm = a_mlp dy, da_mlp = sum dy m
+  LL_HIP(launch_scale_dot(dy, CP<T>(sv.m), p->resid_mlp, P<T>(w.dm), N * d.D, g->resid_mlp,
+                          d.fp8 ? &w.qs[0].amax : nullptr, s));
+  bool done = false;
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (d.fp8) {
+      QScale* q = sv.qs;
+      QScale* qdm = &w.qs[0];
+      QScale* qdu = &w.qs[1];
+      LL_HIP(launch_cast_e4m3(CP<T>(w.dm), N, d.D, d.D, qdm, w.dm8, d.D, w.dm8t, Np, Np, (float*)nullptr,
+                              (float*)nullptr, s));
+      {   // dr = dm W2 (W2^T quantised is [F, D]); du = dr * 2 relu(u)
+        EpiRelu2Bwd<T> e{P<T>(w.du), CP<T>(sv.u), (int64_t)d.F, Deq{&qdm->inv_scale, &q[QS_W2].inv_scale}, &qdu->amax};
+        LL_HIP(launch_gemm_nt(w.dm8, d.D, sv.w28t, d.D, (int)N, d.F, d.D, e, s));
+      }
+      {   // dW2 = dm^T r   [D, F]
+        EpiStore<T> e{P<T>(g->w_proj), (int64_t)d.F, Deq{&qdm->inv_scale, &q[QS_R].inv_scale}};
+        LL_HIP(launch_gemm_nt(w.dm8t, Np, sv.r8t, Np, d.D, d.F, (int)Np, e, s));
+      }
+      LL_HIP(launch_cast_e4m3(CP<T>(w.du), N, d.F, d.F, qdu, w.du8, d.F, w.du8t, Np, Np, (float*)nullptr,
+                              (float*)nullptr, s));
+      {   // dW1 = du^T hn  [F, D]
+        EpiStore<T> e{P<T>(g->w_fc), (int64_t)d.D, Deq{&qdu->inv_scale, &q[QS_HN].inv_scale}};
+        LL_HIP(launch_gemm_nt(w.du8t, Np, sv.hn8t, Np, d.F, d.D, (int)Np, e, s));
+      }
+      {   // dhn = du W1 (W1^T quantised is [D, F])
+        EpiStore<T> e{P<T>(w.dhn), (int64_t)d.D, Deq{&qdu->inv_scale, &q[QS_W1].inv_scale}};
+        LL_HIP(launch_gemm_nt(w.du8, d.F, sv.w18t, d.F, (int)N, d.D, d.F, e, s));
+      }
+      done = true;
+    }
+  }
+  if (!done) {
+    LL_HIP(transpose2d(CP<T>(p->w_proj), d.D, d.F, (int64_t)d.F, P<T>(w.w2T), (int64_t)d.D, (int64_t)d.D, s));
+    LL_HIP(transpose2d(CP<T>(p->w_fc), d.F, d.D, (int64_t)d.D, P<T>(w.w1T), (int64_t)d.F, (int64_t)d.F, s));
+    {
+      EpiRelu2Bwd<T> e{P<T>(w.du), CP<T>(sv.u), (int64_t)d.F, Deq{nullptr, nullptr}, &w.qs[1].amax};
+      LL_HIP(launch_gemm_nt(CP<T>(w.dm), d.D, CP<T>(w.w2T), d.D, (int)N, d.F, d.D, e, s));
+    }
+    LL_HIP(transpose2d(CP<T>(w.dm), N, d.D, (int64_t)d.D, P<T>(w.dmT), Np, Np, s));
+    LL_HIP(transpose2d(CP<T>(sv.r), N, d.F, (int64_t)d.F, P<T>(w.rT), Np, Np, s));
+    {
+      EpiStore<T> e{P<T>(g->w_proj), (int64_t)d.F, Deq{nullptr, nullptr}};
+      LL_HIP(launch_gemm_nt(CP<T>(w.dmT), Np, CP<T>(w.rT), Np, d.D, d.F, (int)Np, e, s));
+    }
+    LL_HIP(transpose2d(CP<T>(w.du), N, d.F, (int64_t)d.F, P<T>(w.duT), Np, Np, s));
+    LL_HIP(transpose2d(CP<T>(sv.hn), N, d.D, (int64_t)d.D, P<T>(w.hnT), Np, Np, s));
+    {
+      EpiStore<T> e{P<T>(g->w_fc), (int64_t)d.D, Deq{nullptr, nullptr}};
+      LL_HIP(launch_gemm_nt(CP<T>(w.duT), Np, CP<T>(w.hnT), Np, d.F, d.D, (int)Np, e, s));
+    }
+    {
+      EpiStore<T> e{P<T>(w.dhn), (int64_t)d.D, Deq{nullptr, nullptr}};
+      LL_HIP(launch_gemm_nt(CP<T>(w.du), d.F, CP<T>(w.w1T), d.F, (int)N, d.D, d.F, e, s));
+    }
+  }
+  // MLP RMSNorm backward + residual, fused with the attention-branch scaling
+  LL_HIP(launch_rmsnorm_bwd(CP<T>(w.dhn), CP<T>(sv.h), g2, sv.r2, dy, P<T>(w.dh), w.dgp, N, d.D, p->resid_attn,
+                            P<T>(w.dattn), CP<T>(sv.attn_out), g->resid_attn, s));
+  LL_HIP(launch_colsum(w.dgp, rmsnorm_bwd_partials(N), d.D, P<float>(g->mlp_norm_w), s));
+  // O projection
+  LL_HIP(transpose2d(CP<T>(p->w_o), d.D, d.QD, (int64_t)d.QD, P<T>(w.woT), (int64_t)d.D, (int64_t)d.D, s));
+  {
+    EpiStore<T> e{P<T>(w.dout), (int64_t)d.QD, Deq{nullptr, nullptr}};
+    LL_HIP(launch_gemm_nt(CP<T>(w.dattn), d.D, CP<T>(w.woT), d.D, (int)N, d.QD, d.D, e, s));
+  }
+  LL_HIP(transpose2d(CP<T>(w.dattn), N, d.D, (int64_t)d.D, P<T>(w.dattnT), Np, Np, s));
+  LL_HIP(transpose2d(CP<T>(sv.o), N, d.QD, (int64_t)d.QD, P<T>(w.oT), Np, Np, s));
+  {
+    EpiStore<T> e{P<T>(g->w_o), (int64_t)d.QD, Deq{nullptr, nullptr}};
+    LL_HIP(launch_gemm_nt(CP<T>(w.dattnT), Np, CP<T>(w.oT), Np, d.D, d.QD, (int)Np, e, s));
+  }
+  // attention core
+  T* dqkv = P<T>(w.dqkv);
+  if (N > 0) {
+    const int64_t dthreads = N * d.Hq * (DH / 2);
+    hipLaunchKernelGGL((attn_delta_kernel<T, DH>), dim3((unsigned)cdiv(dthreads, 256)), dim3(256), 0, s,
+                       CP<T>(w.dout), CP<T>(sv.o), w.delta, N, (int)d.T, d.Hq);
+    LL_HIP(hipGetLastError());
+    LL_HIP(launch_transpose(CP<T>(sv.qh), d.T, DH, (int64_t)d.QD, P<T>(w.qt), d.Tp, d.Tp, (int)(d.B * d.Hq), d.Hq,
+                            d.T * d.QD, (int64_t)DH, (int64_t)DH * d.Tp, s));
+    LL_HIP(launch_transpose(CP<T>(sv.kh), d.T, DH, (int64_t)d.KVD, P<T>(w.kt), d.Tp, d.Tp, (int)(d.B * d.Hkv), d.Hkv,
+                            d.T * d.KVD, (int64_t)DH, (int64_t)DH * d.Tp, s));
+    LL_HIP(launch_transpose(CP<T>(w.dout), d.T, DH, (int64_t)d.QD, P<T>(w.dot), d.Tp, d.Tp, (int)(d.B * d.Hq), d.Hq,
+                            d.T * d.QD, (int64_t)DH, (int64_t)DH * d.Tp, s));
+    const int nkb = (int)cdiv(d.T, 64);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DH>), dim3((unsigned)(d.B * d.Hkv * nkb)), dim3(256), 0, s,
+                       CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout),
+                       CP<T>(w.qt), CP<T>(w.dot), sv.lse, w.delta, w.dkh, dqkv + d.vcol0, (int64_t)d.QKVD,
+                       (int)d.B, (int)d.T, (int)d.Tp, d.Hq, d.Hkv);
+    LL_HIP(hipGetLastError());
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nkb)), dim3(256), 0, s,
+                       CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout),
+                       CP<T>(w.kt), sv.lse, w.delta, w.dqh, (int)d.B, (int)d.T, (int)d.Tp, d.Hq, d.Hkv);
+    LL_HIP(hipGetLastError());
+    const int64_t pthreads = N * (d.Hq + d.Hkv) * (DH / 2);
+    hipLaunchKernelGGL((qk_post_kernel<T, DH>), dim3((unsigned)cdiv(pthreads, 256)), dim3(256), 0, s, w.dqh, w.dkh,
+                       CP<T>(sv.qkv), (int64_t)d.QKVD, w.cs, sv.rq, sv.rk, dqkv, N, (int)d.T, d.Hq, d.Hkv);
+    LL_HIP(hipGetLastError());
+    if (d.ve) {
+      const int64_t tot = N * d.KVD;
+      hipLaunchKernelGGL((ve_scatter_kernel<T>), dim3((unsigned)std::min<int64_t>(cdiv(tot, 256), 16384)), dim3(256),
+                         0, s, CP<T>(dqkv) + d.vcol0, (int64_t)d.QKVD, ids, g->ve_table, (int64_t)d.KVD, N, d.KVD);
+      LL_HIP(hipGetLastError());
+    }
+  }
+  // QKV projection
+  LL_HIP(transpose2d(CP<T>(p->w_qkv), d.QKVD, d.D, (int64_t)d.D, P<T>(w.wqkvT), (int64_t)d.QKVD, (int64_t)d.QKVD, s));
+  {
+    EpiStore<T> e{P<T>(w.dxn), (int64_t)d.D, Deq{nullptr, nullptr}};
+    LL_HIP(launch_gemm_nt(CP<T>(dqkv), d.QKVD, CP<T>(w.wqkvT), d.QKVD, (int)N, d.D, d.QKVD, e, s));
+  }
+  LL_HIP(transpose2d(CP<T>(dqkv), N, d.QKVD, (int64_t)d.QKVD, P<T>(w.dqkvT), Np, Np, s));
+  LL_HIP(transpose2d(CP<T>(sv.xn), N, d.D, (int64_t)d.D, P<T>(w.xnT), Np, Np, s));
+  {
+    EpiStore<T> e{P<T>(g->w_qkv), (int64_t)d.D, Deq{nullptr, nullptr}};
+    LL_HIP(launch_gemm_nt(CP<T>(w.dqkvT), Np, CP<T>(w.xnT), Np, d.QKVD, d.D, (int)Np, e, s));
+  }
+  // input RMSNorm backward + residual
+  LL_HIP(launch_rmsnorm_bwd(CP<T>(w.dxn), x, g1, sv.r1, CP<T>(w.dh), dx, w.dgp, N, d.D, (const float*)nullptr,
+                            (T*)nullptr, (const T*)nullptr, (float*)nullptr, s));
+  LL_HIP(launch_colsum(w.dgp, rmsnorm_bwd_partials(N), d.D, P<float>(g->attn_norm_w), s));
+  return LL_OK;
+}
+
+}  // namespace
+
+extern "C" size_t ll_layer_saved_bytes(const ll_layer_cfg* cfg) {
+  Dims d;
+  if (make_dims(cfg, d) != LL_OK) return 0;
+  Saved s;
+  return carve_saved(nullptr, d, s);
+}
+
+extern "C" size_t ll_layer_workspace_bytes(const ll_layer_cfg* cfg) {
+  Dims d;
+  if (make_dims(cfg, d) != LL_OK) return 0;
+  FwdWs f;
+  BwdWs b;
+  return std::max(carve_fwd(nullptr, d, f), carve_bwd(nullptr, d, b));
+}
+
+extern "C" int ll_layer_fwd(const ll_layer_cfg* cfg, const ll_layer_params* p, const void* x, const int32_t* token_ids,
+                            void* y, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  if (int st = make_dims(cfg, d)) return st;
+  LL_CHECK(p, LL_ERR_INVALID_ARG, "params must not be null");
+  if (int st = check_ptrs({p->attn_norm_w, p->w_qkv, p->w_o, p->mlp_norm_w, p->w_fc, p->w_proj, p->resid_attn,
+                           p->resid_mlp}, "params")) return st;
+  if (d.ve) {
+    if (int st = check_ptrs({p->ve_table}, "params.ve_table")) return st;
+    LL_CHECK(d.N == 0 || token_ids, LL_ERR_INVALID_ARG, "token_ids required on value-embedding layers");
+  }
+  if (d.N > 0) {
+    if (int st = check_ptrs({x, y}, "x/y")) return st;
+    LL_CHECK(x != y, LL_ERR_INVALID_ARG, "y must not alias x");
+  }
+  Saved sv;
+  FwdWs w;
+  const size_t need_s = carve_saved(nullptr, d, sv), need_w = carve_fwd(nullptr, d, w);
+  LL_CHECK(saved && aligned16(saved), LL_ERR_INVALID_ARG, "saved must be a 16-byte aligned device pointer");
+  LL_CHECK(ws && aligned16(ws), LL_ERR_INVALID_ARG, "ws must be a 16-byte aligned device pointer");
+  LL_CHECK(saved_bytes >= need_s, LL_ERR_WORKSPACE, "saved buffer too small: need " + std::to_string(need_s));
+  LL_CHECK(ws_bytes >= need_w, LL_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_w));
+  carve_saved(saved, d, sv);
+  carve_fwd(ws, d, w);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d.bf) return layer_fwd_t<bf16, 128>(d, p, CP<bf16>(x), token_ids, P<bf16>(y), sv, w, s);
+  return layer_fwd_t<float, 64>(d, p, CP<float>(x), token_ids, P<float>(y), sv, w, s);
+}
+
+extern "C" int ll_layer_bwd(const ll_layer_cfg* cfg, const ll_layer_params* p, const void* x, const int32_t* token_ids,
+                            const void* saved, size_t saved_bytes, const void* dy, void* dx, const ll_layer_grads* g,
+                            void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  if (int st = make_dims(cfg, d)) return st;
+  LL_CHECK(p && g, LL_ERR_INVALID_ARG, "params and grads must not be null");
+  if (int st = check_ptrs({p->attn_norm_w, p->w_qkv, p->w_o, p->mlp_norm_w, p->w_fc, p->w_proj, p->resid_attn,
+                           p->resid_mlp}, "params")) return st;
+  if (int st = check_ptrs({g->attn_norm_w, g->w_qkv, g->w_o, g->mlp_norm_w, g->w_fc, g->w_proj, g->resid_attn,
+                           g->resid_mlp}, "grads")) return st;
+  if (d.ve) {
+    if (int st = check_ptrs({p->ve_table, g->ve_table}, "ve_table")) return st;
+    LL_CHECK(d.N == 0 || token_ids, LL_ERR_INVALID_ARG, "token_ids required on value-embedding layers");
+  }
+  if (d.N > 0) {
+    if (int st = check_ptrs({x, dy, dx}, "x/dy/dx")) return st;
+    LL_CHECK(dx != dy && dx != x, LL_ERR_INVALID_ARG, "dx must not alias dy or x");
+  }
+  Saved sv;
+  BwdWs w;
+  const size_t need_s = carve_saved(nullptr, d, sv), need_w = carve_bwd(nullptr, d, w);
+  LL_CHECK(saved && aligned16(saved), LL_ERR_INVALID_ARG, "saved must be a 16-byte aligned device pointer");
+  LL_CHECK(ws && aligned16(ws), LL_ERR_INVALID_ARG, "ws must be a 16-byte aligned device pointer");
+  LL_CHECK(saved_bytes >= need_s, LL_ERR_WORKSPACE, "saved buffer too small: need " + std::to_string(need_s));
+  LL_CHECK(ws_bytes >= need_w, LL_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_w));
+  carve_saved(const_cast<void*>(saved), d, sv);
+  carve_bwd(ws, d, w);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d.bf)
+    return layer_bwd_t<bf16, 128>(d, p, CP<bf16>(x), token_ids, sv, CP<bf16>(dy), P<bf16>(dx), g, w, s);
+  return layer_bwd_t<float, 64>(d, p, CP<float>(x), token_ids, sv, CP<float>(dy), P<float>(dx), g, w, s);
+}

@@ -1,0 +1,119 @@
+// Fused linear cross-entropy with tanh logit softcap [youdonthavefriends cost analysis,
+// "Increasing throughput" (the fused loss chunks the LM-head matmul so the (B*T, vocab) logits are
+// never materialised) and "config appendix" (LigerFusedLinearCrossEntropyLoss(softcap=15.0))].
+// Per chunk of C rows:
+//   1. z = H_c W^T on MFMA; the epilogue rounds z to the storage type, stores it, and reduces
+//      c = s tanh(z/s) over each 128-column vocabulary tile to an online (max, sum exp) pair;
+//   2. one wave per row combines the pairs into lse and adds lse - c[target] to the loss;
+//   3. dz = grad_scale/n_valid (exp(c - lse) - onehot)(1 - (c/s)^2), rounded, stored as dz and
+//      dz^T (64 x 64 LDS tile transpose) in one pass;
+//   4. dH_c = dz W (GEMM against W^T) and dW += dz^T H_c (fp32 accumulation across chunks).
+#pragma once
+#include "common.h"
+#include "gemm.h"
+
+namespace ll {
+namespace {
+
+template <class T> struct EpiLceLogits {
+  static constexpr int kKind = kEpiRowLse;
+  T* z; int64_t ldz; float2* part; int nparts; float softcap; float inv_softcap;
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8], float& mx, float& se) const {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = Elem<T>::rnd(v[k]);
+    Vec8<T>::store(z + (int64_t)m * ldz + n, v);
+    float c[8];
+    mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      c[k] = softcap * tanhf(v[k] * inv_softcap);
+      mx = fmaxf(mx, c[k]);
+    }
+    se = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) se += __expf(c[k] - mx);
+  }
+  __device__ __forceinline__ void row(int m, int bn, float mx, float se) const {
+    part[(int64_t)m * nparts + bn] = make_float2(mx, se);
+  }
+};
+
+__global__ void count_valid_kernel(const int32_t* __restrict__ y, int64_t n, int32_t ignore, int* __restrict__ nv) {
+  int c = 0;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    c += (y[i] != ignore);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  if ((threadIdx.x & 63) == 0 && c) atomicAdd(nv, c);
+}
+
+// one wave per row of the chunk: lse = M + log(sum_t se_t exp(m_t - M)); loss += lse - c[y]
+template <class T>
+__global__ void __launch_bounds__(256)
+lce_lse_kernel(const float2* __restrict__ part, int nparts, const T* __restrict__ z, int64_t ldz,
+               const int32_t* __restrict__ y, int rows, int32_t ignore, float softcap, float* __restrict__ lse_out,
+               float* __restrict__ lse_chunk, float* __restrict__ loss_acc) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float2* pr = part + (int64_t)row * nparts;
+  float M = -INFINITY;
+  for (int t = lane; t < nparts; t += 64) M = fmaxf(M, pr[t].x);
+  M = wave_max(M);
+  float S = 0.f;
+  for (int t = lane; t < nparts; t += 64) S += pr[t].y * __expf(pr[t].x - M);
+  S = wave_sum(S);
+  const float l = M + __logf(S);
+  if (lane == 0) {
+    lse_chunk[row] = l;
+    if (lse_out) lse_out[row] = l;
+    const int32_t t = y[row];
+    if (t != ignore) {
+      const float zt = Elem<T>::ld(z, (int64_t)row * ldz + t);
+      atomicAdd(loss_acc, l - softcap * tanhf(zt / softcap));
+    }
+  }
+}
+
+// dz / dz^T over a 64 (rows) x 64 (vocab) tile; rows >= rows_valid or cols >= V give 0.
+//   dz [rows_pad, ldz] (written for cols < Vpad), dzt [Vpad, ldzt] (written for rows < rows_pad)
+template <class T>
+__global__ void __launch_bounds__(256)
+lce_dz_kernel(const T* __restrict__ z, int64_t ldz, const float* __restrict__ lse, const int32_t* __restrict__ y,
+              int rows_valid, int rows_pad, int V, int Vpad, int32_t ignore, float softcap, float grad_scale,
+              const int* __restrict__ nv, T* __restrict__ dz, T* __restrict__ dzt, int64_t ldzt) {
+  __shared__ float tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int n_valid = *nv;
+  const float gs = n_valid > 0 ? grad_scale / (float)n_valid : 0.f;
+  const float inv_s = 1.f / softcap;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    float d = 0.f;
+    if (r < rows_valid && c < V) {
+      const int32_t t = y[r];
+      if (t != ignore) {
+        const float cv = softcap * tanhf(Elem<T>::ld(z, (int64_t)r * ldz + c) * inv_s);
+        const float p = __expf(cv - lse[r]) - (c == t ? 1.f : 0.f);
+        const float w = cv * inv_s;
+        d = Elem<T>::rnd(gs * p * (1.f - w * w));
+      }
+    }
+    if (r < rows_pad && c < Vpad) Elem<T>::st(dz, (int64_t)r * ldz + c, d);
+    tile[i][tx] = d;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < Vpad && r < rows_pad) Elem<T>::st(dzt, (int64_t)c * ldzt + r, tile[tx][i]);
+  }
+}
+
+__global__ void lce_finalize_kernel(const float* __restrict__ loss_acc, const int* __restrict__ nv, float* __restrict__ loss) {
+  const int n = *nv;
+  *loss = n > 0 ? *loss_acc / (float)n : 0.f;
+}
+
+}  // namespace
+}  // namespace ll

@@ -1,0 +1,136 @@
+// ll_fused_lce_fwd_bwd: chunked fused linear cross-entropy with tanh logit softcap.
+#include "api.h"
+#include "gemm.h"
+#include "lce.h"
+#include "norm.h"
+#include "quant.h"
+
+using namespace ll;
+
+namespace {
+
+constexpr int kLceBN = 128;              // vocabulary tile of the logits GEMM (one LSE partial each)
+constexpr int64_t kDefaultChunk = 8192;
+
+struct LcePlan {
+  int64_t chunk, chunk_pad, vpad;
+  int nparts;
+  float2* part = nullptr;
+  void* wt = nullptr;       // [D, Vpad]
+  void* z = nullptr;        // [chunk_pad, Vpad]  (z, then dz in place)
+  void* dzt = nullptr;      // [Vpad, chunk_pad]
+  void* ht = nullptr;       // [D, chunk_pad]
+  float* dw32 = nullptr;    // [V, D]
+  float* lse = nullptr;     // [chunk]
+  float* loss_acc = nullptr;
+  int* nv = nullptr;
+  size_t bytes = 0;
+};
+
+LcePlan plan_lce(void* ws, int es, int64_t n, int d, int64_t v, int64_t token_chunk, bool grads) {
+  LcePlan p;
+  p.chunk = token_chunk > 0 ? token_chunk : kDefaultChunk;
+  if (p.chunk > n) p.chunk = n > 0 ? n : 1;
+  p.chunk_pad = round_up(p.chunk, 64);
+  p.vpad = round_up(v, 64);
+  p.nparts = (int)cdiv(v, kLceBN);
+  Carver c(ws);
+  p.loss_acc = c.take<float>(4);
+  p.nv = c.take<int>(4);
+  p.lse = c.take<float>(p.chunk_pad);
+  p.part = c.take<float2>(p.chunk_pad * p.nparts);
+  p.z = c.take<char>((size_t)p.chunk_pad * p.vpad * es);
+  if (grads) {
+    p.wt = c.take<char>((size_t)d * p.vpad * es);
+    p.dzt = c.take<char>((size_t)p.vpad * p.chunk_pad * es);
+    p.ht = c.take<char>((size_t)d * p.chunk_pad * es);
+    p.dw32 = c.take<float>((size_t)v * d);
+  }
+  p.bytes = c.bytes();
+  return p;
+}
+
+template <class T>
+int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t v, float softcap,
+            int32_t ignore, float grad_scale, const LcePlan& p, float* loss, float* lse_out, T* dH, T* dW,
+            hipStream_t s) {
+  const bool grads = dH != nullptr;
+  LL_HIP(fill_f32(p.loss_acc, 0.f, 4, s));
+  LL_HIP(fill_f32(reinterpret_cast<float*>(p.nv), 0.f, 4, s));
+  if (n > 0) {
+    hipLaunchKernelGGL(count_valid_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 1024)), dim3(256), 0, s,
+                       y, n, ignore, p.nv);
+    LL_HIP(hipGetLastError());
+  }
+  if (grads) LL_HIP(transpose2d(W, v, d, (int64_t)d, static_cast<T*>(p.wt), p.vpad, p.vpad, s));
+  T* z = static_cast<T*>(p.z);
+  for (int64_t r0 = 0; r0 < n; r0 += p.chunk) {
+    const int rows = (int)std::min<int64_t>(p.chunk, n - r0);
+    const T* Hc = H + r0 * d;
+    EpiLceLogits<T> epi{z, p.vpad, p.part, p.nparts, softcap, 1.f / softcap};
+    LL_HIP(launch_gemm_nt(Hc, (int64_t)d, W, (int64_t)d, rows, (int)v, d, epi, s));
+    hipLaunchKernelGGL((lce_lse_kernel<T>), dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, s, p.part, p.nparts, z,
+                       p.vpad, y + r0, rows, ignore, softcap, lse_out ? lse_out + r0 : nullptr, p.lse, p.loss_acc);
+    LL_HIP(hipGetLastError());
+    if (!grads) continue;
+    const int rows_pad = (int)round_up(rows, 64);
+    dim3 g((unsigned)cdiv(p.vpad, 64), (unsigned)cdiv(rows_pad, 64));
+    hipLaunchKernelGGL((lce_dz_kernel<T>), g, dim3(256), 0, s, z, p.vpad, p.lse, y + r0, rows, rows_pad, (int)v,
+                       (int)p.vpad, ignore, softcap, grad_scale, p.nv, z, static_cast<T*>(p.dzt), (int64_t)rows_pad);
+    LL_HIP(hipGetLastError());
+    // dH_c = dz W  (B operand: W^T [D, Vpad])
+    EpiStore<T> eh{dH + r0 * d, (int64_t)d, Deq{nullptr, nullptr}};
+    LL_HIP(launch_gemm_nt(z, p.vpad, static_cast<const T*>(p.wt), p.vpad, rows, d, (int)p.vpad, eh, s));
+    // dW += dz^T H_c  (A: dz^T [Vpad, rows_pad], B: H_c^T [D, rows_pad])
+    LL_HIP(transpose2d(Hc, rows, d, (int64_t)d, static_cast<T*>(p.ht), (int64_t)rows_pad, (int64_t)rows_pad, s));
+    EpiAcc32 ew{p.dw32, (int64_t)d, r0 > 0 ? 1 : 0};
+    LL_HIP(launch_gemm_nt(static_cast<const T*>(p.dzt), (int64_t)rows_pad, static_cast<const T*>(p.ht),
+                          (int64_t)rows_pad, (int)v, d, rows_pad, ew, s));
+  }
+  if (grads) {
+    if (n == 0) LL_HIP(fill_f32(p.dw32, 0.f, v * d, s));     // no chunk ran: dW = 0
+    LL_HIP(launch_convert(p.dw32, dW, v * d, s));
+  }
+  hipLaunchKernelGGL(lce_finalize_kernel, dim3(1), dim3(1), 0, s, p.loss_acc, p.nv, loss);
+  LL_HIP(hipGetLastError());
+  return LL_OK;
+}
+
+}  // namespace
+
+extern "C" size_t ll_fused_lce_workspace_bytes(int32_t dtype, int64_t n, int32_t d, int64_t v, int64_t token_chunk) {
+  if ((dtype != LL_F32 && dtype != LL_BF16) || n < 0 || d <= 0 || v <= 0) return 0;
+  const int es = dtype == LL_F32 ? 4 : 2;
+  return plan_lce(nullptr, es, n, d, v, token_chunk, true).bytes;
+}
+
+extern "C" int ll_fused_lce_fwd_bwd(int32_t dtype, const void* hidden, const void* weight, const int32_t* targets,
+                                    int64_t n, int32_t d, int64_t v, float softcap, int32_t ignore_index,
+                                    float grad_scale, int64_t token_chunk, float* loss, float* lse, void* d_hidden,
+                                    void* d_weight, void* ws, size_t ws_bytes, void* stream) {
+  LL_CHECK(dtype == LL_F32 || dtype == LL_BF16, LL_ERR_INVALID_ARG, "dtype must be LL_F32 or LL_BF16");
+  LL_CHECK(n >= 0 && d > 0 && v > 0, LL_ERR_INVALID_ARG, "need n >= 0, d > 0, v > 0");
+  LL_CHECK(d % (dtype == LL_F32 ? 32 : 64) == 0, LL_ERR_UNSUPPORTED, "d must be a multiple of 64 (bf16) / 32 (fp32)");
+  LL_CHECK(v % 8 == 0, LL_ERR_UNSUPPORTED, "v must be a multiple of 8");
+  LL_CHECK(v < (int64_t)1 << 31 && n < (int64_t)1 << 31, LL_ERR_UNSUPPORTED, "n and v must fit in int32");
+  LL_CHECK(softcap > 0.f, LL_ERR_INVALID_ARG, "softcap must be > 0");
+  LL_CHECK(token_chunk >= 0, LL_ERR_INVALID_ARG, "token_chunk must be >= 0");
+  LL_CHECK(token_chunk == 0 || token_chunk <= (int64_t)65535 * 64, LL_ERR_UNSUPPORTED, "token_chunk too large");
+  LL_CHECK(loss, LL_ERR_INVALID_ARG, "loss must not be null");
+  LL_CHECK((d_hidden == nullptr) == (d_weight == nullptr), LL_ERR_INVALID_ARG, "d_hidden and d_weight: both or neither");
+  LL_CHECK(weight && aligned16(weight), LL_ERR_INVALID_ARG, "weight must be a 16-byte aligned device pointer");
+  LL_CHECK(n == 0 || (hidden && targets && aligned16(hidden)), LL_ERR_INVALID_ARG, "hidden/targets must not be null");
+  LL_CHECK(!d_hidden || (aligned16(d_hidden) && aligned16(d_weight)), LL_ERR_INVALID_ARG, "gradients must be 16-byte aligned");
+  const int es = dtype == LL_F32 ? 4 : 2;
+  const bool grads = d_hidden != nullptr;
+  const size_t need = plan_lce(nullptr, es, n, d, v, token_chunk, grads).bytes;
+  LL_CHECK(ws && aligned16(ws), LL_ERR_INVALID_ARG, "ws must be a 16-byte aligned device pointer");
+  LL_CHECK(ws_bytes >= need, LL_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  const LcePlan p = plan_lce(ws, es, n, d, v, token_chunk, grads);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == LL_BF16)
+    return run_lce(static_cast<const bf16*>(hidden), static_cast<const bf16*>(weight), targets, n, d, v, softcap,
+                   ignore_index, grad_scale, p, loss, lse, static_cast<bf16*>(d_hidden), static_cast<bf16*>(d_weight), s);
+  return run_lce(static_cast<const float*>(hidden), static_cast<const float*>(weight), targets, n, d, v, softcap,
+                 ignore_index, grad_scale, p, loss, lse, static_cast<float*>(d_hidden), static_cast<float*>(d_weight), s);
+}

@@ -1,0 +1,262 @@
+// RMSNorm forward/backward and the small HBM-bound kernels around the GEMMs of the layer:
+// residual-scalar branch scaling with its fused gradient reduction, column sums, transposes.
+// RMSNorm with eps 1e-6 and the learnable residual scalars are parts of the little-lm block
+// [hn.213312.xyz translation, 设置 / Setup; youdonthavefriends cost analysis, "config appendix":
+// rms_norm_eps 1e-6, layer_scale true].
+#pragma once
+#include "common.h"
+
+namespace ll {
+namespace {
+
+constexpr int kMaxDChunks = 8;   // D <= 8 * 512 = 4096 (one wave covers 512 columns per pass)
+
+// y = round(x * r * g), r = 1 / sqrt(mean(x^2) + eps); one wave per row; optional amax of y.
+template <class T>
+__global__ void __launch_bounds__(256)
+rmsnorm_fwd_kernel(const T* __restrict__ x, const float* __restrict__ g, T* __restrict__ y,
+                   float* __restrict__ rstd, int64_t N, int D, float eps, float* amax) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  float mx = 0.f;
+  if (row < N) {
+    const T* xr = x + row * D;
+    float ss = 0.f;
+    for (int c = lane * 8; c < D; c += 512) {
+      float v[8];
+      Vec8<T>::load(xr + c, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ss += v[k] * v[k];
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)D + eps);
+    if (lane == 0) rstd[row] = r;
+    for (int c = lane * 8; c < D; c += 512) {
+      float v[8], gv[8];
+      Vec8<T>::load(xr + c, v);
+      Vec8<float>::load(g + c, gv);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        v[k] = Elem<T>::rnd(v[k] * r * gv[k]);
+        mx = fmaxf(mx, fabsf(v[k]));
+      }
+      Vec8<T>::store(y + row * D + c, v);
+    }
+  }
+  if (amax) {
+    mx = wave_max(mx);
+    if (lane == 0) atomic_max_nonneg(amax, mx);
+  }
+}
+
+template <class T>
+inline hipError_t launch_rmsnorm_fwd(const T* x, const float* g, T* y, float* rstd, int64_t N, int D,
+                                     float eps, float* amax, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  hipLaunchKernelGGL((rmsnorm_fwd_kernel<T>), dim3((unsigned)cdiv(N, 4)), dim3(256), 0, s, x, g, y, rstd, N, D, eps, amax);
+  return hipGetLastError();
+}
+
+// RMSNorm backward fused with the residual add (and optionally the next branch scaling):
+//   out  = round(resid + r (g d) - x r^3 mean(x g d))       (d = dL/d(normed), x = norm input)
+//   dg   : per-wave partial sums of d * x * r  -> dg_part[wave_global][D]
+//   if bout: bout = round(a * out) and *dot += sum(out * aux)   (next residual branch)
+// Waves own whole rows; ROWS_PER_WAVE rows each.
+constexpr int kNormBwdRowsPerWave = 16;
+
+template <class T>
+__global__ void __launch_bounds__(256)
+rmsnorm_bwd_kernel(const T* __restrict__ d, const T* __restrict__ x, const float* __restrict__ g,
+                   const float* __restrict__ rstd, const T* __restrict__ resid, T* __restrict__ out,
+                   float* __restrict__ dg_part, int64_t N, int D, const float* a, T* bout,
+                   const T* aux, float* dot) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  float dga[kMaxDChunks][8];
+#pragma unroll
+  for (int j = 0; j < kMaxDChunks; ++j)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dga[j][k] = 0.f;
+  const float av = bout ? *a : 0.f;
+  float dsum = 0.f;
+  for (int i = 0; i < kNormBwdRowsPerWave; ++i) {
+    const int64_t row = wg * kNormBwdRowsPerWave + i;
+    if (row >= N) break;
+    const float r = rstd[row];
+    const T* dr = d + row * D;
+    const T* xr = x + row * D;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxDChunks; ++j) {
+      const int c = lane * 8 + j * 512;
+      if (c < D) {
+        float dv[8], xv[8], gv[8];
+        Vec8<T>::load(dr + c, dv);
+        Vec8<T>::load(xr + c, xv);
+        Vec8<float>::load(g + c, gv);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          s += xv[k] * gv[k] * dv[k];
+          dga[j][k] += dv[k] * xv[k] * r;
+        }
+      }
+    }
+    s = wave_sum(s) / (float)D;
+    const float r3s = r * r * r * s;
+#pragma unroll
+    for (int j = 0; j < kMaxDChunks; ++j) {
+      const int c = lane * 8 + j * 512;
+      if (c < D) {
+        float dv[8], xv[8], gv[8], rv[8];
+        Vec8<T>::load(dr + c, dv);
+        Vec8<T>::load(xr + c, xv);
+        Vec8<float>::load(g + c, gv);
+        Vec8<T>::load(resid + row * D + c, rv);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rv[k] = Elem<T>::rnd(rv[k] + (r * (gv[k] * dv[k]) - xv[k] * r3s));
+        Vec8<T>::store(out + row * D + c, rv);
+        if (bout) {
+          float ax[8], bv[8];
+          Vec8<T>::load(aux + row * D + c, ax);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            dsum += rv[k] * ax[k];
+            bv[k] = av * rv[k];
+          }
+          Vec8<T>::store(bout + row * D + c, bv);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxDChunks; ++j) {
+    const int c = lane * 8 + j * 512;
+    if (c < D) Vec8<float>::store(dg_part + wg * D + c, dga[j]);
+  }
+  if (bout) {
+    dsum = wave_sum(dsum);
+    if (lane == 0) atomicAdd(dot, dsum);
+  }
+}
+
+inline int64_t rmsnorm_bwd_partials(int64_t N) { return cdiv(cdiv(N, kNormBwdRowsPerWave), 4) * 4; }
+
+template <class T>
+inline hipError_t launch_rmsnorm_bwd(const T* d, const T* x, const float* g, const float* rstd,
+                                     const T* resid, T* out, float* dg_part, int64_t N, int D,
+                                     const float* a, T* bout, const T* aux, float* dot, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const int64_t blocks = cdiv(cdiv(N, kNormBwdRowsPerWave), 4);
+  hipLaunchKernelGGL((rmsnorm_bwd_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, s, d, x, g, rstd, resid,
+                     out, dg_part, N, D, a, bout, aux, dot);
+  return hipGetLastError();
+}
+
+// out[c] = sum_p part[p][c]
+__global__ void colsum_kernel(const float* __restrict__ part, int64_t P, int D, float* __restrict__ out) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= D) return;
+  float s = 0.f;
+  for (int64_t p = 0; p < P; ++p) s += part[p * D + c];
+  out[c] = s;
+}
+inline hipError_t launch_colsum(const float* part, int64_t P, int D, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)cdiv(D, 256)), dim3(256), 0, s, part, P, D, out);
+  return hipGetLastError();
+}
+
+// out = round(a * dy); *dot += sum(dy * aux); optional amax of out. (dm = a_mlp dy, da_mlp = sum dy m)
+template <class T>
+__global__ void __launch_bounds__(256)
+scale_dot_kernel(const T* __restrict__ dy, const T* __restrict__ aux, const float* a, T* __restrict__ out,
+                 int64_t n8, float* dot, float* amax) {
+  const float av = *a;
+  float ds = 0.f, mx = 0.f;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    float dv[8], xv[8];
+    Vec8<T>::load(dy + i * 8, dv);
+    Vec8<T>::load(aux + i * 8, xv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ds += dv[k] * xv[k];
+      dv[k] = Elem<T>::rnd(av * dv[k]);
+      mx = fmaxf(mx, fabsf(dv[k]));
+    }
+    Vec8<T>::store(out + i * 8, dv);
+  }
+  ds = wave_sum(ds);
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) {
+    atomicAdd(dot, ds);
+    if (amax) atomic_max_nonneg(amax, mx);
+  }
+}
+template <class T>
+inline hipError_t launch_scale_dot(const T* dy, const T* aux, const float* a, T* out, int64_t n, float* dot,
+                                   float* amax, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  if (n8 <= 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>(cdiv(n8, 256), 2048);
+  hipLaunchKernelGGL((scale_dot_kernel<T>), dim3(blocks), dim3(256), 0, s, dy, aux, a, out, n8, dot, amax);
+  return hipGetLastError();
+}
+
+// Batched 2-D transpose through a 64 x 64 LDS tile:
+//   dst[z][c][r] = src[z][r][c] for r < rows, c < cols;  dst[z][c][r] = 0 for rows <= r < rows_pad.
+// Batch z = blockIdx.z splits as (z / zdiv, z % zdiv) with source offset zo*sb_outer + zi*sb_inner
+// and destination offset z * sd.
+template <class T>
+__global__ void __launch_bounds__(256)
+transpose_kernel(const T* __restrict__ src, int64_t rows, int cols, int64_t lds, T* __restrict__ dst,
+                 int64_t ldd, int64_t rows_pad, int zdiv, int64_t sb_outer, int64_t sb_inner, int64_t sd) {
+  __shared__ float tile[64][65];
+  const int z = blockIdx.z;
+  src += (int64_t)(z / zdiv) * sb_outer + (int64_t)(z % zdiv) * sb_inner;
+  dst += (int64_t)z * sd;
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
+  const int c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i;
+    const int c = c0 + tx;
+    tile[i][tx] = (r < rows && c < cols) ? Elem<T>::ld(src, r * lds + c) : 0.f;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i;
+    const int64_t r = r0 + tx;
+    if (c < cols && r < rows_pad) Elem<T>::st(dst, (int64_t)c * ldd + r, tile[tx][i]);
+  }
+}
+template <class T>
+inline hipError_t launch_transpose(const T* src, int64_t rows, int cols, int64_t lds, T* dst, int64_t ldd,
+                                   int64_t rows_pad, int batch, int zdiv, int64_t sb_outer, int64_t sb_inner,
+                                   int64_t sd, hipStream_t s) {
+  if (cols <= 0 || rows_pad <= 0 || batch <= 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv(cols, 64), (unsigned)cdiv(rows_pad, 64), (unsigned)batch);
+  hipLaunchKernelGGL((transpose_kernel<T>), grid, dim3(256), 0, s, src, rows, cols, lds, dst, ldd, rows_pad,
+                     zdiv, sb_outer, sb_inner, sd);
+  return hipGetLastError();
+}
+template <class T>
+inline hipError_t transpose2d(const T* src, int64_t rows, int cols, int64_t lds, T* dst, int64_t ldd,
+                              int64_t rows_pad, hipStream_t s) {
+  return launch_transpose(src, rows, cols, lds, dst, ldd, rows_pad, 1, 1, 0, 0, 0, s);
+}
+
+// fp32 -> storage type conversion (weight gradients accumulated in fp32)
+template <class T>
+__global__ void convert_kernel(const float* __restrict__ src, T* __restrict__ dst, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    Elem<T>::st(dst, i, src[i]);
+}
+template <class T>
+inline hipError_t launch_convert(const float* src, T* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>(cdiv(n, 256), 8192);
+  hipLaunchKernelGGL((convert_kernel<T>), dim3(blocks), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace ll

@@ -1,0 +1,142 @@
+// Dynamic tensorwise e4m3fn quantisation (two phases: global amax, then cast), as used by the
+// FP8 GEMMs of the MLP [hn.213312.xyz translation, 提升吞吐量 / Increasing throughput: FP8 with
+// dynamic scaling on three GEMMs; linlog.top article, 吞吐量优化: torch._scaled_mm, dynamic
+// tensorwise scaling].
+//   amax      = max |x|                           (order-independent, so bit-reproducible)
+//   scale     = 2^floor(log2(fl32(448 / max(amax, 1e-12))))   (power of two: x * scale is exact
+//               and a rounding-level change of amax leaves the scale unchanged)
+//   inv_scale = 1 / scale                         (exact)
+//   q         = e4m3fn_rne(clamp(fl32(x * scale), -448, 448))
+// The cast kernel writes the row-major codes and, optionally, the transposed codes (the K-major
+// operand of the weight-gradient GEMMs) through a 64 x 64 byte tile in LDS. The transposed
+// buffer may have more columns than `rows` (a padded leading dimension); those are zero-filled
+// so a GEMM may run its K loop over whole 128-byte tiles.
+#pragma once
+#include "common.h"
+
+namespace ll {
+namespace {
+
+struct QScale {        // per-tensor quantisation state (device memory)
+  float amax;
+  float scale;
+  float inv_scale;
+  float pad;
+};
+
+__global__ void fill_f32_kernel(float* p, float v, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+inline hipError_t fill_f32(float* p, float v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>(cdiv(n, 256), 4096);
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+// amax of x [rows, cols] (ld elements per row); cols % 8 == 0 and ld % 8 == 0.
+template <class T>
+__global__ void __launch_bounds__(256) amax_kernel(const T* __restrict__ x, int64_t rows, int cols, int64_t ld, float* amax) {
+  const int segs = cols / 8;
+  float mx = 0.f;
+  const int64_t total = rows * segs;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / segs;
+    const int c = (int)(i - r * segs) * 8;
+    float v[8];
+    Vec8<T>::load(x + r * ld + c, v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mx = fmaxf(mx, fabsf(v[k]));
+  }
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax, mx);
+}
+
+template <class T>
+inline hipError_t launch_amax(const T* x, int64_t rows, int cols, int64_t ld, float* amax, hipStream_t s) {
+  const int64_t total = rows * (cols / 8);
+  if (total <= 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>(cdiv(total, 256), 2048);
+  hipLaunchKernelGGL((amax_kernel<T>), dim3(blocks), dim3(256), 0, s, x, rows, cols, ld, amax);
+  return hipGetLastError();
+}
+
+__device__ __forceinline__ void scales_from_amax(float amax, float& scale, float& inv) {
+  const float ratio = __fdiv_rn(448.0f, fmaxf(amax, 1e-12f));   // normal: in [1.3e-36, 4.5e14]
+  scale = __uint_as_float(__float_as_uint(ratio) & 0x7F800000u);  // clear the mantissa
+  inv = __fdiv_rn(1.0f, scale);                                   // exact for a power of two
+}
+
+__device__ __forceinline__ uint8_t quant_one(float x, float scale) {
+  float y = __fmul_rn(x, scale);
+  y = fminf(fmaxf(y, -448.0f), 448.0f);
+  return f32_to_e4m3(y);
+}
+
+// Cast of x [rows, cols] with the scale derived from qs->amax. Block = 64 rows x 64 cols tile,
+// 256 threads; each thread converts 16 consecutive elements of one row.
+//   q   [rows, ldq] (or null); qt [cols, ldqt] (or null) with ldqt >= rows_pad >= rows;
+//   the grid covers rows_pad rows so qt[:, rows:rows_pad] is zero-filled.
+// cols % 16 == 0, ld % 8 == 0, ldq % 16 == 0 (any ldqt; 16-byte stores when ldqt % 16 == 0). Block (0,0) thread 0 also writes qs->scale / qs->inv_scale.
+template <class T>
+__global__ void __launch_bounds__(256)
+cast_e4m3_kernel(const T* __restrict__ x, int64_t rows, int cols, int64_t ld, QScale* qs,
+                 uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qt, int64_t ldqt,
+                 int64_t rows_pad, float* scale_out, float* inv_out) {
+  __shared__ uint32_t tile[64][17];                  // 64 rows x 64 bytes (+4 B pad per row)
+  float scale, inv;
+  scales_from_amax(qs->amax, scale, inv);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    qs->scale = scale;
+    qs->inv_scale = inv;
+    if (scale_out) *scale_out = scale;
+    if (inv_out) *inv_out = inv;
+  }
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
+  const int c0 = blockIdx.x * 64;
+  const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
+  const int64_t r = r0 + tr;
+  const int c = c0 + tc;
+  uint32_t w[4] = {0, 0, 0, 0};
+  if (r < rows && c < cols) {
+    float v[16];
+    Vec8<T>::load(x + r * ld + c, *reinterpret_cast<float(*)[8]>(v));
+    Vec8<T>::load(x + r * ld + c + 8, *reinterpret_cast<float(*)[8]>(v + 8));
+#pragma unroll
+    for (int k = 0; k < 16; ++k) w[k >> 2] |= (uint32_t)quant_one(v[k], scale) << (8 * (k & 3));
+    if (q) *reinterpret_cast<uint4*>(q + r * ldq + c) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (!qt) return;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) tile[tr][(tc >> 2) + k] = w[k];
+  __syncthreads();
+  // transposed: thread -> output row (source column) cc = tid / 4, 16 source rows
+  const int cc = threadIdx.x >> 2, rr = (threadIdx.x & 3) * 16;
+  if (c0 + cc < cols && r0 + rr < rows_pad) {
+    const unsigned char* tb = reinterpret_cast<const unsigned char*>(&tile[0][0]);
+    uint8_t* dst = qt + (int64_t)(c0 + cc) * ldqt + r0 + rr;
+    if ((ldqt & 15) == 0 && r0 + rr + 16 <= rows_pad) {
+      uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < 16; ++k) o[k >> 2] |= (uint32_t)tb[(rr + k) * 68 + cc] << (8 * (k & 3));
+      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+      for (int k = 0; k < 16 && r0 + rr + k < rows_pad; ++k) dst[k] = tb[(rr + k) * 68 + cc];
+    }
+  }
+}
+
+template <class T>
+inline hipError_t launch_cast_e4m3(const T* x, int64_t rows, int cols, int64_t ld, QScale* qs,
+                                   uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, int64_t rows_pad,
+                                   float* scale_out, float* inv_out, hipStream_t s) {
+  const int64_t rp = qt ? rows_pad : rows;
+  const int64_t gy = cdiv(std::max<int64_t>(rp, 1), 64);
+  const int gx = (int)cdiv(std::max(cols, 1), 64);
+  hipLaunchKernelGGL((cast_e4m3_kernel<T>), dim3(gx, (unsigned)gy), dim3(256), 0, s, x, rows, cols, ld, qs,
+                     q, ldq, qt, ldqt, rp, scale_out, inv_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace ll

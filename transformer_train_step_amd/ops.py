@@ -1,0 +1,129 @@
+"""Torch-side convenience around the C ABI: allocates outputs, `saved` and workspace buffers with
+torch on the current device and calls libll. No arithmetic happens here."""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class LayerConfig:
+    batch: int
+    seq: int
+    d_model: int = 3072
+    n_q_heads: int = 24
+    n_kv_heads: int = 8
+    head_dim: int = 128
+    d_ff: int = 12288
+    dtype: str = "bf16"          # 'bf16' or 'fp32'
+    fp8_mlp: bool = True
+    value_embed: bool = False
+    ve_rows: int = 50304
+    rms_eps: float = 1e-6
+    rope_theta: float = 10000.0
+
+    def c_struct(self) -> L.LayerCfg:
+        return L.LayerCfg(dtype=L.LL_BF16 if self.dtype == "bf16" else L.LL_F32, fp8_mlp=int(self.fp8_mlp),
+                          batch=self.batch, seq=self.seq, d_model=self.d_model, n_q_heads=self.n_q_heads,
+                          n_kv_heads=self.n_kv_heads, head_dim=self.head_dim, d_ff=self.d_ff,
+                          rms_eps=self.rms_eps, rope_theta=self.rope_theta,
+                          has_value_embed=int(self.value_embed), ve_rows=self.ve_rows if self.value_embed else 0)
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seq
+
+    @property
+    def qkv_dim(self) -> int:
+        return (self.n_q_heads + 2 * self.n_kv_heads) * self.head_dim
+
+
+PARAM_NAMES = ("attn_norm_w", "w_qkv", "w_o", "mlp_norm_w", "w_fc", "w_proj", "ve_table", "resid_attn", "resid_mlp")
+
+
+def param_shapes(c: LayerConfig) -> dict:
+    D, F = c.d_model, c.d_ff
+    s = {"attn_norm_w": (D,), "w_qkv": (c.qkv_dim, D), "w_o": (D, c.n_q_heads * c.head_dim),
+         "mlp_norm_w": (D,), "w_fc": (F, D), "w_proj": (D, F), "resid_attn": (1,), "resid_mlp": (1,)}
+    if c.value_embed:
+        s["ve_table"] = (c.ve_rows, c.n_kv_heads * c.head_dim)
+    return s
+
+
+def _is_fp32_param(name: str) -> bool:
+    return name in ("attn_norm_w", "mlp_norm_w", "resid_attn", "resid_mlp")
+
+
+class Layer:
+    """One decoder layer bound to a configuration: owns the `saved` and workspace buffers."""
+
+    def __init__(self, cfg: LayerConfig, device="cuda"):
+        self.cfg = cfg
+        self.c = cfg.c_struct()
+        self.saved_bytes = L.ll_layer_saved_bytes(self.c)
+        self.ws_bytes = L.ll_layer_workspace_bytes(self.c)
+        if self.saved_bytes == 0 or self.ws_bytes == 0:
+            raise L.LLError(L.LL_ERR_INVALID_ARG, "ll_layer_*_bytes", "invalid layer configuration")
+        self.saved = torch.empty(self.saved_bytes, dtype=torch.uint8, device=device)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.device = device
+
+    def c_params(self, p: dict) -> L.LayerParams:
+        return L.LayerParams(**{k: L.ptr(p.get(k)) for k in PARAM_NAMES})
+
+    def new_grads(self) -> dict:
+        g = {}
+        for k, shp in param_shapes(self.cfg).items():
+            dt = torch.float32 if (_is_fp32_param(k) or k == "ve_table") else self.cfg.torch_dtype
+            g[k] = (torch.zeros if k == "ve_table" else torch.empty)(shp, dtype=dt, device=self.device)
+        return g
+
+    def forward(self, p: dict, x: torch.Tensor, ids: torch.Tensor | None, y: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+        if y is None:
+            y = torch.empty_like(x)
+        L.ll_layer_fwd(self.c, self.c_params(p), x, ids, y, self.saved, self.saved_bytes, self.ws, self.ws_bytes,
+                       stream)
+        return y
+
+    def backward(self, p: dict, x, ids, dy, dx=None, grads: dict | None = None, stream=None):
+        if dx is None:
+            dx = torch.empty_like(dy)
+        if grads is None:
+            grads = self.new_grads()
+        cg = L.LayerGrads(**{k: L.ptr(grads.get(k)) for k in PARAM_NAMES})
+        L.ll_layer_bwd(self.c, self.c_params(p), x, ids, self.saved, self.saved_bytes, dy, dx, cg, self.ws,
+                       self.ws_bytes, stream)
+        return dx, grads
+
+
+class FusedLCE:
+    """Fused linear cross-entropy bound to (dtype, n, d, v, token_chunk): owns its workspace."""
+
+    def __init__(self, dtype: str, n: int, d: int, v: int, token_chunk: int = 0, device="cuda"):
+        self.dt = L.LL_BF16 if dtype == "bf16" else L.LL_F32
+        self.n, self.d, self.v, self.chunk = n, d, v, token_chunk
+        self.ws_bytes = L.ll_fused_lce_workspace_bytes(self.dt, n, d, v, token_chunk)
+        if self.ws_bytes == 0:
+            raise L.LLError(L.LL_ERR_INVALID_ARG, "ll_fused_lce_workspace_bytes", "invalid sizes")
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.loss = torch.empty(1, dtype=torch.float32, device=device)
+        self.device = device
+
+    def __call__(self, hidden, weight, targets, softcap=15.0, ignore_index=-100, grad_scale=1.0, grads=True,
+                 lse=None, d_hidden=None, d_weight=None, stream=None):
+        if grads:
+            d_hidden = torch.empty_like(hidden) if d_hidden is None else d_hidden
+            d_weight = torch.empty_like(weight) if d_weight is None else d_weight
+        L.ll_fused_lce_fwd_bwd(self.dt, hidden, weight, targets, self.n, self.d, self.v, softcap, ignore_index,
+                               grad_scale, self.chunk, self.loss, lse, d_hidden if grads else None,
+                               d_weight if grads else None, self.ws, self.ws_bytes, stream)
+        return self.loss, d_hidden, d_weight
