@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Throughput of the little-lm training-step hot path on one MI355X.
+
+A step is one pass of the whole hot path over one micro-batch of 40 x 1024 synthetic tokens:
+forward of one 3.8B decoder layer (FP8 e4m3 MLP GEMMs, bf16 elsewhere), the fused linear
+cross-entropy (softcap 15, 50304-padded vocab) on its output with loss and both gradients, and the
+layer backward from that gradient. Every kernel is libll's (HIP, gfx950); inputs are resident in
+HBM before the timed region. Prints one JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload layer_lce|layer|layer_ve_2k|lce]
+                    [--no-cpu-baseline]
+
+FLOP accounting (algorithmic, not executed work): per token of one layer, fwd + bwd,
+6 * P_mm + 6 * Hq * Dh * (T + 1) with P_mm = 100,663,296 matrix weights (causal attention counted
+at half of full); the loss adds 6 * N * V * D. 60,000 tokens/s/GPU x 28 layers x that layer count
+gives the ~1,047 TFLOP/s per B200 printed on the hn.213312.xyz translation ("结果 / Results"), so
+the same formula prices this step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "train tokens/sec per MI355X (3.8B layer fwd+bwd + fused LCE); % dense MFMA peak"
+PEAK_BF16 = 2.5e15          # MI355X dense bf16 MFMA, FLOP/s
+PEAK_FP8 = 5.0e15           # dense e4m3
+PEAK_HBM = 8.0e12           # bytes/s
+
+D, HQ, HKV, DH, F, V, V_REAL = 3072, 24, 8, 128, 12288, 50304, 50257
+P_MM = D * (HQ + 2 * HKV) * DH + D * HQ * DH + 2 * D * F          # 100,663,296
+
+
+def layer_flops_per_token(seq: int, hq: int = HQ, dh: int = DH, p_mm: int = P_MM) -> int:
+    return 6 * p_mm + 6 * hq * dh * (seq + 1)
+
+
+def lce_flops(n: int, v: int = V, d: int = D) -> int:
+    return 6 * n * v * d
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+WORKLOADS = {
+    "layer_lce": dict(batch=40, seq=1024, ve=False, layer=True, lce=True,
+                      desc="3.8B decoder layer fwd+bwd (40x1024 tokens, FP8 e4m3 MLP, no value embedding) "
+                           "+ fused linear cross-entropy fwd+bwd on its output (40960x3072 @ 50304x3072, softcap 15)"),
+    "layer": dict(batch=40, seq=1024, ve=False, layer=True, lce=False,
+                  desc="3.8B decoder layer fwd+bwd (40x1024 tokens, FP8 e4m3 MLP)"),
+    "layer_ve_2k": dict(batch=20, seq=2048, ve=True, layer=True, lce=False,
+                        desc="3.8B value-embedding decoder layer fwd+bwd (20x2048 tokens, FP8 e4m3 MLP)"),
+    "lce": dict(batch=40, seq=1024, ve=False, layer=False, lce=True,
+                desc="fused linear cross-entropy fwd+bwd (hidden 40960x3072 bf16 N(0,1), head 50304x3072 "
+                     "N(0,0.02), softcap 15)"),
+}
+
+
+def step_flops(w: dict) -> int:
+    n = w["batch"] * w["seq"]
+    f = 0
+    if w["layer"]:
+        f += layer_flops_per_token(w["seq"]) * n
+    if w["lce"]:
+        f += lce_flops(n)
+    return f
+
+
+def cpu_baseline(seq: int, ve: bool, with_layer: bool, with_lce: bool) -> dict:
+    """The oracle, as it stands, on a bounded sample: one sequence of `seq` tokens through the same
+    step (layer fwd -> loss -> layer bwd) at full model width, float64 numpy on the host."""
+    import synth
+    from oracle import lce as olce
+    from oracle import model as om
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or os.cpu_count()
+    except Exception:
+        threads = os.cpu_count()
+    s = synth.LayerShape(batch=1, seq=seq, value_embed=ve)
+    inp = synth.layer_inputs(s, seed=0)
+    if with_lce:
+        w_head = synth.normal((V, D), 0.02, 0, synth.K_WHEAD, "bf16")
+        tg = synth.uniform_ints((seq,), V_REAL, 0, synth.K_TARGETS)
+    t0 = time.perf_counter()                      # inputs drawn; time the oracle only
+    y, dy = inp.x, inp.dy
+    if with_layer:
+        p, d = om.params_from_inputs(inp), om.dims_from_shape(s)
+        y, cache = om.layer_fwd(p, inp.x, inp.ids, d)
+    if with_lce:
+        dy = olce.lce_fwd_bwd(y, w_head, tg, softcap=15.0, mode="bf16")["dh"]
+    if with_layer:
+        om.layer_bwd(p, cache, dy, d)
+    sec = time.perf_counter() - t0
+    return {"value": round(seq / sec, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 sequence x {seq} tokens of the same step at full width (float64 numpy), "
+                      f"{sec:.1f} s", "seconds": round(sec, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="layer_lce", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true", help="skip the traced pass (roofline)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import transformer_train_step_amd as ll
+    from transformer_train_step_amd import _lib as L
+    from transformer_train_step_amd.ops import FusedLCE, Layer, LayerConfig
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    L.lib()
+    w = WORKLOADS[args.workload]
+    B, T = w["batch"], w["seq"]
+    N = B * T
+    dev = "cuda"
+    log(f"[bench] workload {args.workload}: {w['desc']}")
+
+    def to_dev(a, dt=torch.bfloat16):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).to(dev)
+
+    t_in = time.perf_counter()
+    s = synth.LayerShape(batch=B, seq=T, value_embed=w["ve"])
+    inp = synth.layer_inputs(s, seed=0)
+    x = to_dev(inp.x)
+    ids = torch.from_numpy(inp.ids).to(dev)
+    p = None
+    layer = None
+    if w["layer"]:
+        cfg = LayerConfig(batch=B, seq=T, value_embed=w["ve"])
+        layer = Layer(cfg, dev)
+        p = {"attn_norm_w": torch.from_numpy(inp.g_attn).to(dev), "mlp_norm_w": torch.from_numpy(inp.g_mlp).to(dev),
+             "w_qkv": to_dev(inp.w_qkv), "w_o": to_dev(inp.w_o), "w_fc": to_dev(inp.w_fc), "w_proj": to_dev(inp.w_proj),
+             "resid_attn": torch.ones(1, dtype=torch.float32, device=dev),
+             "resid_mlp": torch.ones(1, dtype=torch.float32, device=dev)}
+        if w["ve"]:
+            p["ve_table"] = to_dev(inp.ve_table)
+        grads = layer.new_grads()
+        y = torch.empty_like(x)
+        dx = torch.empty_like(x)
+    dy = to_dev(inp.dy)
+    lce = None
+    if w["lce"]:
+        w_head = to_dev(synth.normal((V, D), 0.02, 0, synth.K_WHEAD, "bf16"))
+        targets = torch.from_numpy(synth.uniform_ints((N,), V_REAL, 0, synth.K_TARGETS)).to(dev)
+        lce = FusedLCE("bf16", N, D, V, token_chunk=8192, device=dev)
+        dh_buf = torch.empty_like(x)
+        dw_head = torch.empty_like(w_head)
+    del inp
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t_in:.1f} s to generate)")
+
+    def step():
+        h = x
+        if layer is not None:
+            layer.forward(p, x, ids, y)
+            h = y
+        g = dy
+        if lce is not None:
+            lce(h, w_head, targets, d_hidden=dh_buf, d_weight=dw_head)
+            g = dh_buf
+        if layer is not None:
+            layer.backward(p, x, ids, g, dx=dx, grads=grads)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+
+    # timed region: K steps, synchronised on both sides
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
+
+    flops = step_flops(w)
+    tok_s = N / (ms * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16+e4m3",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, uniform token ids)",
+        "config": {"workload": w["desc"], "tokens_per_step": N, "batch": B, "seq_len": T},
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / PEAK_BF16, 2),
+        "algorithmic_flops_per_step": flops,
+    }
+
+    # traced pass: the same K steps with every launch bracketed by HIP events on its stream
+    if not args.no_trace:
+        L.llt_trace_begin(4096)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        L.llt_trace_end()
+        traced_ms = ev0.elapsed_time(ev1) / args.steps
+        recs = L.llt_trace_read()
+        per = {}
+        for tag, t, mnk in recs:
+            e = per.setdefault(tag, {"launches": 0, "ms": 0.0, "flops": 0})
+            e["launches"] += 1
+            e["ms"] += t
+            e["flops"] += 2 * mnk[0] * mnk[1] * mnk[2]
+        top = sorted(per.items(), key=lambda kv: -kv[1]["ms"])
+        dom_tag, dom = top[0]
+        avg_ms = dom["ms"] / dom["launches"]
+        flops_launch = dom["flops"] / dom["launches"]
+        peak = PEAK_FP8 if "_e4m3_" in dom_tag else PEAK_BF16
+        achieved = flops_launch / (avg_ms * 1e-3) / 1e12 if flops_launch else 0.0
+        out["roofline"] = {"kernel": dom_tag, "bound": "mfma", "achieved": round(achieved, 1),
+                           "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved * 1e12 / peak, 4),
+                           "traffic": None, "avg_launch_ms": round(avg_ms, 4),
+                           "flops_per_launch": int(flops_launch), "launches_per_step": dom["launches"] / args.steps}
+        out["kernel_breakdown_ms_per_step"] = {k: round(v["ms"] / args.steps, 3) for k, v in top[:12]}
+        out["traced_ms_per_step"] = round(traced_ms, 4)
+        log("[bench] per-kernel time per step (ms): " +
+            ", ".join(f"{k} {v['ms'] / args.steps:.2f}" for k, v in top[:12]))
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host (bounded sample)...")
+        seq = T if w["layer"] else 1024
+        out["cpu_baseline"] = cpu_baseline(seq, w["ve"], w["layer"], w["lce"])
+        log(f"[bench] oracle: {out['cpu_baseline']['value']} tokens/s on {out['cpu_baseline']['cores']} threads")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

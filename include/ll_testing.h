@@ -28,6 +28,21 @@ int llt_gemm_nt(int32_t op_dtype, const void* A, int64_t lda, const void* B, int
                 int32_t N, int32_t K, int32_t out_dtype, void* C, int64_t ldc, const float* inv_a,
                 const float* inv_b, void* stream);
 
+/* Launch trace: while tracing is on, every kernel launch of the library is bracketed by two HIP
+ * events recorded on the launch's own stream and tagged with the kernel's name (GEMMs as
+ * "gemm_<operand type>_<epilogue>"). Up to `capacity` launches are recorded per begin; later ones
+ * are not traced. The events are created by llt_trace_begin (the only call here that creates
+ * HIP objects) and reused until the capacity changes. Not thread-safe across concurrent
+ * begin/get on different threads beyond the internal lock; host-side bookkeeping only.
+ *   llt_trace_begin: reset and start recording; llt_trace_end: stop recording;
+ *   llt_trace_count: launches recorded; llt_trace_get: tag and duration (ms) of launch i, waiting
+ *   for its end event, and (if mnk is not NULL) the GEMM sizes M, N, K of that launch (0 for
+ *   launches that are not GEMMs). */
+int llt_trace_begin(int32_t capacity);
+int llt_trace_end(void);
+int32_t llt_trace_count(void);
+int llt_trace_get(int32_t i, const char** tag, float* ms, int64_t* mnk);
+
 #ifdef __cplusplus
 }
 #endif

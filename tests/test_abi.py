@@ -106,3 +106,21 @@ def test_lce_validation():
     need = ll.ll_fused_lce_workspace_bytes(1, 40960, 3072, 50304, 8192)
     assert 2e9 < need < 5e9
     assert ll.ll_fused_lce_workspace_bytes(9, 1, 64, 8, 0) == 0
+
+
+def test_flop_accounting_reproduces_pages_b200_rate():
+    """bench.py's per-token layer FLOP count reproduces the pages' ~1,047 TFLOP/s per B200 from
+    their ~480,000 tokens/s on 8 GPUs at 1024 context over 28 layers (tests/golden)."""
+    import bench
+    gold = {}
+    with open(os.path.join(ROOT, "tests", "golden", "b200_throughput.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                k, v = line.split()
+                gold[k] = float(v)
+    per_gpu = gold["tokens_per_s_node"] / gold["gpus"]
+    tf = per_gpu * gold["n_layers"] * bench.layer_flops_per_token(int(gold["seq"])) / 1e12
+    assert abs(tf - gold["tflops_per_gpu"]) / gold["tflops_per_gpu"] < 0.005, tf
+    assert bench.P_MM == 100_663_296
+    assert bench.layer_flops_per_token(1024) == 622_872_576

@@ -71,6 +71,11 @@ _SIGS = {
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "llt_gemm_nt": (c_int32, [c_int32, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_int32,
                               c_int32, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_void_p]),
+    "llt_trace_begin": (c_int32, [c_int32]),
+    "llt_trace_end": (c_int32, []),
+    "llt_trace_count": (c_int32, []),
+    "llt_trace_get": (c_int32, [c_int32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(c_float),
+                                ctypes.POINTER(c_int64)]),
 }
 
 ENTRY_POINTS = tuple(_SIGS)
@@ -188,3 +193,28 @@ def llt_gemm_nt(op_dtype, A, lda, B, ldb, M, N, K, out_dtype, C, ldc, inv_a=None
                 stream=None, raise_on_error=True):
     return _call("llt_gemm_nt", op_dtype, ptr(A), lda, ptr(B), ldb, M, N, K, out_dtype, ptr(C), ldc,
                  ptr(inv_a), ptr(inv_b), stream_handle(stream), raise_on_error=raise_on_error)
+
+
+def llt_trace_begin(capacity: int):
+    return _call("llt_trace_begin", capacity)
+
+
+def llt_trace_end():
+    return _call("llt_trace_end")
+
+
+def llt_trace_count() -> int:
+    return lib().llt_trace_count()
+
+
+def llt_trace_get(i: int):
+    tag = ctypes.c_char_p()
+    ms = c_float()
+    mnk = (c_int64 * 3)()
+    _call("llt_trace_get", i, ctypes.byref(tag), ctypes.byref(ms), mnk)
+    return tag.value.decode(), ms.value, (mnk[0], mnk[1], mnk[2])
+
+
+def llt_trace_read() -> list:
+    """[(tag, ms, (M, N, K))] of every launch recorded since llt_trace_begin."""
+    return [llt_trace_get(i) for i in range(llt_trace_count())]

@@ -6,6 +6,7 @@
 #include <string>
 
 #include "../../include/ll.h"
+#include "../../include/ll_testing.h"
 
 namespace ll {
 

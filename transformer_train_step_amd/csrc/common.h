@@ -108,6 +108,23 @@ __device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
   atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
 }
 
+// ------------------------------------------------------------------ launch tracing (host)
+// When tracing is on (llt_trace_begin), every launch is bracketed by two HIP events recorded on
+// the launch's own stream, tagged with the kernel's name; llt_trace_get reads the durations.
+// GEMM launches also record their (M, N, K).
+bool trace_on();
+int trace_open(const char* tag, hipStream_t s, int64_t m = 0, int64_t n = 0, int64_t k = 0);
+void trace_close(int slot, hipStream_t s);
+
+#define LL_LAUNCH_MNK(tag, m, n, k, kern, grid, block, shm, stream, ...)                          \
+  do {                                                                                          \
+    const int ll_slot_ = ::ll::trace_on() ? ::ll::trace_open((tag), (stream), (m), (n), (k)) : -1; \
+    hipLaunchKernelGGL(kern, grid, block, shm, stream, __VA_ARGS__);                            \
+    if (ll_slot_ >= 0) ::ll::trace_close(ll_slot_, (stream));                                   \
+  } while (0)
+#define LL_LAUNCH(tag, kern, grid, block, shm, stream, ...) \
+  LL_LAUNCH_MNK(tag, 0, 0, 0, kern, grid, block, shm, stream, __VA_ARGS__)
+
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 

@@ -16,6 +16,8 @@
 // staged through LDS in slabs of 64 rows and the epilogue functor then sees 8 consecutive
 // columns of one row per thread (16-byte coalesced stores, row reductions across 16 lanes).
 #pragma once
+#include <string>
+
 #include "common.h"
 
 namespace ll {
@@ -228,6 +230,7 @@ struct Deq {
 
 // C = round(deq(acc))
 template <class OutT> struct EpiStore {
+  static constexpr const char* kName = "store";
   static constexpr int kKind = kEpiPlain;
   OutT* C; int64_t ldc; Deq dq;
   __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
@@ -239,6 +242,7 @@ template <class OutT> struct EpiStore {
 
 // t = round(deq(acc)); branch[m, n] = t (optional); out = round(x + a * t)
 template <class T> struct EpiResidual {
+  static constexpr const char* kName = "residual";
   static constexpr int kKind = kEpiPlain;
   T* out; const T* x; T* branch; int64_t ld; const float* a; Deq dq;
   __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
@@ -257,6 +261,7 @@ template <class T> struct EpiResidual {
 
 // u = round(deq(acc)); r = round(relu(u)^2); stores u and r; returns max |r|
 template <class T> struct EpiRelu2 {
+  static constexpr const char* kName = "relu2";
   static constexpr int kKind = kEpiAmax;
   T* u; T* r; int64_t ld; Deq dq; float* amax;
   __device__ __forceinline__ float seg(int m, int n, float (&v)[8]) const {
@@ -277,6 +282,7 @@ template <class T> struct EpiRelu2 {
 
 // dr = round(deq(acc)); du = round(dr * 2 relu(u)); stores du; returns max |du|
 template <class T> struct EpiRelu2Bwd {
+  static constexpr const char* kName = "relu2_bwd";
   static constexpr int kKind = kEpiAmax;
   T* du; const T* u; int64_t ld; Deq dq; float* amax;
   __device__ __forceinline__ float seg(int m, int n, float (&v)[8]) const {
@@ -297,6 +303,7 @@ template <class T> struct EpiRelu2Bwd {
 // qkv = round(acc); on the v columns (n >= vcol0) of value-embedding layers:
 // v = round(v + table[ids[m], n - vcol0])
 template <class T> struct EpiQkv {
+  static constexpr const char* kName = "qkv";
   static constexpr int kKind = kEpiPlain;
   T* C; int64_t ldc; const T* table; int64_t ldt; const int32_t* ids; int vcol0;
   __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
@@ -314,6 +321,7 @@ template <class T> struct EpiQkv {
 
 // C32 = (accumulate ? C32 : 0) + acc   (fp32 accumulation across calls)
 struct EpiAcc32 {
+  static constexpr const char* kName = "acc32";
   static constexpr int kKind = kEpiPlain;
   float* C; int64_t ldc; int accumulate;
   __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
@@ -329,13 +337,26 @@ struct EpiAcc32 {
 };
 
 // ------------------------------------------------------------------ launcher
+template <class ET> struct OpName;
+template <> struct OpName<float> { static constexpr const char* s = "f32"; };
+template <> struct OpName<bf16> { static constexpr const char* s = "bf16"; };
+template <> struct OpName<fp8> { static constexpr const char* s = "e4m3"; };
+
+// trace tag of a GEMM instantiation: "gemm_<operand type>_<epilogue>"
+template <class ET, class Epi>
+inline const char* gemm_tag() {
+  static const std::string t = std::string("gemm_") + OpName<ET>::s + "_" + Epi::kName;
+  return t.c_str();
+}
+
 template <class ET, class Epi>
 inline hipError_t launch_gemm_nt(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N,
                                  int K, const Epi& epi, hipStream_t s) {
   constexpr int BM = 128, BN = 128;
   if (M <= 0 || N <= 0) return hipSuccess;
   const int64_t nb = cdiv(M, BM) * cdiv(N, BN);
-  hipLaunchKernelGGL((gemm_nt_kernel<ET, BM, BN, Epi>), dim3((unsigned)nb), dim3(kGemmThreads), 0, s,
+  const char* tag = gemm_tag<ET, Epi>();
+  LL_LAUNCH_MNK(tag, M, N, K, (gemm_nt_kernel<ET, BM, BN, Epi>), dim3((unsigned)nb), dim3(kGemmThreads), 0, s,
                      A, lda, B, ldb, M, N, K, epi);
   return hipGetLastError();
 }

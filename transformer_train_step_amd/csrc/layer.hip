@@ -178,7 +178,7 @@ int check_ptrs(std::initializer_list<const void*> ps, const char* what) {
 hipError_t rope_table(float2* cs, const Dims& d, hipStream_t s) {
   const int64_t n = d.T * (d.DH / 2);
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 4096)), dim3(256), 0, s, cs,
+  LL_LAUNCH("rope_table", rope_table_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 4096)), dim3(256), 0, s, cs,
                      (int)d.T, d.DH / 2, (double)d.theta);
   return hipGetLastError();
 }
@@ -200,13 +200,13 @@ int layer_fwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   }
   if (N > 0) {
     const int64_t threads = N * (d.Hq + d.Hkv) * (DH / 2);
-    hipLaunchKernelGGL((qk_prep_kernel<T, DH>), dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, s, CP<T>(sv.qkv),
+    LL_LAUNCH("qk_prep", (qk_prep_kernel<T, DH>), dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, s, CP<T>(sv.qkv),
                        (int64_t)d.QKVD, w.cs, P<T>(sv.qh), P<T>(sv.kh), sv.rq, sv.rk, N, (int)d.T, d.Hq, d.Hkv, d.eps);
     LL_HIP(hipGetLastError());
     LL_HIP(launch_transpose(CP<T>(sv.qkv) + d.vcol0, d.T, DH, (int64_t)d.QKVD, P<T>(w.vt), d.Tp, d.Tp,
                             (int)(d.B * d.Hkv), d.Hkv, d.T * d.QKVD, (int64_t)DH, (int64_t)DH * d.Tp, s));
     const int nqb = (int)cdiv(d.T, 128);
-    hipLaunchKernelGGL((attn_fwd_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nqb)), dim3(256), 0, s, CP<T>(sv.qh),
+    LL_LAUNCH("attn_fwd", (attn_fwd_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nqb)), dim3(256), 0, s, CP<T>(sv.qh),
                        CP<T>(sv.kh), CP<T>(w.vt), P<T>(sv.o), sv.lse, (int)d.B, (int)d.T, (int)d.Tp, d.Hq, d.Hkv);
     LL_HIP(hipGetLastError());
   }
@@ -341,7 +341,7 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   T* dqkv = P<T>(w.dqkv);
   if (N > 0) {
     const int64_t dthreads = N * d.Hq * (DH / 2);
-    hipLaunchKernelGGL((attn_delta_kernel<T, DH>), dim3((unsigned)cdiv(dthreads, 256)), dim3(256), 0, s,
+    LL_LAUNCH("attn_delta", (attn_delta_kernel<T, DH>), dim3((unsigned)cdiv(dthreads, 256)), dim3(256), 0, s,
                        CP<T>(w.dout), CP<T>(sv.o), w.delta, N, (int)d.T, d.Hq);
     LL_HIP(hipGetLastError());
     LL_HIP(launch_transpose(CP<T>(sv.qh), d.T, DH, (int64_t)d.QD, P<T>(w.qt), d.Tp, d.Tp, (int)(d.B * d.Hq), d.Hq,
@@ -351,22 +351,22 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
     LL_HIP(launch_transpose(CP<T>(w.dout), d.T, DH, (int64_t)d.QD, P<T>(w.dot), d.Tp, d.Tp, (int)(d.B * d.Hq), d.Hq,
                             d.T * d.QD, (int64_t)DH, (int64_t)DH * d.Tp, s));
     const int nkb = (int)cdiv(d.T, 64);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DH>), dim3((unsigned)(d.B * d.Hkv * nkb)), dim3(256), 0, s,
+    LL_LAUNCH("attn_bwd_dkdv", (attn_bwd_dkdv_kernel<T, DH>), dim3((unsigned)(d.B * d.Hkv * nkb)), dim3(256), 0, s,
                        CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout),
                        CP<T>(w.qt), CP<T>(w.dot), sv.lse, w.delta, w.dkh, dqkv + d.vcol0, (int64_t)d.QKVD,
                        (int)d.B, (int)d.T, (int)d.Tp, d.Hq, d.Hkv);
     LL_HIP(hipGetLastError());
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nkb)), dim3(256), 0, s,
+    LL_LAUNCH("attn_bwd_dq", (attn_bwd_dq_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nkb)), dim3(256), 0, s,
                        CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout),
                        CP<T>(w.kt), sv.lse, w.delta, w.dqh, (int)d.B, (int)d.T, (int)d.Tp, d.Hq, d.Hkv);
     LL_HIP(hipGetLastError());
     const int64_t pthreads = N * (d.Hq + d.Hkv) * (DH / 2);
-    hipLaunchKernelGGL((qk_post_kernel<T, DH>), dim3((unsigned)cdiv(pthreads, 256)), dim3(256), 0, s, w.dqh, w.dkh,
+    LL_LAUNCH("qk_post", (qk_post_kernel<T, DH>), dim3((unsigned)cdiv(pthreads, 256)), dim3(256), 0, s, w.dqh, w.dkh,
                        CP<T>(sv.qkv), (int64_t)d.QKVD, w.cs, sv.rq, sv.rk, dqkv, N, (int)d.T, d.Hq, d.Hkv);
     LL_HIP(hipGetLastError());
     if (d.ve) {
       const int64_t tot = N * d.KVD;
-      hipLaunchKernelGGL((ve_scatter_kernel<T>), dim3((unsigned)std::min<int64_t>(cdiv(tot, 256), 16384)), dim3(256),
+      LL_LAUNCH("ve_scatter", (ve_scatter_kernel<T>), dim3((unsigned)std::min<int64_t>(cdiv(tot, 256), 16384)), dim3(256),
                          0, s, CP<T>(dqkv) + d.vcol0, (int64_t)d.QKVD, ids, g->ve_table, (int64_t)d.KVD, N, d.KVD);
       LL_HIP(hipGetLastError());
     }

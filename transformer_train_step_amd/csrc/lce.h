@@ -16,6 +16,7 @@ namespace ll {
 namespace {
 
 template <class T> struct EpiLceLogits {
+  static constexpr const char* kName = "lce_logits";
   static constexpr int kKind = kEpiRowLse;
   T* z; int64_t ldz; float2* part; int nparts; float softcap; float inv_softcap;
   __device__ __forceinline__ void seg(int m, int n, float (&v)[8], float& mx, float& se) const {

@@ -58,7 +58,7 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
   LL_HIP(fill_f32(p.loss_acc, 0.f, 4, s));
   LL_HIP(fill_f32(reinterpret_cast<float*>(p.nv), 0.f, 4, s));
   if (n > 0) {
-    hipLaunchKernelGGL(count_valid_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 1024)), dim3(256), 0, s,
+    LL_LAUNCH("count_valid", count_valid_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 1024)), dim3(256), 0, s,
                        y, n, ignore, p.nv);
     LL_HIP(hipGetLastError());
   }
@@ -69,13 +69,13 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     const T* Hc = H + r0 * d;
     EpiLceLogits<T> epi{z, p.vpad, p.part, p.nparts, softcap, 1.f / softcap};
     LL_HIP(launch_gemm_nt(Hc, (int64_t)d, W, (int64_t)d, rows, (int)v, d, epi, s));
-    hipLaunchKernelGGL((lce_lse_kernel<T>), dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, s, p.part, p.nparts, z,
+    LL_LAUNCH("lce_lse", (lce_lse_kernel<T>), dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, s, p.part, p.nparts, z,
                        p.vpad, y + r0, rows, ignore, softcap, lse_out ? lse_out + r0 : nullptr, p.lse, p.loss_acc);
     LL_HIP(hipGetLastError());
     if (!grads) continue;
     const int rows_pad = (int)round_up(rows, 64);
     dim3 g((unsigned)cdiv(p.vpad, 64), (unsigned)cdiv(rows_pad, 64));
-    hipLaunchKernelGGL((lce_dz_kernel<T>), g, dim3(256), 0, s, z, p.vpad, p.lse, y + r0, rows, rows_pad, (int)v,
+    LL_LAUNCH("lce_dz", (lce_dz_kernel<T>), g, dim3(256), 0, s, z, p.vpad, p.lse, y + r0, rows, rows_pad, (int)v,
                        (int)p.vpad, ignore, softcap, grad_scale, p.nv, z, static_cast<T*>(p.dzt), (int64_t)rows_pad);
     LL_HIP(hipGetLastError());
     // dH_c = dz W  (B operand: W^T [D, Vpad])
@@ -91,7 +91,7 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     if (n == 0) LL_HIP(fill_f32(p.dw32, 0.f, v * d, s));     // no chunk ran: dW = 0
     LL_HIP(launch_convert(p.dw32, dW, v * d, s));
   }
-  hipLaunchKernelGGL(lce_finalize_kernel, dim3(1), dim3(1), 0, s, p.loss_acc, p.nv, loss);
+  LL_LAUNCH("lce_finalize", lce_finalize_kernel, dim3(1), dim3(1), 0, s, p.loss_acc, p.nv, loss);
   LL_HIP(hipGetLastError());
   return LL_OK;
 }

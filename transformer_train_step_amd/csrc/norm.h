@@ -53,7 +53,7 @@ template <class T>
 inline hipError_t launch_rmsnorm_fwd(const T* x, const float* g, T* y, float* rstd, int64_t N, int D,
                                      float eps, float* amax, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  hipLaunchKernelGGL((rmsnorm_fwd_kernel<T>), dim3((unsigned)cdiv(N, 4)), dim3(256), 0, s, x, g, y, rstd, N, D, eps, amax);
+  LL_LAUNCH("rmsnorm_fwd", (rmsnorm_fwd_kernel<T>), dim3((unsigned)cdiv(N, 4)), dim3(256), 0, s, x, g, y, rstd, N, D, eps, amax);
   return hipGetLastError();
 }
 
@@ -147,7 +147,7 @@ inline hipError_t launch_rmsnorm_bwd(const T* d, const T* x, const float* g, con
                                      const float* a, T* bout, const T* aux, float* dot, hipStream_t s) {
   if (N <= 0) return hipSuccess;
   const int64_t blocks = cdiv(cdiv(N, kNormBwdRowsPerWave), 4);
-  hipLaunchKernelGGL((rmsnorm_bwd_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, s, d, x, g, rstd, resid,
+  LL_LAUNCH("rmsnorm_bwd", (rmsnorm_bwd_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, s, d, x, g, rstd, resid,
                      out, dg_part, N, D, a, bout, aux, dot);
   return hipGetLastError();
 }
@@ -161,7 +161,7 @@ __global__ void colsum_kernel(const float* __restrict__ part, int64_t P, int D, 
   out[c] = s;
 }
 inline hipError_t launch_colsum(const float* part, int64_t P, int D, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)cdiv(D, 256)), dim3(256), 0, s, part, P, D, out);
+  LL_LAUNCH("colsum", colsum_kernel, dim3((unsigned)cdiv(D, 256)), dim3(256), 0, s, part, P, D, out);
   return hipGetLastError();
 }
 
@@ -197,7 +197,7 @@ inline hipError_t launch_scale_dot(const T* dy, const T* aux, const float* a, T*
   const int64_t n8 = n / 8;
   if (n8 <= 0) return hipSuccess;
   const int blocks = (int)std::min<int64_t>(cdiv(n8, 256), 2048);
-  hipLaunchKernelGGL((scale_dot_kernel<T>), dim3(blocks), dim3(256), 0, s, dy, aux, a, out, n8, dot, amax);
+  LL_LAUNCH("scale_dot", (scale_dot_kernel<T>), dim3(blocks), dim3(256), 0, s, dy, aux, a, out, n8, dot, amax);
   return hipGetLastError();
 }
 
@@ -234,7 +234,7 @@ inline hipError_t launch_transpose(const T* src, int64_t rows, int cols, int64_t
                                    int64_t sd, hipStream_t s) {
   if (cols <= 0 || rows_pad <= 0 || batch <= 0) return hipSuccess;
   dim3 grid((unsigned)cdiv(cols, 64), (unsigned)cdiv(rows_pad, 64), (unsigned)batch);
-  hipLaunchKernelGGL((transpose_kernel<T>), grid, dim3(256), 0, s, src, rows, cols, lds, dst, ldd, rows_pad,
+  LL_LAUNCH("transpose", (transpose_kernel<T>), grid, dim3(256), 0, s, src, rows, cols, lds, dst, ldd, rows_pad,
                      zdiv, sb_outer, sb_inner, sd);
   return hipGetLastError();
 }
@@ -254,7 +254,7 @@ template <class T>
 inline hipError_t launch_convert(const float* src, T* dst, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int blocks = (int)std::min<int64_t>(cdiv(n, 256), 8192);
-  hipLaunchKernelGGL((convert_kernel<T>), dim3(blocks), dim3(256), 0, s, src, dst, n);
+  LL_LAUNCH("convert", (convert_kernel<T>), dim3(blocks), dim3(256), 0, s, src, dst, n);
   return hipGetLastError();
 }
 

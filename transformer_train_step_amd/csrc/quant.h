@@ -30,7 +30,7 @@ __global__ void fill_f32_kernel(float* p, float v, int64_t n) {
 inline hipError_t fill_f32(float* p, float v, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int blocks = (int)std::min<int64_t>(cdiv(n, 256), 4096);
-  hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks), dim3(256), 0, s, p, v, n);
+  LL_LAUNCH("fill_f32", fill_f32_kernel, dim3(blocks), dim3(256), 0, s, p, v, n);
   return hipGetLastError();
 }
 
@@ -57,7 +57,7 @@ inline hipError_t launch_amax(const T* x, int64_t rows, int cols, int64_t ld, fl
   const int64_t total = rows * (cols / 8);
   if (total <= 0) return hipSuccess;
   const int blocks = (int)std::min<int64_t>(cdiv(total, 256), 2048);
-  hipLaunchKernelGGL((amax_kernel<T>), dim3(blocks), dim3(256), 0, s, x, rows, cols, ld, amax);
+  LL_LAUNCH("amax", (amax_kernel<T>), dim3(blocks), dim3(256), 0, s, x, rows, cols, ld, amax);
   return hipGetLastError();
 }
 
@@ -133,7 +133,7 @@ inline hipError_t launch_cast_e4m3(const T* x, int64_t rows, int cols, int64_t l
   const int64_t rp = qt ? rows_pad : rows;
   const int64_t gy = cdiv(std::max<int64_t>(rp, 1), 64);
   const int gx = (int)cdiv(std::max(cols, 1), 64);
-  hipLaunchKernelGGL((cast_e4m3_kernel<T>), dim3(gx, (unsigned)gy), dim3(256), 0, s, x, rows, cols, ld, qs,
+  LL_LAUNCH("cast_e4m3", (cast_e4m3_kernel<T>), dim3(gx, (unsigned)gy), dim3(256), 0, s, x, rows, cols, ld, qs,
                      q, ldq, qt, ldqt, rp, scale_out, inv_out);
   return hipGetLastError();
 }
