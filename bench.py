@@ -159,7 +159,7 @@ def main():
     if w["lce"]:
         w_head = to_dev(synth.normal((V, D), 0.02, 0, synth.K_WHEAD, "bf16"))
         targets = torch.from_numpy(synth.uniform_ints((N,), V_REAL, 0, synth.K_TARGETS)).to(dev)
-        lce = FusedLCE("bf16", N, D, V, token_chunk=8192, device=dev)
+        lce = FusedLCE("bf16", N, D, V, token_chunk=10240, device=dev)
         dh_buf = torch.empty_like(x)
         dw_head = torch.empty_like(w_head)
     del inp

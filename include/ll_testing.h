@@ -16,17 +16,25 @@ extern "C" {
 
 typedef enum { LLT_OP_F32 = 0, LLT_OP_BF16 = 1, LLT_OP_E4M3 = 2 } llt_op_dtype;
 
-/* C[m, n] = deq * sum_k A[m, k] B[n, k]  (both operands K-contiguous, row-major), the MFMA GEMM
- * of every projection of the layer and of the LM head.
- *   op_dtype: LLT_OP_F32 (fp32 MFMA), LLT_OP_BF16 (bf16 MFMA), LLT_OP_E4M3 (e4m3 MFMA).
- *   A [M, lda], B [N, ldb]: K must be a multiple of 128 bytes of the operand type
- *   (32 fp32 / 64 bf16 / 128 e4m3); lda, ldb >= K with rows 16-byte aligned.
+/* C[m, n] = deq * sum_k A(m, k) B(n, k), the MFMA GEMM of every projection of the layer and of the
+ * LM head, with each operand K-major (A(m, k) = A[m * lda + k]) or MN-major (A(m, k) = A[k * lda + m]).
+ *   op_dtype: LLT_OP_F32 (fp32 MFMA), LLT_OP_BF16 (bf16 MFMA), LLT_OP_E4M3 (e4m3 MFMA). MN-major
+ *   operands are bf16 only (read with LDS transpose reads) and need M (resp. N) % 8 == 0.
+ *   K-major operands are read in whole K tiles of 128 bytes (32 fp32 / 64 bf16 / 128 e4m3): their
+ *   rows must hold K rounded up to the tile, zero beyond K. MN-major operands may end at row K.
  *   out_dtype: LL_F32 or LL_BF16 (ll.h); C [M, ldc], N % 8 == 0, ldc % 8 == 0.
  *   inv_a, inv_b: device fp32 scalars multiplied into the result (deq = *inv_a * *inv_b), or both
- *   NULL (deq = 1). The result is rounded once to out_dtype. */
-int llt_gemm_nt(int32_t op_dtype, const void* A, int64_t lda, const void* B, int64_t ldb, int32_t M,
-                int32_t N, int32_t K, int32_t out_dtype, void* C, int64_t ldc, const float* inv_a,
-                const float* inv_b, void* stream);
+ *   NULL (deq = 1). The result is rounded once to out_dtype.
+ *   ws: >= 64 bytes of device scratch when an operand is MN-major (a zero row), else unused. */
+int llt_gemm(int32_t op_dtype, int32_t a_kmajor, int32_t b_kmajor, const void* A, int64_t lda, const void* B,
+             int64_t ldb, int32_t M, int32_t N, int32_t K, int32_t out_dtype, void* C, int64_t ldc,
+             const float* inv_a, const float* inv_b, void* ws, size_t ws_bytes, void* stream);
+
+/* Process-wide override of the GEMM block tile (for measurements): 0 = automatic (256 x 256 with
+ * 4 waves when that gives >= 256 tiles, else 128 x 128), 1 = 128 x 128 / 4 waves, 2 = 256 x 256 /
+ * 4 waves, 3 = 256 x 256 / 8 waves (2 x 4), 4 = 256 x 256 / 8 waves (4 x 2). The LCE logits GEMM
+ * always uses a 256-wide vocabulary tile (configs 2-4). */
+int llt_set_gemm_config(int32_t cfg);
 
 /* Launch trace: while tracing is on, every kernel launch of the library is bracketed by two HIP
  * events recorded on the launch's own stream and tagged with the kernel's name (GEMMs as

@@ -78,6 +78,7 @@ def test_e4m3_rounding_sweep():
 @pytest.mark.parametrize("op,M,N,K,out", [
     ("fp32", 200, 136, 64, "fp32"), ("fp32", 256, 512, 256, "fp32"),
     ("bf16", 300, 264, 320, "fp32"), ("bf16", 130, 1032, 3072, "bf16"), ("bf16", 1, 8, 64, "fp32"),
+    ("bf16", 4096, 4096, 3072, "bf16"), ("e4m3", 4096, 4096, 1024, "fp32"), ("fp32", 4096, 4096, 64, "fp32"),
     ("e4m3", 257, 200, 384, "fp32"), ("e4m3", 512, 384, 3072, "bf16"),
 ])
 def test_gemm_nt_parity(op, M, N, K, out):
@@ -116,6 +117,31 @@ def test_gemm_nt_parity(op, M, N, K, out):
         assert_close(got, ref, 1e-4, f"gemm {op}", elem_rtol=2e-3)
     else:
         assert_close(got, ref, 1e-5, f"gemm {op}", elem_rtol=1e-4)
+
+
+@pytest.mark.parametrize("ak,bk,M,N,K", [
+    (True, False, 300, 264, 320), (False, True, 264, 136, 256), (False, False, 136, 520, 200),
+    (False, False, 4096, 4096, 448), (True, False, 4096, 4096, 512), (True, True, 4096, 4104, 256),
+    (False, False, 8, 8, 1),
+])
+def test_gemm_operand_layouts(ak, bk, M, N, K):
+    """bf16 GEMM with K-major or MN-major operands (MN-major: A(m, k) = A[k, m]), both block-tile
+    configurations (>= 256 tiles -> 256 x 256), ragged M/N, and a K that is not a multiple of the K
+    tile for MN-major operands (their K tail reads a zero row)."""
+    need_gpu()
+    print(f"gemm layouts ak={ak} bk={bk} {M}x{N}x{K}", flush=True)
+    a = synth.normal((M, K), 1.0, 3, 1, "bf16")
+    b = synth.normal((N, K), 0.05, 3, 2, "bf16")
+    ref = a.astype(np.float64) @ b.astype(np.float64).T
+    A = dev(a if ak else np.ascontiguousarray(a.T), "bf16")
+    B = dev(b if bk else np.ascontiguousarray(b.T), "bf16")
+    lda = K if ak else M
+    ldb = K if bk else N
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    ll.llt_gemm(ll._lib.LLT_OP_BF16, ak, bk, A, lda, B, ldb, M, N, K, ll.LL_F32, C, N, None, None, ws, 256)
+    torch.cuda.synchronize()
+    assert_close(host(C), ref, 1e-5, "gemm layouts", elem_rtol=1e-4)
 
 
 def test_gemm_e4m3_subnormal_operands():

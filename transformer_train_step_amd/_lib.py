@@ -69,8 +69,10 @@ _SIGS = {
     "ll_fused_lce_fwd_bwd": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, c_int64, c_int32,
                                        c_int64, c_float, c_int32, c_float, c_int64, c_void_p,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
-    "llt_gemm_nt": (c_int32, [c_int32, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_int32,
-                              c_int32, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_void_p]),
+    "llt_gemm": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_int64, c_int32,
+                           c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
+                           c_size_t, c_void_p]),
+    "llt_set_gemm_config": (c_int32, [c_int32]),
     "llt_trace_begin": (c_int32, [c_int32]),
     "llt_trace_end": (c_int32, []),
     "llt_trace_count": (c_int32, []),
@@ -189,10 +191,22 @@ def ll_fused_lce_fwd_bwd(dtype, hidden, weight, targets, n, d, v, softcap, ignor
                  ptr(d_weight), ptr(ws), ws_bytes, stream_handle(stream), raise_on_error=raise_on_error)
 
 
-def llt_gemm_nt(op_dtype, A, lda, B, ldb, M, N, K, out_dtype, C, ldc, inv_a=None, inv_b=None,
-                stream=None, raise_on_error=True):
-    return _call("llt_gemm_nt", op_dtype, ptr(A), lda, ptr(B), ldb, M, N, K, out_dtype, ptr(C), ldc,
-                 ptr(inv_a), ptr(inv_b), stream_handle(stream), raise_on_error=raise_on_error)
+def llt_gemm(op_dtype, a_kmajor, b_kmajor, A, lda, B, ldb, M, N, K, out_dtype, C, ldc, inv_a=None,
+             inv_b=None, ws=None, ws_bytes=0, stream=None, raise_on_error=True):
+    return _call("llt_gemm", op_dtype, int(a_kmajor), int(b_kmajor), ptr(A), lda, ptr(B), ldb, M, N, K,
+                 out_dtype, ptr(C), ldc, ptr(inv_a), ptr(inv_b), ptr(ws), ws_bytes, stream_handle(stream),
+                 raise_on_error=raise_on_error)
+
+
+def llt_gemm_nt(op_dtype, A, lda, B, ldb, M, N, K, out_dtype, C, ldc, inv_a=None, inv_b=None, stream=None,
+                raise_on_error=True):
+    """llt_gemm with both operands K-major."""
+    return llt_gemm(op_dtype, 1, 1, A, lda, B, ldb, M, N, K, out_dtype, C, ldc, inv_a, inv_b, None, 0, stream,
+                    raise_on_error)
+
+
+def llt_set_gemm_config(cfg: int):
+    return _call("llt_set_gemm_config", cfg)
 
 
 def llt_trace_begin(capacity: int):

@@ -12,6 +12,7 @@ namespace ll {
 
 void set_error(const std::string& msg);
 int fail(int status, const std::string& msg);   // records msg, returns status
+void set_gemm_config_override(int cfg);
 
 // Returns LL_ERR_HIP (with the HIP text recorded) if e is not hipSuccess.
 #define LL_HIP(expr)                                                                           \

@@ -30,6 +30,10 @@ bool g_trace_on = false;
 
 bool trace_on() { return g_trace_on; }
 
+static int g_gemm_cfg = 0;
+int gemm_config_override() { return g_gemm_cfg; }
+void set_gemm_config_override(int c) { g_gemm_cfg = c; }
+
 int trace_open(const char* tag, hipStream_t s, int64_t m, int64_t n, int64_t k) {
   std::lock_guard<std::mutex> lk(g_trace_mu);
   if (!g_trace_on || g_trace_used >= (int)g_trace.size()) return -1;

@@ -111,6 +111,9 @@ __device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
 // ------------------------------------------------------------------ launch tracing (host)
 // When tracing is on (llt_trace_begin), every launch is bracketed by two HIP events recorded on
 // the launch's own stream, tagged with the kernel's name; llt_trace_get reads the durations.
+// Process-wide GEMM block-tile override (0 = automatic), set through llt_set_gemm_config.
+int gemm_config_override();
+
 // GEMM launches also record their (M, N, K).
 bool trace_on();
 int trace_open(const char* tag, hipStream_t s, int64_t m = 0, int64_t n = 0, int64_t k = 0);

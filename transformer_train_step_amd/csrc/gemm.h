@@ -68,19 +68,93 @@ struct GemmSmem {
   static constexpr int kBytes = kOperand > kSlab ? kOperand : kSlab;
 };
 
-template <class ET, int BM, int BN, class Epi>
-__global__ void __launch_bounds__(kGemmThreads)
-gemm_nt_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int64_t ldb,
-               int M, int N, int K, Epi epi) {
-  constexpr int WN = 2;                        // 4 waves: 2 x 2
-  constexpr int TM = BM / 2, TN = BN / WN;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+// 16-byte chunk swizzles. K-major tiles (rows of 128 B): chunk ^ ((row >> 1) & 7) puts the 16
+// rows of a fragment read on 16 distinct (bank half, chunk) slots. MN-major tiles (k rows of
+// ROWS elements): chunk ^ mn_swz(k) spreads the 4 k-rows of one transpose read over distinct
+// chunk pairs, and alternating 16-row k groups over the two halves of the bank window.
+__device__ __forceinline__ int kmaj_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int mn_swz(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 4) & 1)); }
+
+// Issue the direct global->LDS loads of one operand tile for K tile kt (this wave's share).
+//   K-major: element (r, k) at g[r * ld + k]; tile = ROWS rows x 128 B.
+//   MN-major: element (r, k) at g[k * ld + r]; tile = KE k-rows x ROWS elements; k-rows at or
+//   beyond kvalid read the zero row instead (the K tail of a token-contracted GEMM).
+// Rows/columns past rmax are clamped to valid memory; they only feed outputs that are not stored.
+template <class ET, bool KMAJ, int ROWS, int NW>
+__device__ __forceinline__ void issue_tile(const char* g, int64_t ldb, int r0, int rmax, int kt, int kvalid,
+                                           const char* zrow, unsigned char* lds_op, int wave, int lane) {
+  constexpr int TILE = ROWS * 128;
+  constexpr int NI = TILE / 1024 / NW;
+  static_assert(NI >= 1 && NI * 1024 * NW == TILE, "tile must split evenly over the waves");
+  constexpr int KE = 128 / (int)sizeof(ET);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int base = (wave * NI + i) * 1024;
+    const char* src;
+    if constexpr (KMAJ) {
+      const int row = base / 128 + (lane >> 3);
+      const int logical = (lane & 7) ^ kmaj_swz(row);
+      const int gr = min(r0 + row, rmax - 1);
+      src = g + gr * ldb + (int64_t)kt * 128 + logical * 16;
+    } else {
+      constexpr int CPR = ROWS * (int)sizeof(ET) / 16;
+      const int sidx = base / 16 + lane;
+      const int krow = sidx / CPR;
+      const int logical = (sidx % CPR) ^ mn_swz(krow);
+      const int k = kt * KE + krow;
+      const int col = min(r0 + logical * (16 / (int)sizeof(ET)), rmax - 16 / (int)sizeof(ET));
+      src = k < kvalid ? g + (int64_t)k * ldb + (int64_t)col * (int)sizeof(ET) : zrow;
+    }
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(lds_op + base), 16, 0, 0);
+  }
+}
+
+// Fragment of 16 rows (K-major) or 16 columns (MN-major) starting at f0: 32 bytes per lane,
+// lane (index l & 15, group g = l >> 4) holds K elements [16g, 16g + 16) of the 64 bf16 (or the
+// type's equivalent 32 bytes) of this K tile, in the same order for both layouts.
+template <bool KMAJ, int ROWS>
+__device__ __forceinline__ void read_frag(const unsigned char* t, int f0, int lane, uint32_t (&f)[8]) {
+  const int g = lane >> 4;
+  if constexpr (KMAJ) {
+    const int row = f0 + (lane & 15), sw = kmaj_swz(row);
+    const uint4 lo = *reinterpret_cast<const uint4*>(t + row * 128 + ((2 * g) ^ sw) * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(t + row * 128 + ((2 * g + 1) ^ sw) * 16);
+    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w; f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+  } else {
+    // bf16 only: four ds_read_b64_tr_b16, each giving this lane's column at 4 consecutive k
+    constexpr int RB = ROWS * 2;
+    const int li = lane & 15, r = li >> 2, j = li & 3;
+    const int col = f0 + 4 * j;
+    const int chunk = col >> 3, within = (col & 7) * 2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {                  // q = 2 * substep + half
+      const int k = 16 * g + 4 * q + r;
+      const unsigned char* a = t + k * RB + ((chunk ^ mn_swz(k)) * 16) + within;
+      const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(a));
+      const uint2 u = __builtin_bit_cast(uint2, v);
+      f[2 * q] = u.x;
+      f[2 * q + 1] = u.y;
+    }
+  }
+}
+
+// C[m, n] = sum_k A(m, k) B(n, k), A(m, k) = AK ? A[m * lda + k] : A[k * lda + m] (likewise B).
+// WGM x WGN waves; wave tile (BM/WGM) x (BN/WGN) in 16 x 16 MFMA fragments.
+template <class ET, int BM, int BN, int WGM, int WGN, bool AK, bool BK, class Epi>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int64_t ldb, int M, int N, int K,
+            const ET* __restrict__ zrow, Epi epi) {
+  static_assert((AK && BK) || sizeof(ET) == 2, "MN-major operands are bf16 only");
+  constexpr int NW = WGM * WGN, NT = 64 * NW;
+  constexpr int WN = WGN;
+  constexpr int TM = BM / WGM, TN = BN / WGN;
   constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int KE = 128 / (int)sizeof(ET);    // K elements per tile
-  constexpr int CA = BM * 8 / kGemmThreads, CB = BN * 8 / kGemmThreads;
-  static_assert(CA >= 1 && CB >= 1, "tile too small");
+  constexpr int KE = 128 / (int)sizeof(ET);
+  constexpr int STAGE = (BM + BN) * 128;
   __shared__ __attribute__((aligned(16))) unsigned char smem[GemmSmem<BM, BN>::kBytes];
-  uint4* sA = reinterpret_cast<uint4*>(smem);              // [2][BM][8]
-  uint4* sB = sA + 2 * BM * 8;                              // [2][BN][8]
 
   const int nbm = (int)cdiv(M, BM), nbn = (int)cdiv(N, BN);
   const int nb = nbm * nbn;
@@ -93,38 +167,15 @@ gemm_nt_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-
   const char* Ab = reinterpret_cast<const char*>(A);
   const char* Bb = reinterpret_cast<const char*>(B);
+  const char* zb = reinterpret_cast<const char*>(zrow);
   const int64_t ldab = lda * (int64_t)sizeof(ET), ldbb = ldb * (int64_t)sizeof(ET);
-  uint4 ra[CA], rb[CB];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + i * kGemmThreads, row = c >> 3, col = c & 7;
-      const int gm = m0 + row;
-      ra[i] = gm < M ? *reinterpret_cast<const uint4*>(Ab + gm * ldab + (int64_t)kt * 128 + col * 16)
-                     : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int c = tid + i * kGemmThreads, row = c >> 3, col = c & 7;
-      const int gn = n0 + row;
-      rb[i] = gn < N ? *reinterpret_cast<const uint4*>(Bb + gn * ldbb + (int64_t)kt * 128 + col * 16)
-                     : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + i * kGemmThreads, row = c >> 3, col = c & 7;
-      sA[(st * BM + row) * 8 + (col ^ (row & 7))] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int c = tid + i * kGemmThreads, row = c >> 3, col = c & 7;
-      sB[(st * BN + row) * 8 + (col ^ (row & 7))] = rb[i];
-    }
+
+  auto issue = [&](int kt, int st) {
+    unsigned char* sa = smem + st * STAGE;
+    issue_tile<ET, AK, BM, NW>(Ab, ldab, m0, M, kt, K, zb, sa, wave, lane);
+    issue_tile<ET, BK, BN, NW>(Bb, ldbb, n0, N, kt, K, zb, sa + BM * 128, wave, lane);
   };
 
   floatx4 acc[FN][FM];
@@ -133,43 +184,35 @@ gemm_nt_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, 
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / KE;
-  const int g = lane >> 4, r16 = lane & 15;
-  if (nk > 0) {
-    gload(0);
-    sstore(0);
-  }
+  const int nk = (int)cdiv(K, KE);
+  if (nk > 0) issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    if (kt + 1 < nk) issue(kt + 1, st ^ 1);
+    const unsigned char* sa = smem + st * STAGE;
+    const unsigned char* sb = sa + BM * 128;
     uint32_t bf[FN][8];
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int row = wn * TN + i * 16 + r16;
-      const uint4 lo = sB[(st * BN + row) * 8 + ((2 * g) ^ (row & 7))];
-      const uint4 hi = sB[(st * BN + row) * 8 + ((2 * g + 1) ^ (row & 7))];
-      bf[i][0] = lo.x; bf[i][1] = lo.y; bf[i][2] = lo.z; bf[i][3] = lo.w;
-      bf[i][4] = hi.x; bf[i][5] = hi.y; bf[i][6] = hi.z; bf[i][7] = hi.w;
-    }
+    for (int i = 0; i < FN; ++i) read_frag<BK, BN>(sb, wn * TN + i * 16, lane, bf[i]);
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int row = wm * TM + j * 16 + r16;
-      const uint4 lo = sA[(st * BM + row) * 8 + ((2 * g) ^ (row & 7))];
-      const uint4 hi = sA[(st * BM + row) * 8 + ((2 * g + 1) ^ (row & 7))];
-      const uint32_t af[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      uint32_t af[8];
+      read_frag<AK, BM>(sa, wm * TM + j * 16, lane, af);
 #pragma unroll
       for (int i = 0; i < FN; ++i) Mma<ET>::run(acc[i][j], bf[i], af);
     }
-    if (kt + 1 < nk) sstore(st ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
+  const int g = lane >> 4, r16 = lane & 15;
   // ---------------- epilogue: accumulator -> LDS slab (64 rows) -> functor on row segments
   float* slab = reinterpret_cast<float*>(smem);
   constexpr int LDS_LD = BN + 4;
   constexpr int SEGS = BN / 8;                              // 8-column segments per row
-  constexpr int ROWS_PER_PASS = kGemmThreads / SEGS;
+  constexpr int ROWS_PER_PASS = NT / SEGS;
   float red_amax = 0.f;
 #pragma unroll 1
   for (int s0 = 0; s0 < BM; s0 += kSlabRows) {
@@ -349,16 +392,78 @@ inline const char* gemm_tag() {
   return t.c_str();
 }
 
-template <class ET, class Epi>
-inline hipError_t launch_gemm_nt(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N,
-                                 int K, const Epi& epi, hipStream_t s) {
-  constexpr int BM = 128, BN = 128;
-  if (M <= 0 || N <= 0) return hipSuccess;
+// Operand layouts of a GEMM call: K-major ("row m holds its K elements contiguously") or MN-major.
+struct GemmOps {
+  bool a_kmajor = true, b_kmajor = true;
+  const void* zrow = nullptr;       // >= 16 zero bytes: K-tail rows of MN-major operands
+};
+
+template <class ET, int BM, int BN, int WGM, int WGN, class Epi>
+inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
+                                  const Epi& epi, const GemmOps& o, hipStream_t s) {
   const int64_t nb = cdiv(M, BM) * cdiv(N, BN);
   const char* tag = gemm_tag<ET, Epi>();
-  LL_LAUNCH_MNK(tag, M, N, K, (gemm_nt_kernel<ET, BM, BN, Epi>), dim3((unsigned)nb), dim3(kGemmThreads), 0, s,
-                     A, lda, B, ldb, M, N, K, epi);
+  const ET* z = static_cast<const ET*>(o.zrow);
+  constexpr int NT = 64 * WGM * WGN;
+  if constexpr (sizeof(ET) == 2) {
+    if (!o.a_kmajor && !o.b_kmajor) {
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, false, false, Epi>), dim3((unsigned)nb), dim3(NT),
+                    0, s, A, lda, B, ldb, M, N, K, z, epi);
+      return hipGetLastError();
+    }
+    if (!o.a_kmajor) {
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, false, true, Epi>), dim3((unsigned)nb), dim3(NT),
+                    0, s, A, lda, B, ldb, M, N, K, z, epi);
+      return hipGetLastError();
+    }
+    if (!o.b_kmajor) {
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, true, false, Epi>), dim3((unsigned)nb), dim3(NT),
+                    0, s, A, lda, B, ldb, M, N, K, z, epi);
+      return hipGetLastError();
+    }
+  }
+  LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, true, true, Epi>), dim3((unsigned)nb), dim3(NT), 0, s,
+                A, lda, B, ldb, M, N, K, z, epi);
   return hipGetLastError();
+}
+
+// Block-tile configurations: 1 = 128 x 128 (4 waves), 2 = 256 x 256 (4 waves), 3 = 256 x 256
+// (8 waves, 2 x 4), 4 = 256 x 256 (8 waves, 4 x 2); 0 = automatic (gemm_config_override()).
+
+template <class ET, class Epi>
+inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
+                                   const Epi& epi, const GemmOps& o, hipStream_t s) {
+  switch (cfg) {
+    case 1: return launch_gemm_cfg<ET, 128, 128, 2, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+    case 2: return launch_gemm_cfg<ET, 256, 256, 2, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+    case 3: return launch_gemm_cfg<ET, 256, 256, 2, 4>(A, lda, B, ldb, M, N, K, epi, o, s);
+    default: return launch_gemm_cfg<ET, 256, 256, 4, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+  }
+}
+
+// Picks the block tile from the wave quantisation on 256 CUs: 256 x 256 with 8 waves (measured
+// ~15% faster per FLOP than 128 x 128 on the layer's shapes) unless its last wave of blocks leaves
+// so many CUs idle that 128 x 128 finishes first. Requirements (checked by the callers): K a multiple of the K tile for K-major
+// operands (64 bf16, 128 e4m3, 32 fp32) or rows zero-padded to it; MN-major operands bf16 with M
+// (or N) a multiple of 8 and >= 8, and a zero row for the K tail; N a multiple of 8.
+template <class ET, class Epi>
+inline hipError_t launch_gemm(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
+                              const Epi& epi, const GemmOps& o, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  int cfg = gemm_config_override();
+  if (cfg == 0) {
+    const int64_t t256 = cdiv(M, 256) * cdiv(N, 256), t128 = cdiv(M, 128) * cdiv(N, 128);
+    const double e256 = (double)t256 / (double)(cdiv(t256, 256) * 256);
+    const double e128 = 0.85 * (double)t128 / (double)(cdiv(t128, 256) * 256);
+    cfg = e256 >= e128 ? 3 : 1;
+  }
+  return launch_gemm_with(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
+}
+
+template <class ET, class Epi>
+inline hipError_t launch_gemm_nt(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
+                                 const Epi& epi, hipStream_t s) {
+  return launch_gemm(A, lda, B, ldb, M, N, K, epi, GemmOps{}, s);
 }
 
 }  // namespace

@@ -115,8 +115,9 @@ size_t carve_fwd(void* base, const Dims& d, FwdWs& w) {
 struct BwdWs {
   float2* cs;
   QScale* qs;            // [2]: dm, du
-  void *dm, *du, *dhn, *dh, *dattn, *dout, *dattnT, *oT, *woT, *qt, *kt, *dot, *dqkv, *dqkvT, *xnT, *wqkvT, *dxn;
-  void *w2T, *w1T, *dmT, *rT, *duT, *hnT;
+  void *dm, *du, *dhn, *dh, *dattn, *dout, *qt, *kt, *dot, *dqkv, *dxn;
+  void *t0, *t1;         // fp32 only: transposed operand copies for mm_nn / mm_tn
+  const void* zrow;      // 256 zero bytes: K-tail rows of MN-major GEMM operands
   uint8_t *dm8, *dm8t, *du8, *du8t;
   float *delta, *dqh, *dkh, *dgp;
 };
@@ -125,15 +126,13 @@ size_t carve_bwd(void* base, const Dims& d, BwdWs& w) {
   const size_t e = d.es;
   w.cs = c.take<float2>(d.T * (d.DH / 2) + 1);
   w.qs = c.take<QScale>(2);
+  w.zrow = c.take<char>(256);
   w.dm = c.take<char>(d.N * d.D * e);
   w.du = c.take<char>(d.N * d.F * e);
   w.dhn = c.take<char>(d.N * d.D * e);
   w.dh = c.take<char>(d.N * d.D * e);
   w.dattn = c.take<char>(d.N * d.D * e);
   w.dout = c.take<char>(d.N * d.QD * e);
-  w.dattnT = c.take<char>((int64_t)d.D * d.Np * e);
-  w.oT = c.take<char>((int64_t)d.QD * d.Np * e);
-  w.woT = c.take<char>((int64_t)d.QD * d.D * e);
   w.qt = c.take<char>(d.B * d.QD * d.Tp * e);
   w.kt = c.take<char>(d.B * d.KVD * d.Tp * e);
   w.dot = c.take<char>(d.B * d.QD * d.Tp * e);
@@ -141,25 +140,21 @@ size_t carve_bwd(void* base, const Dims& d, BwdWs& w) {
   w.dqh = c.take<float>(d.N * d.QD);
   w.dkh = c.take<float>(d.N * d.KVD);
   w.dqkv = c.take<char>(d.N * d.QKVD * e);
-  w.dqkvT = c.take<char>((int64_t)d.QKVD * d.Np * e);
-  w.xnT = c.take<char>((int64_t)d.D * d.Np * e);
-  w.wqkvT = c.take<char>((int64_t)d.D * d.QKVD * e);
   w.dxn = c.take<char>(d.N * d.D * e);
   w.dgp = c.take<float>(rmsnorm_bwd_partials(d.N) * d.D + 1);
-  w.w2T = w.w1T = w.dmT = w.rT = w.duT = w.hnT = nullptr;
+  w.t0 = w.t1 = nullptr;
   w.dm8 = w.dm8t = w.du8 = w.du8t = nullptr;
+  if (!d.bf) {
+    const int64_t big = std::max<int64_t>({(int64_t)d.QKVD, (int64_t)d.F, (int64_t)d.D, (int64_t)d.QD});
+    const int64_t t = std::max<int64_t>(big * d.Np, big * big);
+    w.t0 = c.take<char>(t * e);
+    w.t1 = c.take<char>(t * e);
+  }
   if (d.fp8) {
     w.dm8 = c.take<uint8_t>(d.N * d.D);
     w.dm8t = c.take<uint8_t>((int64_t)d.D * d.Np);
     w.du8 = c.take<uint8_t>(d.N * d.F);
     w.du8t = c.take<uint8_t>((int64_t)d.F * d.Np);
-  } else {
-    w.w2T = c.take<char>((int64_t)d.F * d.D * e);
-    w.w1T = c.take<char>((int64_t)d.D * d.F * e);
-    w.dmT = c.take<char>((int64_t)d.D * d.Np * e);
-    w.rT = c.take<char>((int64_t)d.F * d.Np * e);
-    w.duT = c.take<char>((int64_t)d.F * d.Np * e);
-    w.hnT = c.take<char>((int64_t)d.D * d.Np * e);
   }
   return c.bytes();
 }
@@ -181,6 +176,35 @@ hipError_t rope_table(float2* cs, const Dims& d, hipStream_t s) {
   LL_LAUNCH("rope_table", rope_table_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 4096)), dim3(256), 0, s, cs,
                      (int)d.T, d.DH / 2, (double)d.theta);
   return hipGetLastError();
+}
+
+// Backward GEMMs whose operands are not both K-major.
+//   mm_nn: C = A W with A [M, K] K-major and W [K, N] row-major (the input-gradient GEMMs).
+//   mm_tn: C = X^T Y with X [K, M], Y [K, N] row-major, K = tokens (the weight-gradient GEMMs).
+// bf16 reads the row-major operands in place (MN-major, LDS transpose reads); fp32 goes through
+// transposed copies (token axis padded with zeros to Kp).
+template <class T, class Epi>
+hipError_t mm_nn(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const Epi& e, T* wT,
+                 const void* zrow, hipStream_t s) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    return launch_gemm(A, lda, W, ldw, M, N, K, e, GemmOps{true, false, zrow}, s);
+  } else {
+    hipError_t r = transpose2d(W, (int64_t)K, N, ldw, wT, (int64_t)K, (int64_t)K, s);
+    if (r != hipSuccess) return r;
+    return launch_gemm_nt(A, lda, static_cast<const T*>(wT), (int64_t)K, M, N, K, e, s);
+  }
+}
+template <class T, class Epi>
+hipError_t mm_tn(const T* X, int64_t ldx, const T* Y, int64_t ldy, int M, int N, int64_t K, int64_t Kp, const Epi& e,
+                 T* xT, T* yT, const void* zrow, hipStream_t s) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    return launch_gemm(X, ldx, Y, ldy, M, N, (int)K, e, GemmOps{false, false, zrow}, s);
+  } else {
+    hipError_t r = transpose2d(X, K, M, ldx, xT, Kp, Kp, s);
+    if (r == hipSuccess) r = transpose2d(Y, K, N, ldy, yT, Kp, Kp, s);
+    if (r != hipSuccess) return r;
+    return launch_gemm_nt(static_cast<const T*>(xT), Kp, static_cast<const T*>(yT), Kp, M, N, (int)Kp, e, s);
+  }
 }
 
 // ------------------------------------------------------------------------------------------ fwd
@@ -263,6 +287,7 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   const float* g2 = CP<float>(p->mlp_norm_w);
   LL_HIP(rope_table(w.cs, d, s));
   LL_HIP(fill_f32(reinterpret_cast<float*>(w.qs), 0.f, 2 * 4, s));
+  LL_HIP(fill_f32(reinterpret_cast<float*>(const_cast<void*>(w.zrow)), 0.f, 64, s));
   LL_HIP(fill_f32(g->resid_mlp, 0.f, 1, s));
   LL_HIP(fill_f32(g->resid_attn, 0.f, 1, s));
   // MLP residual branch: dm = a_mlp dy, da_mlp = sum dy m
@@ -298,44 +323,35 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
     }
   }
   if (!done) {
-    LL_HIP(transpose2d(CP<T>(p->w_proj), d.D, d.F, (int64_t)d.F, P<T>(w.w2T), (int64_t)d.D, (int64_t)d.D, s));
-    LL_HIP(transpose2d(CP<T>(p->w_fc), d.F, d.D, (int64_t)d.D, P<T>(w.w1T), (int64_t)d.F, (int64_t)d.F, s));
-    {
+    {   // dr = dm W2; du = dr * 2 relu(u)
       EpiRelu2Bwd<T> e{P<T>(w.du), CP<T>(sv.u), (int64_t)d.F, Deq{nullptr, nullptr}, &w.qs[1].amax};
-      LL_HIP(launch_gemm_nt(CP<T>(w.dm), d.D, CP<T>(w.w2T), d.D, (int)N, d.F, d.D, e, s));
+      LL_HIP(mm_nn(CP<T>(w.dm), d.D, CP<T>(p->w_proj), d.F, (int)N, d.F, d.D, e, P<T>(w.t0), w.zrow, s));
     }
-    LL_HIP(transpose2d(CP<T>(w.dm), N, d.D, (int64_t)d.D, P<T>(w.dmT), Np, Np, s));
-    LL_HIP(transpose2d(CP<T>(sv.r), N, d.F, (int64_t)d.F, P<T>(w.rT), Np, Np, s));
-    {
+    {   // dW2 = dm^T r
       EpiStore<T> e{P<T>(g->w_proj), (int64_t)d.F, Deq{nullptr, nullptr}};
-      LL_HIP(launch_gemm_nt(CP<T>(w.dmT), Np, CP<T>(w.rT), Np, d.D, d.F, (int)Np, e, s));
+      LL_HIP(mm_tn(CP<T>(w.dm), d.D, CP<T>(sv.r), d.F, d.D, d.F, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s));
     }
-    LL_HIP(transpose2d(CP<T>(w.du), N, d.F, (int64_t)d.F, P<T>(w.duT), Np, Np, s));
-    LL_HIP(transpose2d(CP<T>(sv.hn), N, d.D, (int64_t)d.D, P<T>(w.hnT), Np, Np, s));
-    {
+    {   // dW1 = du^T hn
       EpiStore<T> e{P<T>(g->w_fc), (int64_t)d.D, Deq{nullptr, nullptr}};
-      LL_HIP(launch_gemm_nt(CP<T>(w.duT), Np, CP<T>(w.hnT), Np, d.F, d.D, (int)Np, e, s));
+      LL_HIP(mm_tn(CP<T>(w.du), d.F, CP<T>(sv.hn), d.D, d.F, d.D, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s));
     }
-    {
+    {   // dhn = du W1
       EpiStore<T> e{P<T>(w.dhn), (int64_t)d.D, Deq{nullptr, nullptr}};
-      LL_HIP(launch_gemm_nt(CP<T>(w.du), d.F, CP<T>(w.w1T), d.F, (int)N, d.D, d.F, e, s));
+      LL_HIP(mm_nn(CP<T>(w.du), d.F, CP<T>(p->w_fc), d.D, (int)N, d.D, d.F, e, P<T>(w.t0), w.zrow, s));
     }
   }
   // MLP RMSNorm backward + residual, fused with the attention-branch scaling
   LL_HIP(launch_rmsnorm_bwd(CP<T>(w.dhn), CP<T>(sv.h), g2, sv.r2, dy, P<T>(w.dh), w.dgp, N, d.D, p->resid_attn,
                             P<T>(w.dattn), CP<T>(sv.attn_out), g->resid_attn, s));
   LL_HIP(launch_colsum(w.dgp, rmsnorm_bwd_partials(N), d.D, P<float>(g->mlp_norm_w), s));
-  // O projection
-  LL_HIP(transpose2d(CP<T>(p->w_o), d.D, d.QD, (int64_t)d.QD, P<T>(w.woT), (int64_t)d.D, (int64_t)d.D, s));
+  // O projection: do = dattn W_o, dW_o = dattn^T o
   {
     EpiStore<T> e{P<T>(w.dout), (int64_t)d.QD, Deq{nullptr, nullptr}};
-    LL_HIP(launch_gemm_nt(CP<T>(w.dattn), d.D, CP<T>(w.woT), d.D, (int)N, d.QD, d.D, e, s));
+    LL_HIP(mm_nn(CP<T>(w.dattn), d.D, CP<T>(p->w_o), d.QD, (int)N, d.QD, d.D, e, P<T>(w.t0), w.zrow, s));
   }
-  LL_HIP(transpose2d(CP<T>(w.dattn), N, d.D, (int64_t)d.D, P<T>(w.dattnT), Np, Np, s));
-  LL_HIP(transpose2d(CP<T>(sv.o), N, d.QD, (int64_t)d.QD, P<T>(w.oT), Np, Np, s));
   {
     EpiStore<T> e{P<T>(g->w_o), (int64_t)d.QD, Deq{nullptr, nullptr}};
-    LL_HIP(launch_gemm_nt(CP<T>(w.dattnT), Np, CP<T>(w.oT), Np, d.D, d.QD, (int)Np, e, s));
+    LL_HIP(mm_tn(CP<T>(w.dattn), d.D, CP<T>(sv.o), d.QD, d.D, d.QD, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s));
   }
   // attention core
   T* dqkv = P<T>(w.dqkv);
@@ -371,17 +387,14 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
       LL_HIP(hipGetLastError());
     }
   }
-  // QKV projection
-  LL_HIP(transpose2d(CP<T>(p->w_qkv), d.QKVD, d.D, (int64_t)d.D, P<T>(w.wqkvT), (int64_t)d.QKVD, (int64_t)d.QKVD, s));
+  // QKV projection: dxn = dqkv W_qkv, dW_qkv = dqkv^T xn
   {
     EpiStore<T> e{P<T>(w.dxn), (int64_t)d.D, Deq{nullptr, nullptr}};
-    LL_HIP(launch_gemm_nt(CP<T>(dqkv), d.QKVD, CP<T>(w.wqkvT), d.QKVD, (int)N, d.D, d.QKVD, e, s));
+    LL_HIP(mm_nn(CP<T>(dqkv), d.QKVD, CP<T>(p->w_qkv), d.D, (int)N, d.D, d.QKVD, e, P<T>(w.t0), w.zrow, s));
   }
-  LL_HIP(transpose2d(CP<T>(dqkv), N, d.QKVD, (int64_t)d.QKVD, P<T>(w.dqkvT), Np, Np, s));
-  LL_HIP(transpose2d(CP<T>(sv.xn), N, d.D, (int64_t)d.D, P<T>(w.xnT), Np, Np, s));
   {
     EpiStore<T> e{P<T>(g->w_qkv), (int64_t)d.D, Deq{nullptr, nullptr}};
-    LL_HIP(launch_gemm_nt(CP<T>(w.dqkvT), Np, CP<T>(w.xnT), Np, d.QKVD, d.D, (int)Np, e, s));
+    LL_HIP(mm_tn(CP<T>(dqkv), d.QKVD, CP<T>(sv.xn), d.D, d.QKVD, d.D, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s));
   }
   // input RMSNorm backward + residual
   LL_HIP(launch_rmsnorm_bwd(CP<T>(w.dxn), x, g1, sv.r1, CP<T>(w.dh), dx, w.dgp, N, d.D, (const float*)nullptr,

@@ -5,15 +5,24 @@
 //   1. z = H_c W^T on MFMA; the epilogue rounds z to the storage type, stores it, and reduces
 //      c = s tanh(z/s) over each 128-column vocabulary tile to an online (max, sum exp) pair;
 //   2. one wave per row combines the pairs into lse and adds lse - c[target] to the loss;
-//   3. dz = grad_scale/n_valid (exp(c - lse) - onehot)(1 - (c/s)^2), rounded, stored as dz and
-//      dz^T (64 x 64 LDS tile transpose) in one pass;
-//   4. dH_c = dz W (GEMM against W^T) and dW += dz^T H_c (fp32 accumulation across chunks).
+//   3. dz = grad_scale/n_valid (exp(c - lse) - onehot)(1 - (c/s)^2), rounded, stored in place of z;
+//   4. dH_c = dz W and dW += dz^T H_c (fp32 accumulation across chunks); in bf16 both GEMMs read
+//      W, dz and H_c where they are (MN-major operands through LDS transpose reads).
 #pragma once
 #include "common.h"
 #include "gemm.h"
 
 namespace ll {
 namespace {
+
+// c = s * tanh(z / s), with tanh(x) = sign(x) (1 - 2 / (exp(2|x|) + 1)): one exponential and one
+// division; the absolute error stays at a few fp32 ulps of s. Every kernel of the loss uses this
+// function, so the logits epilogue, the loss and the gradient see identical c.
+__device__ __forceinline__ float softcap_tanh(float z, float s, float inv_s) {
+  const float x = fabsf(z * inv_s);
+  const float t = 1.f - __fdividef(2.f, __expf(2.f * x) + 1.f);
+  return copysignf(s * t, z);
+}
 
 template <class T> struct EpiLceLogits {
   static constexpr const char* kName = "lce_logits";
@@ -27,7 +36,7 @@ template <class T> struct EpiLceLogits {
     mx = -INFINITY;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      c[k] = softcap * tanhf(v[k] * inv_softcap);
+      c[k] = softcap_tanh(v[k], softcap, inv_softcap);
       mx = fmaxf(mx, c[k]);
     }
     se = 0.f;
@@ -71,13 +80,13 @@ lce_lse_kernel(const float2* __restrict__ part, int nparts, const T* __restrict_
     const int32_t t = y[row];
     if (t != ignore) {
       const float zt = Elem<T>::ld(z, (int64_t)row * ldz + t);
-      atomicAdd(loss_acc, l - softcap * tanhf(zt / softcap));
+      atomicAdd(loss_acc, l - softcap_tanh(zt, softcap, 1.f / softcap));
     }
   }
 }
 
 // dz / dz^T over a 64 (rows) x 64 (vocab) tile; rows >= rows_valid or cols >= V give 0.
-//   dz [rows_pad, ldz] (written for cols < Vpad), dzt [Vpad, ldzt] (written for rows < rows_pad)
+//   dz [rows_pad, ldz] (written for cols < Vpad), dzt [Vpad, ldzt] (written for rows < rows_pad, if not null)
 template <class T>
 __global__ void __launch_bounds__(256)
 lce_dz_kernel(const T* __restrict__ z, int64_t ldz, const float* __restrict__ lse, const int32_t* __restrict__ y,
@@ -95,7 +104,7 @@ lce_dz_kernel(const T* __restrict__ z, int64_t ldz, const float* __restrict__ ls
     if (r < rows_valid && c < V) {
       const int32_t t = y[r];
       if (t != ignore) {
-        const float cv = softcap * tanhf(Elem<T>::ld(z, (int64_t)r * ldz + c) * inv_s);
+        const float cv = softcap_tanh(Elem<T>::ld(z, (int64_t)r * ldz + c), softcap, inv_s);
         const float p = __expf(cv - lse[r]) - (c == t ? 1.f : 0.f);
         const float w = cv * inv_s;
         d = Elem<T>::rnd(gs * p * (1.f - w * w));
@@ -105,9 +114,47 @@ lce_dz_kernel(const T* __restrict__ z, int64_t ldz, const float* __restrict__ ls
     tile[i][tx] = d;
   }
   __syncthreads();
+  if (!dzt) return;
   for (int i = ty; i < 64; i += 4) {
     const int c = c0 + i, r = r0 + tx;
     if (c < Vpad && r < rows_pad) Elem<T>::st(dzt, (int64_t)c * ldzt + r, tile[tx][i]);
+  }
+}
+
+// In-place dz over rows [0, rows) x cols [0, Vpad) of z (ld = Vpad, a multiple of 8): each
+// thread turns 8 consecutive logits into 8 gradient values (16-byte loads and stores); columns at
+// or beyond V become 0.
+template <class T>
+__global__ void __launch_bounds__(256)
+lce_dz_inplace_kernel(T* __restrict__ z, int64_t ldz, const float* __restrict__ lse, const int32_t* __restrict__ y,
+                      int rows, int V, int32_t ignore, float softcap, float grad_scale, const int* __restrict__ nv) {
+  const int n_valid = *nv;
+  const float gs = n_valid > 0 ? grad_scale / (float)n_valid : 0.f;
+  const float inv_s = 1.f / softcap;
+  const int segs = (int)(ldz / 8);
+  const int64_t total = (int64_t)rows * segs;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(i / segs);
+    const int c0 = (int)(i - (int64_t)r * segs) * 8;
+    T* p = z + (int64_t)r * ldz + c0;
+    const int32_t t = y[r];
+    float v[8];
+    if (t == ignore) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = 0.f;
+    } else {
+      Vec8<T>::load(p, v);
+      const float l = lse[r];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int c = c0 + k;
+        const float cv = softcap_tanh(v[k], softcap, inv_s);
+        const float w = cv * inv_s;
+        const float pr = __expf(cv - l) - (c == t ? 1.f : 0.f);
+        v[k] = c < V ? Elem<T>::rnd(gs * pr * (1.f - w * w)) : 0.f;
+      }
+    }
+    Vec8<T>::store(p, v);
   }
 }
 

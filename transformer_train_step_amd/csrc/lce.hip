@@ -9,17 +9,18 @@ using namespace ll;
 
 namespace {
 
-constexpr int kLceBN = 128;              // vocabulary tile of the logits GEMM (one LSE partial each)
-constexpr int64_t kDefaultChunk = 8192;
+constexpr int kLceBN = 256;   // logits GEMM N tile (never the 128-wide config): one LSE partial per 256 columns
+constexpr int64_t kDefaultChunk = 10240;
 
 struct LcePlan {
   int64_t chunk, chunk_pad, vpad;
   int nparts;
   float2* part = nullptr;
-  void* wt = nullptr;       // [D, Vpad]
   void* z = nullptr;        // [chunk_pad, Vpad]  (z, then dz in place)
-  void* dzt = nullptr;      // [Vpad, chunk_pad]
-  void* ht = nullptr;       // [D, chunk_pad]
+  void* wt = nullptr;       // fp32 only: W^T [D, Vpad]
+  void* dzt = nullptr;      // fp32 only: dz^T [Vpad, chunk_pad]
+  void* ht = nullptr;       // fp32 only: H_c^T [D, chunk_pad]
+  void* zrow = nullptr;     // 256 zero bytes (K tails of MN-major operands)
   float* dw32 = nullptr;    // [V, D]
   float* lse = nullptr;     // [chunk]
   float* loss_acc = nullptr;
@@ -37,13 +38,16 @@ LcePlan plan_lce(void* ws, int es, int64_t n, int d, int64_t v, int64_t token_ch
   Carver c(ws);
   p.loss_acc = c.take<float>(4);
   p.nv = c.take<int>(4);
+  p.zrow = c.take<char>(256);
   p.lse = c.take<float>(p.chunk_pad);
   p.part = c.take<float2>(p.chunk_pad * p.nparts);
   p.z = c.take<char>((size_t)p.chunk_pad * p.vpad * es);
   if (grads) {
-    p.wt = c.take<char>((size_t)d * p.vpad * es);
-    p.dzt = c.take<char>((size_t)p.vpad * p.chunk_pad * es);
-    p.ht = c.take<char>((size_t)d * p.chunk_pad * es);
+    if (es == 4) {
+      p.wt = c.take<char>((size_t)d * p.vpad * es);
+      p.dzt = c.take<char>((size_t)p.vpad * p.chunk_pad * es);
+      p.ht = c.take<char>((size_t)d * p.chunk_pad * es);
+    }
     p.dw32 = c.take<float>((size_t)v * d);
   }
   p.bytes = c.bytes();
@@ -55,37 +59,55 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
             int32_t ignore, float grad_scale, const LcePlan& p, float* loss, float* lse_out, T* dH, T* dW,
             hipStream_t s) {
   const bool grads = dH != nullptr;
+  constexpr bool kMN = std::is_same<T, bf16>::value;   // bf16 reads W, dz and H in place (MN-major)
   LL_HIP(fill_f32(p.loss_acc, 0.f, 4, s));
   LL_HIP(fill_f32(reinterpret_cast<float*>(p.nv), 0.f, 4, s));
+  LL_HIP(fill_f32(static_cast<float*>(p.zrow), 0.f, 64, s));
   if (n > 0) {
     LL_LAUNCH("count_valid", count_valid_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 1024)), dim3(256), 0, s,
-                       y, n, ignore, p.nv);
+              y, n, ignore, p.nv);
     LL_HIP(hipGetLastError());
   }
-  if (grads) LL_HIP(transpose2d(W, v, d, (int64_t)d, static_cast<T*>(p.wt), p.vpad, p.vpad, s));
+  if (grads && !kMN) LL_HIP(transpose2d(W, v, d, (int64_t)d, static_cast<T*>(p.wt), p.vpad, p.vpad, s));
   T* z = static_cast<T*>(p.z);
   for (int64_t r0 = 0; r0 < n; r0 += p.chunk) {
     const int rows = (int)std::min<int64_t>(p.chunk, n - r0);
     const T* Hc = H + r0 * d;
     EpiLceLogits<T> epi{z, p.vpad, p.part, p.nparts, softcap, 1.f / softcap};
-    LL_HIP(launch_gemm_nt(Hc, (int64_t)d, W, (int64_t)d, rows, (int)v, d, epi, s));
+    {
+      const hipError_t e = launch_gemm_with(gemm_config_override() >= 2 ? gemm_config_override() : 3,
+                                            Hc, (int64_t)d, W, (int64_t)d, rows, (int)v, d, epi, GemmOps{}, s);
+      LL_HIP(e);
+    }
     LL_LAUNCH("lce_lse", (lce_lse_kernel<T>), dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, s, p.part, p.nparts, z,
-                       p.vpad, y + r0, rows, ignore, softcap, lse_out ? lse_out + r0 : nullptr, p.lse, p.loss_acc);
+              p.vpad, y + r0, rows, ignore, softcap, lse_out ? lse_out + r0 : nullptr, p.lse, p.loss_acc);
     LL_HIP(hipGetLastError());
     if (!grads) continue;
     const int rows_pad = (int)round_up(rows, 64);
-    dim3 g((unsigned)cdiv(p.vpad, 64), (unsigned)cdiv(rows_pad, 64));
-    LL_LAUNCH("lce_dz", (lce_dz_kernel<T>), g, dim3(256), 0, s, z, p.vpad, p.lse, y + r0, rows, rows_pad, (int)v,
-                       (int)p.vpad, ignore, softcap, grad_scale, p.nv, z, static_cast<T*>(p.dzt), (int64_t)rows_pad);
+    if constexpr (kMN) {
+      const int64_t work = (int64_t)rows * (p.vpad / 8);
+      LL_LAUNCH("lce_dz", (lce_dz_inplace_kernel<T>), dim3((unsigned)std::min<int64_t>(cdiv(work, 256), 16384)),
+                dim3(256), 0, s, z, p.vpad, p.lse, y + r0, rows, (int)v, ignore, softcap, grad_scale, p.nv);
+    } else {
+      dim3 g((unsigned)cdiv(p.vpad, 64), (unsigned)cdiv(rows_pad, 64));
+      LL_LAUNCH("lce_dz", (lce_dz_kernel<T>), g, dim3(256), 0, s, z, p.vpad, p.lse, y + r0, rows, rows_pad, (int)v,
+                (int)p.vpad, ignore, softcap, grad_scale, p.nv, z, static_cast<T*>(p.dzt), (int64_t)rows_pad);
+    }
     LL_HIP(hipGetLastError());
-    // dH_c = dz W  (B operand: W^T [D, Vpad])
     EpiStore<T> eh{dH + r0 * d, (int64_t)d, Deq{nullptr, nullptr}};
-    LL_HIP(launch_gemm_nt(z, p.vpad, static_cast<const T*>(p.wt), p.vpad, rows, d, (int)p.vpad, eh, s));
-    // dW += dz^T H_c  (A: dz^T [Vpad, rows_pad], B: H_c^T [D, rows_pad])
-    LL_HIP(transpose2d(Hc, rows, d, (int64_t)d, static_cast<T*>(p.ht), (int64_t)rows_pad, (int64_t)rows_pad, s));
     EpiAcc32 ew{p.dw32, (int64_t)d, r0 > 0 ? 1 : 0};
-    LL_HIP(launch_gemm_nt(static_cast<const T*>(p.dzt), (int64_t)rows_pad, static_cast<const T*>(p.ht),
-                          (int64_t)rows_pad, (int)v, d, rows_pad, ew, s));
+    if constexpr (kMN) {
+      // dH_c = dz W: A = dz [rows, Vpad] (K-major), B(n = d, k = v) = W[v, d] (MN-major), K = V
+      LL_HIP(launch_gemm(z, p.vpad, W, (int64_t)d, rows, d, (int)v, eh, GemmOps{true, false, p.zrow}, s));
+      // dW += dz^T H_c: A(m = v, k = c) = dz[c, v], B(n = d, k = c) = H_c[c, d], both MN-major, K = rows
+      LL_HIP(launch_gemm(static_cast<const T*>(z), p.vpad, Hc, (int64_t)d, (int)v, d, rows, ew,
+                         GemmOps{false, false, p.zrow}, s));
+    } else {
+      LL_HIP(launch_gemm_nt(z, p.vpad, static_cast<const T*>(p.wt), p.vpad, rows, d, (int)p.vpad, eh, s));
+      LL_HIP(transpose2d(Hc, rows, d, (int64_t)d, static_cast<T*>(p.ht), (int64_t)rows_pad, (int64_t)rows_pad, s));
+      LL_HIP(launch_gemm_nt(static_cast<const T*>(p.dzt), (int64_t)rows_pad, static_cast<const T*>(p.ht),
+                            (int64_t)rows_pad, (int)v, d, rows_pad, ew, s));
+    }
   }
   if (grads) {
     if (n == 0) LL_HIP(fill_f32(p.dw32, 0.f, v * d, s));     // no chunk ran: dW = 0
