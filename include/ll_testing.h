@@ -30,10 +30,13 @@ int llt_gemm(int32_t op_dtype, int32_t a_kmajor, int32_t b_kmajor, const void* A
              int64_t ldb, int32_t M, int32_t N, int32_t K, int32_t out_dtype, void* C, int64_t ldc,
              const float* inv_a, const float* inv_b, void* ws, size_t ws_bytes, void* stream);
 
-/* Process-wide override of the GEMM block tile (for measurements): 0 = automatic (256 x 256 with
- * 4 waves when that gives >= 256 tiles, else 128 x 128), 1 = 128 x 128 / 4 waves, 2 = 256 x 256 /
- * 4 waves, 3 = 256 x 256 / 8 waves (2 x 4), 4 = 256 x 256 / 8 waves (4 x 2). The LCE logits GEMM
- * always uses a 256-wide vocabulary tile (configs 2-4). */
+/* Process-wide override of the GEMM configuration (for measurements). Block tile, waves, bytes of K
+ * per LDS tile row, LDS stages: 1 = 128 x 128, 4 waves, 128 B, 2; 2 = 256 x 256, 4 waves, 128 B, 2;
+ * 3 = 256 x 256, 8 waves (2 x 4), 128 B, 2; 4 = 256 x 256, 8 waves (4 x 2), 128 B, 2;
+ * 5 = 256 x 256, 8 waves (2 x 4), 64 B, 4; 6 = 256 x 256, 8 waves (4 x 2), 64 B, 4;
+ * 7 = 128 x 128, 4 waves, 64 B, 4. e4m3 GEMMs need 128-byte K tiles and run 5, 6, 7 as 3, 4, 1.
+ * 0 = automatic choice per GEMM shape. The LCE logits GEMM always uses a 256-wide vocabulary tile
+ * (configurations 1 and 7 select 3 there). */
 int llt_set_gemm_config(int32_t cfg);
 
 /* Launch trace: while tracing is on, every kernel launch of the library is bracketed by two HIP

@@ -193,3 +193,46 @@ def test_gemm_e4m3_products_and_accumulation_precision():
     got = float(C[0, 0].item())
     print(f"e4m3 MFMA: 2^16 + 127 * 1 = {got} (exact 65663)", flush=True)
     assert abs(got - 65663.0) <= 65663.0 * 2.0 ** -10
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("op,ak,bk,K", [
+    ("bf16", True, True, 64), ("bf16", True, True, 192), ("bf16", True, True, 320),
+    ("bf16", False, False, 200), ("bf16", True, False, 1000), ("bf16", False, True, 96),
+    ("fp32", True, True, 96), ("e4m3", True, True, 384),
+])
+def test_gemm_block_configs(cfg, op, ak, bk, K):
+    """Every block-tile / K-tile / LDS-stage configuration on ragged M and N and on K-tile counts
+    of 1 to 16, so that each pipeline depth meets its prologue, steady state and drain."""
+    need_gpu()
+    print(f"gemm cfg{cfg} {op} ak={ak} bk={bk} K={K}", flush=True)
+    M, N = 264, 520
+    if op == "e4m3":
+        rng = np.random.default_rng(K)
+        a_codes = rng.integers(0, 256, (M, K), dtype=np.uint8)
+        b_codes = rng.integers(0, 256, (N, K), dtype=np.uint8)
+        for c in (a_codes, b_codes):
+            c[((c & 0x7F) == 0x7F) | ((c & 0x78) == 0)] = 0x38
+        a, b = nu.e4m3_decode(a_codes), nu.e4m3_decode(b_codes)
+        A, B = torch.from_numpy(a_codes).cuda(), torch.from_numpy(b_codes).cuda()
+        opd, tol = ll._lib.LLT_OP_E4M3, (1e-4, 2e-3)
+    else:
+        a = synth.normal((M, K), 1.0, 4, 1, op)
+        b = synth.normal((N, K), 0.05, 4, 2, op)
+        A = dev(a if ak else np.ascontiguousarray(a.T), op)
+        B = dev(b if bk else np.ascontiguousarray(b.T), op)
+        opd, tol = (ll._lib.LLT_OP_BF16 if op == "bf16" else ll._lib.LLT_OP_F32), (1e-5, 1e-4)
+    if ak and op != "e4m3":
+        A = torch.nn.functional.pad(A, (0, (-K) % 64))      # K-major rows padded to the K tile
+    if bk and op != "e4m3":
+        B = torch.nn.functional.pad(B, (0, (-K) % 64))
+    ref = a.astype(np.float64) @ b.astype(np.float64).T
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    try:
+        ll._lib.llt_set_gemm_config(cfg)
+        ll.llt_gemm(opd, ak, bk, A, A.shape[1], B, B.shape[1], M, N, K, ll.LL_F32, C, N, None, None, ws, 256)
+        torch.cuda.synchronize()
+    finally:
+        ll._lib.llt_set_gemm_config(0)
+    assert_close(host(C), ref, tol[0], f"gemm cfg{cfg}", elem_rtol=tol[1])

@@ -350,8 +350,8 @@ attn_fwd_kernel(const ET* __restrict__ qh, const ET* __restrict__ kh, const ET* 
       for (int kk = 0; kk < KT; ++kk) {
         uint32_t kf[8];
         Tl::frag_rows(sK, i * 16, kk, kf);
-        Mma<ET>::run(s[i][0], kf, qf[0][kk]);
-        Mma<ET>::run(s[i][1], kf, qf[1][kk]);
+        Mma<ET>::template run<2>(s[i][0], kf, qf[0][kk]);
+        Mma<ET>::template run<2>(s[i][1], kf, qf[1][kk]);
       }
     }
 #pragma unroll
@@ -477,9 +477,9 @@ attn_bwd_dkdv_kernel(const ET* __restrict__ qh, const ET* __restrict__ kh, const
         for (int kk = 0; kk < KT; ++kk) {
           uint32_t f[8];
           Tl::frag_rows(sQ, i * 16, kk, f);
-          Mma<ET>::run(s, f, kf[kk]);
+          Mma<ET>::template run<2>(s, f, kf[kk]);
           Tl::frag_rows(sD, i * 16, kk, f);
-          Mma<ET>::run(dp, f, vf[kk]);
+          Mma<ET>::template run<2>(dp, f, vf[kk]);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -568,9 +568,9 @@ attn_bwd_dq_kernel(const ET* __restrict__ qh, const ET* __restrict__ kh, const E
       for (int kk = 0; kk < KT; ++kk) {
         uint32_t f[8];
         Tl::frag_rows(sK, i * 16, kk, f);
-        Mma<ET>::run(s, f, qf[kk]);
+        Mma<ET>::template run<2>(s, f, qf[kk]);
         Tl::frag_rows(sV, i * 16, kk, f);
-        Mma<ET>::run(dp, f, of[kk]);
+        Mma<ET>::template run<2>(dp, f, of[kk]);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {

@@ -17,6 +17,7 @@
 // columns of one row per thread (16-byte coalesced stores, row reductions across 16 lanes).
 #pragma once
 #include <string>
+#include <type_traits>
 
 #include "common.h"
 
@@ -27,30 +28,54 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// One 16 x 16 output fragment += first . second^T over the NC 16-byte chunks (NC = 1 or 2) of K
+// that each lane holds for its row / column. Fragments stay whole 16-byte vectors from the LDS read
+// to the MFMA (the vector loads then keep the LDS alias scope of the stage they read).
 template <class ET> struct Mma;
 template <> struct Mma<float> {
+  template <int NC>
+  __device__ __forceinline__ static void run(floatx4& acc, const u32x4 (&a)[2], const u32x4 (&b)[2]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[c][s]), __uint_as_float(b[c][s]), acc, 0, 0, 0);
+  }
+  template <int NC>
   __device__ __forceinline__ static void run(floatx4& acc, const uint32_t (&a)[8], const uint32_t (&b)[8]) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int s = 0; s < 4 * NC; ++s)
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[s]), __uint_as_float(b[s]), acc, 0, 0, 0);
   }
 };
 template <> struct Mma<bf16> {
+  template <int NC>
+  __device__ __forceinline__ static void run(floatx4& acc, const u32x4 (&a)[2], const u32x4 (&b)[2]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[c]),
+                                                     __builtin_bit_cast(bf16x8_t, b[c]), acc, 0, 0, 0);
+  }
+  template <int NC>
   __device__ __forceinline__ static void run(floatx4& acc, const uint32_t (&a)[8], const uint32_t (&b)[8]) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint4 ua = make_uint4(a[4 * s], a[4 * s + 1], a[4 * s + 2], a[4 * s + 3]);
-      uint4 ub = make_uint4(b[4 * s], b[4 * s + 1], b[4 * s + 2], b[4 * s + 3]);
+    for (int s = 0; s < NC; ++s) {
+      u32x4 ua = {a[4 * s], a[4 * s + 1], a[4 * s + 2], a[4 * s + 3]};
+      u32x4 ub = {b[4 * s], b[4 * s + 1], b[4 * s + 2], b[4 * s + 3]};
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ua),
                                                      __builtin_bit_cast(bf16x8_t, ub), acc, 0, 0, 0);
     }
   }
 };
 template <> struct Mma<fp8> {
-  __device__ __forceinline__ static void run(floatx4& acc, const uint32_t (&a)[8], const uint32_t (&b)[8]) {
-    intx8 va, vb;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { va[i] = (int)a[i]; vb[i] = (int)b[i]; }
+  template <int NC>
+  __device__ __forceinline__ static void run(floatx4& acc, const u32x4 (&a)[2], const u32x4 (&b)[2]) {
+    static_assert(NC == 2, "the e4m3 MFMA takes 32 bytes of K per lane");
+    const intx8 va = __builtin_bit_cast(intx8, __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    const intx8 vb = __builtin_bit_cast(intx8, __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7));
     // format 0 = e4m3 for both operands; E8M0 block scales 127 = 2^0
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, vb, acc, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
   }
@@ -59,46 +84,42 @@ template <> struct Mma<fp8> {
 enum EpiKind { kEpiPlain = 0, kEpiAmax = 1, kEpiRowLse = 2 };
 
 constexpr int kGemmThreads = 256;
-constexpr int kSlabRows = 64;
-
-template <int BM, int BN>
-struct GemmSmem {
-  static constexpr int kOperand = 2 * (BM + BN) * 128;              // bytes, 2 stages
-  static constexpr int kSlab = kSlabRows * (BN + 4) * 4;            // fp32 slab + pad
-  static constexpr int kBytes = kOperand > kSlab ? kOperand : kSlab;
-};
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
-// 16-byte chunk swizzles. K-major tiles (rows of 128 B): chunk ^ ((row >> 1) & 7) puts the 16
-// rows of a fragment read on 16 distinct (bank half, chunk) slots. MN-major tiles (k rows of
-// ROWS elements): chunk ^ mn_swz(k) spreads the 4 k-rows of one transpose read over distinct
-// chunk pairs, and alternating 16-row k groups over the two halves of the bank window.
-__device__ __forceinline__ int kmaj_swz(int row) { return (row >> 1) & 7; }
+// 16-byte chunk swizzles. K-major tiles (rows of KB bytes): the 16 rows of a fragment read land on
+// 16 distinct (row slot in the 256-byte bank window, chunk) pairs. MN-major tiles (k rows of ROWS
+// elements): chunk ^ mn_swz(k) spreads the 4 k-rows of one transpose read over distinct chunk
+// pairs, and alternating 16-row k groups over the two halves of the bank window.
+template <int KB>
+__device__ __forceinline__ int kmaj_swz(int row) {
+  if constexpr (KB == 128) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
 __device__ __forceinline__ int mn_swz(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 4) & 1)); }
 
 // Issue the direct global->LDS loads of one operand tile for K tile kt (this wave's share).
-//   K-major: element (r, k) at g[r * ld + k]; tile = ROWS rows x 128 B.
-//   MN-major: element (r, k) at g[k * ld + r]; tile = KE k-rows x ROWS elements; k-rows at or
+//   K-major: element (r, k) at g[r * ld + k]; tile = ROWS rows x KB bytes.
+//   MN-major: element (r, k) at g[k * ld + r]; tile = KB/es k-rows x ROWS elements; k-rows at or
 //   beyond kvalid read the zero row instead (the K tail of a token-contracted GEMM).
 // Rows/columns past rmax are clamped to valid memory; they only feed outputs that are not stored.
-template <class ET, bool KMAJ, int ROWS, int NW>
+template <class ET, bool KMAJ, int ROWS, int KB, int NW>
 __device__ __forceinline__ void issue_tile(const char* g, int64_t ldb, int r0, int rmax, int kt, int kvalid,
                                            const char* zrow, unsigned char* lds_op, int wave, int lane) {
-  constexpr int TILE = ROWS * 128;
+  constexpr int TILE = ROWS * KB;
   constexpr int NI = TILE / 1024 / NW;
+  constexpr int KE = KB / (int)sizeof(ET);
   static_assert(NI >= 1 && NI * 1024 * NW == TILE, "tile must split evenly over the waves");
-  constexpr int KE = 128 / (int)sizeof(ET);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int base = (wave * NI + i) * 1024;
     const char* src;
     if constexpr (KMAJ) {
-      const int row = base / 128 + (lane >> 3);
-      const int logical = (lane & 7) ^ kmaj_swz(row);
+      constexpr int CPR = KB / 16;
+      const int row = base / KB + lane / CPR;
+      const int logical = (lane % CPR) ^ kmaj_swz<KB>(row);
       const int gr = min(r0 + row, rmax - 1);
-      src = g + gr * ldb + (int64_t)kt * 128 + logical * 16;
+      src = g + gr * ldb + (int64_t)kt * KB + logical * 16;
     } else {
       constexpr int CPR = ROWS * (int)sizeof(ET) / 16;
       const int sidx = base / 16 + lane;
@@ -106,55 +127,81 @@ __device__ __forceinline__ void issue_tile(const char* g, int64_t ldb, int r0, i
       const int logical = (sidx % CPR) ^ mn_swz(krow);
       const int k = kt * KE + krow;
       const int col = min(r0 + logical * (16 / (int)sizeof(ET)), rmax - 16 / (int)sizeof(ET));
-      src = k < kvalid ? g + (int64_t)k * ldb + (int64_t)col * (int)sizeof(ET) : zrow;
+      // address formed for every lane (k clamped to a valid row), then a select: no branch
+      const char* rowp = g + (int64_t)min(k, kvalid - 1) * ldb + (int64_t)col * (int)sizeof(ET);
+      src = k < kvalid ? rowp : zrow;
     }
     __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(lds_op + base), 16, 0, 0);
   }
 }
 
-// Fragment of 16 rows (K-major) or 16 columns (MN-major) starting at f0: 32 bytes per lane,
-// lane (index l & 15, group g = l >> 4) holds K elements [16g, 16g + 16) of the 64 bf16 (or the
-// type's equivalent 32 bytes) of this K tile, in the same order for both layouts.
-template <bool KMAJ, int ROWS>
-__device__ __forceinline__ void read_frag(const unsigned char* t, int f0, int lane, uint32_t (&f)[8]) {
+// Fragment of 16 rows (K-major) or 16 columns (MN-major) starting at f0: KB/4 bytes per lane;
+// lane (index l & 15, group g = l >> 4) holds chunks [g * KB/64, (g+1) * KB/64) of 16 bytes of
+// the K tile, in the same K order for both layouts. The tile starts at byte off of the stage array
+// t; each address is formed as t + (integer offset) so that every LDS read stays a direct
+// derivative of its stage array (the compiler then keeps the reads apart from the direct loads
+// into the other stages).
+template <bool KMAJ, int ROWS, int KB>
+__device__ __forceinline__ void read_frag(const unsigned char* t, int off, int f0, int lane, u32x4 (&f)[2]) {
+  constexpr int NC = KB / 64;
   const int g = lane >> 4;
   if constexpr (KMAJ) {
-    const int row = f0 + (lane & 15), sw = kmaj_swz(row);
-    const uint4 lo = *reinterpret_cast<const uint4*>(t + row * 128 + ((2 * g) ^ sw) * 16);
-    const uint4 hi = *reinterpret_cast<const uint4*>(t + row * 128 + ((2 * g + 1) ^ sw) * 16);
-    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w; f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+    const int row = f0 + (lane & 15), sw = kmaj_swz<KB>(row);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) f[c] = *reinterpret_cast<const u32x4*>(t + (off + row * KB + ((NC * g + c) ^ sw) * 16));
   } else {
-    // bf16 only: four ds_read_b64_tr_b16, each giving this lane's column at 4 consecutive k
+    // bf16 only: ds_read_b64_tr_b16, each giving this lane's column at 4 consecutive k
     constexpr int RB = ROWS * 2;
     const int li = lane & 15, r = li >> 2, j = li & 3;
     const int col = f0 + 4 * j;
     const int chunk = col >> 3, within = (col & 7) * 2;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {                  // q = 2 * substep + half
-      const int k = 16 * g + 4 * q + r;
-      const unsigned char* a = t + k * RB + ((chunk ^ mn_swz(k)) * 16) + within;
-      const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(a));
-      const uint2 u = __builtin_bit_cast(uint2, v);
-      f[2 * q] = u.x;
-      f[2 * q + 1] = u.y;
+    for (int c = 0; c < NC; ++c) {
+      u32x2 h[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int k = 8 * NC * g + 8 * c + 4 * q + r;
+        const unsigned char* a = t + (off + k * RB + ((chunk ^ mn_swz(k)) * 16) + within);
+        h[q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                              (__attribute__((address_space(3))) shortx4*)(a)));
+      }
+      f[c] = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3);
     }
   }
 }
 
+// s_waitcnt vmcnt(N) only (expcnt and lgkmcnt fields at their no-wait maxima). Issued through the
+// builtin so that the compiler's own wait insertion knows which loads have completed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // C[m, n] = sum_k A(m, k) B(n, k), A(m, k) = AK ? A[m * lda + k] : A[k * lda + m] (likewise B).
-// WGM x WGN waves; wave tile (BM/WGM) x (BN/WGN) in 16 x 16 MFMA fragments.
-template <class ET, int BM, int BN, int WGM, int WGN, bool AK, bool BK, class Epi>
+// WGM x WGN waves; wave tile (BM/WGM) x (BN/WGN) in 16 x 16 MFMA fragments. K advances KB bytes
+// per tile through an NS-stage LDS ring: tile kt + NS - 1 is in flight while tile kt is multiplied.
+template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, bool AK, bool BK, class Epi>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int64_t ldb, int M, int N, int K,
             const ET* __restrict__ zrow, Epi epi) {
   static_assert((AK && BK) || sizeof(ET) == 2, "MN-major operands are bf16 only");
+  static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
   constexpr int NW = WGM * WGN, NT = 64 * NW;
   constexpr int WN = WGN;
   constexpr int TM = BM / WGM, TN = BN / WGN;
   constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int KE = 128 / (int)sizeof(ET);
-  constexpr int STAGE = (BM + BN) * 128;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[GemmSmem<BM, BN>::kBytes];
+  constexpr int KE = KB / (int)sizeof(ET);
+  constexpr int NC = KB / 64;
+  constexpr int STAGE = (BM + BN) * KB;
+  constexpr int NIW = STAGE / 1024 / NW;                    // load instructions per wave per tile
+  // One LDS array per stage: distinct objects let the compiler see that the direct loads into the
+  // next stages do not alias the fragment reads of the current one (a single array indexed by
+  // stage makes it wait for every load in flight before the first read of each tile).
+  __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st2[NS > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char st3[NS > 3 ? STAGE : 16];
 
   const int nbm = (int)cdiv(M, BM), nbn = (int)cdiv(N, BN);
   const int nb = nbm * nbn;
@@ -172,10 +219,16 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   const char* zb = reinterpret_cast<const char*>(zrow);
   const int64_t ldab = lda * (int64_t)sizeof(ET), ldbb = ldb * (int64_t)sizeof(ET);
 
-  auto issue = [&](int kt, int st) {
-    unsigned char* sa = smem + st * STAGE;
-    issue_tile<ET, AK, BM, NW>(Ab, ldab, m0, M, kt, K, zb, sa, wave, lane);
-    issue_tile<ET, BK, BN, NW>(Bb, ldbb, n0, N, kt, K, zb, sa + BM * 128, wave, lane);
+  auto stage = [&](auto si) -> unsigned char* {
+    constexpr int S = decltype(si)::value;
+    if constexpr (S == 0) return st0;
+    else if constexpr (S == 1) return st1;
+    else if constexpr (S == 2) return st2;
+    else return st3;
+  };
+  auto issue = [&](int kt, unsigned char* sa) {
+    issue_tile<ET, AK, BM, KB, NW>(Ab, ldab, m0, M, kt, K, zb, sa, wave, lane);
+    issue_tile<ET, BK, BN, KB, NW>(Bb, ldbb, n0, N, kt, K, zb, sa + BM * KB, wave, lane);
   };
 
   floatx4 acc[FN][FM];
@@ -185,32 +238,54 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
     for (int j = 0; j < FM; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (int)cdiv(K, KE);
-  if (nk > 0) issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) issue(kt + 1, st ^ 1);
-    const unsigned char* sa = smem + st * STAGE;
-    const unsigned char* sb = sa + BM * 128;
-    uint32_t bf[FN][8];
+  // K tile kt lives in stage kt % NS; step<S> handles the tiles with kt % NS == S. Every step
+  // issues exactly one tile (NIW loads per wave), so NS - 1 tiles are always in flight and one
+  // constant wait count holds in every step: past the last tile, the loads repeat tile nk - 1
+  // into stages that are not read again (an L2 hit; the drain below waits for them).
+  auto step = [&](auto si, int kt) {
+    constexpr int S = decltype(si)::value;
+    wait_vmcnt<(NS - 2) * NIW>();                           // tile kt has landed (this wave's part)
+    // Barrier without a memory fence: a fence would also wait for the loads of the later tiles.
+    // Every wave's part of tile kt has landed once all waves pass it, and the MFMAs of kt - 1
+    // have consumed every fragment read of the stage refilled next; the memory clobber keeps the
+    // compiler from moving LDS accesses across it.
+    asm volatile("s_barrier" ::: "memory");
+    issue(min(kt + NS - 1, nk - 1), stage(std::integral_constant<int, (S + NS - 1) % NS>{}));
+    const unsigned char* sa = stage(si);
+    {
+      u32x4 bf[FN][2];
 #pragma unroll
-    for (int i = 0; i < FN; ++i) read_frag<BK, BN>(sb, wn * TN + i * 16, lane, bf[i]);
+      for (int i = 0; i < FN; ++i) read_frag<BK, BN, KB>(sa, BM * KB, wn * TN + i * 16, lane, bf[i]);
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      uint32_t af[8];
-      read_frag<AK, BM>(sa, wm * TM + j * 16, lane, af);
+      for (int j = 0; j < FM; ++j) {
+        u32x4 af[2];
+        read_frag<AK, BM, KB>(sa, 0, wm * TM + j * 16, lane, af);
 #pragma unroll
-      for (int i = 0; i < FN; ++i) Mma<ET>::run(acc[i][j], bf[i], af);
+        for (int i = 0; i < FN; ++i) Mma<ET>::template run<NC>(acc[i][j], bf[i], af);
+      }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  };
+
+  if (nk > 0) {
+    issue(0, st0);
+    if constexpr (NS > 2) issue(min(1, nk - 1), st1);
+    if constexpr (NS > 3) issue(min(2, nk - 1), st2);
   }
+  for (int kb = 0; kb < nk; kb += NS) {
+    step(std::integral_constant<int, 0>{}, kb);
+    if (kb + 1 < nk) step(std::integral_constant<int, 1>{}, kb + 1);
+    if constexpr (NS > 2) if (kb + 2 < nk) step(std::integral_constant<int, 2>{}, kb + 2);
+    if constexpr (NS > 3) if (kb + 3 < nk) step(std::integral_constant<int, 3>{}, kb + 3);
+  }
+  wait_vmcnt<0>();                                          // drain the repeated tail loads
+  __syncthreads();
 
   const int g = lane >> 4, r16 = lane & 15;
-  // ---------------- epilogue: accumulator -> LDS slab (64 rows) -> functor on row segments
-  float* slab = reinterpret_cast<float*>(smem);
+  // ---------------- epilogue: accumulator -> LDS slab (stage 0) -> functor on row segments
+  float* slab = reinterpret_cast<float*>(st0);
   constexpr int LDS_LD = BN + 4;
+  constexpr int kSlabRows = STAGE / (LDS_LD * 4) >= 64 ? 64 : STAGE / (LDS_LD * 4) >= 32 ? 32 : 16;
+  static_assert(kSlabRows * LDS_LD * 4 <= STAGE, "slab must fit in one stage");
   constexpr int SEGS = BN / 8;                              // 8-column segments per row
   constexpr int ROWS_PER_PASS = NT / SEGS;
   float red_amax = 0.f;
@@ -398,7 +473,7 @@ struct GemmOps {
   const void* zrow = nullptr;       // >= 16 zero bytes: K-tail rows of MN-major operands
 };
 
-template <class ET, int BM, int BN, int WGM, int WGN, class Epi>
+template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, class Epi>
 inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
                                   const Epi& epi, const GemmOps& o, hipStream_t s) {
   const int64_t nb = cdiv(M, BM) * cdiv(N, BN);
@@ -407,37 +482,53 @@ inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t
   constexpr int NT = 64 * WGM * WGN;
   if constexpr (sizeof(ET) == 2) {
     if (!o.a_kmajor && !o.b_kmajor) {
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, false, false, Epi>), dim3((unsigned)nb), dim3(NT),
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, false, Epi>), dim3((unsigned)nb), dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
     if (!o.a_kmajor) {
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, false, true, Epi>), dim3((unsigned)nb), dim3(NT),
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, true, Epi>), dim3((unsigned)nb), dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
     if (!o.b_kmajor) {
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, true, false, Epi>), dim3((unsigned)nb), dim3(NT),
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, false, Epi>), dim3((unsigned)nb), dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
   }
-  LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, true, true, Epi>), dim3((unsigned)nb), dim3(NT), 0, s,
+  LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, true, Epi>), dim3((unsigned)nb), dim3(NT), 0, s,
                 A, lda, B, ldb, M, N, K, z, epi);
   return hipGetLastError();
 }
 
-// Block-tile configurations: 1 = 128 x 128 (4 waves), 2 = 256 x 256 (4 waves), 3 = 256 x 256
-// (8 waves, 2 x 4), 4 = 256 x 256 (8 waves, 4 x 2); 0 = automatic (gemm_config_override()).
-
+// Block-tile configurations (block tile, waves, K-tile bytes, LDS stages):
+//   1 = 128 x 128, 4 waves, 128 B, 2      2 = 256 x 256, 4 waves (2 x 2), 128 B, 2
+//   3 = 256 x 256, 8 waves (2 x 4), 128 B, 2   4 = 256 x 256, 8 waves (4 x 2), 128 B, 2
+//   5 = 256 x 256, 8 waves (2 x 4), 64 B, 4    6 = 256 x 256, 8 waves (4 x 2), 64 B, 4
+//   7 = 128 x 128, 4 waves, 64 B, 4
+// e4m3 needs 128-byte K tiles (32 bytes of K per lane per MFMA): 5, 6, 7 fall back to 3, 4, 1.
+// 0 = automatic (gemm_config_override()).
 template <class ET, class Epi>
 inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
                                    const Epi& epi, const GemmOps& o, hipStream_t s) {
+  if constexpr (sizeof(ET) == 1) {
+    if (cfg == 5) cfg = 3;
+    if (cfg == 6) cfg = 4;
+    if (cfg == 7) cfg = 1;
+  }
   switch (cfg) {
-    case 1: return launch_gemm_cfg<ET, 128, 128, 2, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
-    case 2: return launch_gemm_cfg<ET, 256, 256, 2, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
-    case 3: return launch_gemm_cfg<ET, 256, 256, 2, 4>(A, lda, B, ldb, M, N, K, epi, o, s);
-    default: return launch_gemm_cfg<ET, 256, 256, 4, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+    case 1: return launch_gemm_cfg<ET, 128, 128, 2, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+    case 2: return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+    case 3: return launch_gemm_cfg<ET, 256, 256, 2, 4, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+    case 4: return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+    default:
+      if constexpr (sizeof(ET) != 1) {
+        if (cfg == 5) return launch_gemm_cfg<ET, 256, 256, 2, 4, 64, 4>(A, lda, B, ldb, M, N, K, epi, o, s);
+        if (cfg == 6) return launch_gemm_cfg<ET, 256, 256, 4, 2, 64, 4>(A, lda, B, ldb, M, N, K, epi, o, s);
+        if (cfg == 7) return launch_gemm_cfg<ET, 128, 128, 2, 2, 64, 4>(A, lda, B, ldb, M, N, K, epi, o, s);
+      }
+      return launch_gemm_cfg<ET, 256, 256, 2, 4, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
   }
 }
 

@@ -75,7 +75,9 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     const T* Hc = H + r0 * d;
     EpiLceLogits<T> epi{z, p.vpad, p.part, p.nparts, softcap, 1.f / softcap};
     {
-      const hipError_t e = launch_gemm_with(gemm_config_override() >= 2 ? gemm_config_override() : 3,
+      // the row-LSE partials assume 256 vocabulary columns per block tile
+      const int oc = gemm_config_override();
+      const hipError_t e = launch_gemm_with(oc >= 2 && oc <= 6 ? oc : 3,
                                             Hc, (int64_t)d, W, (int64_t)d, rows, (int)v, d, epi, GemmOps{}, s);
       LL_HIP(e);
     }
