@@ -64,6 +64,31 @@ template <> struct Vec8<float> {
   }
 };
 
+// 4 consecutive elements <-> 4 floats (8 B for bf16, 16 B for fp32).
+template <class T> struct Vec4;
+template <> struct Vec4<bf16> {
+  __device__ __forceinline__ static void load(const bf16* p, float (&v)[4]) {
+    const uint2 r = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(r.x << 16); v[1] = __uint_as_float(r.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(r.y << 16); v[3] = __uint_as_float(r.y & 0xFFFF0000u);
+  }
+  __device__ __forceinline__ static void store(bf16* p, const float (&v)[4]) {
+    uint2 r;
+    r.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    r.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = r;
+  }
+};
+template <> struct Vec4<float> {
+  __device__ __forceinline__ static void load(const float* p, float (&v)[4]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+  __device__ __forceinline__ static void store(float* p, const float (&v)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
 // ------------------------------------------------------------------ e4m3fn
 // Round a finite fp32 with |v| <= 448 to the nearest e4m3fn code, ties to even. Written from the
 // OCP E4M3 definition: bias 7, 3 mantissa bits, subnormal quantum 2^-9, largest finite 448.

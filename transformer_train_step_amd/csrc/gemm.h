@@ -281,36 +281,51 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   __syncthreads();
 
   const int g = lane >> 4, r16 = lane & 15;
-  // ---------------- epilogue: accumulator -> LDS slab (stage 0) -> functor on row segments
-  float* slab = reinterpret_cast<float*>(st0);
-  constexpr int LDS_LD = BN + 4;
-  constexpr int kSlabRows = STAGE / (LDS_LD * 4) >= 64 ? 64 : STAGE / (LDS_LD * 4) >= 32 ? 32 : 16;
-  static_assert(kSlabRows * LDS_LD * 4 <= STAGE, "slab must fit in one stage");
-  constexpr int SEGS = BN / 8;                              // 8-column segments per row
-  constexpr int ROWS_PER_PASS = NT / SEGS;
+  // ---------------- epilogue: accumulators -> LDS slab -> functor on 8-column segments of rows.
+  // A pass covers PR = 2 SR rows, rows [0, SR) in stage array 0 and [SR, 2 SR) in stage array 1
+  // (all loads have drained). Slab rows hold BN floats with no padding; 16-byte chunk c of row r
+  // sits at chunk c ^ x(r), x(r) = 2 (r & 7) + ((r >> 3) & 1), a bijection over 16 rows, so each
+  // fragment write (16 rows x one chunk per 16 lanes) is conflict-free. In the read phase a lane
+  // takes the chunk pair (2 s, 2 s + 1) of a row, the lower half of each 8 lanes the even chunk
+  // first and the upper half the odd one, so that 16 lanes again hit 16 distinct bank slots.
+  constexpr int CPR = BN / 4;                               // 16-byte chunks per slab row
+  constexpr int SR = STAGE / (BN * 4) >= 64 ? 64 : STAGE / (BN * 4) >= 32 ? 32 : 16;
+  constexpr int PR = 2 * SR;
+  constexpr int SPR = CPR / 2;                              // 8-column segments per row
+  constexpr int RPI = 64 / SPR;                             // rows per wave instruction
+  static_assert(CPR >= 16 && CPR <= 64 && SR >= 16 && SR * BN * 4 <= STAGE, "slab shape");
+  static_assert(BM % PR == 0 || PR > BM, "passes must tile the block rows");
+  auto slab_row = [&](int r) -> float* {
+    return reinterpret_cast<float*>(r < SR ? st0 : st1) + (r < SR ? r : r - SR) * BN;
+  };
+  auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
   float red_amax = 0.f;
 #pragma unroll 1
-  for (int s0 = 0; s0 < BM; s0 += kSlabRows) {
+  for (int s0 = 0; s0 < BM; s0 += PR) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int rloc = wm * TM + j * 16 + r16 - s0;
-      if (rloc >= 0 && rloc < kSlabRows) {
+      if (rloc >= 0 && rloc < PR) {                         // uniform over each 16-row fragment
+        float* row = slab_row(rloc);
+        const int x = swz(rloc);
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
-          const int c = wn * TN + i * 16 + 4 * g;
-          *reinterpret_cast<floatx4*>(slab + rloc * LDS_LD + c) = acc[i][j];
+          const int c = ((wn * TN + i * 16) >> 2) + g;
+          *reinterpret_cast<floatx4*>(row + ((c ^ x) << 2)) = acc[i][j];
         }
       }
     }
     __syncthreads();
 #pragma unroll 1
-    for (int p = 0; p < kSlabRows; p += ROWS_PER_PASS) {
-      const int rloc = p + tid / SEGS, seg = tid % SEGS;
-      const int m = m0 + s0 + rloc, n = n0 + seg * 8;
-      float v[8];
-      const float4 x0 = *reinterpret_cast<const float4*>(slab + rloc * LDS_LD + seg * 8);
-      const float4 x1 = *reinterpret_cast<const float4*>(slab + rloc * LDS_LD + seg * 8 + 4);
-      v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w; v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+    for (int p = wave * RPI; p < PR && s0 + p < BM; p += NW * RPI) {
+      const int rloc = p + lane / SPR, sg = lane % SPR;
+      const int m = m0 + s0 + rloc, n = n0 + 8 * sg;
+      const float* row = slab_row(rloc);
+      const int x = swz(rloc), odd = (sg >> 3) & 1;
+      const floatx4 u0 = *reinterpret_cast<const floatx4*>(row + (((2 * sg + odd) ^ x) << 2));
+      const floatx4 u1 = *reinterpret_cast<const floatx4*>(row + (((2 * sg + 1 - odd) ^ x) << 2));
+      const floatx4 lo = odd ? u1 : u0, hi = odd ? u0 : u1;
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       const bool ok = (m < M) && (n < N);
       if constexpr (Epi::kKind == kEpiPlain) {
         if (ok) epi.seg(m, n, v);
@@ -319,15 +334,15 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
       } else {
         float mx = -INFINITY, se = 0.f;
         if (ok) epi.seg(m, n, v, mx, se);
-        // combine the SEGS (<= 16) segments of this row: lanes tid % SEGS are consecutive
+        // combine the SPR segments of this row (consecutive lanes)
 #pragma unroll
-        for (int o = 1; o < SEGS && o < 64; o <<= 1) {
+        for (int o = 1; o < SPR; o <<= 1) {
           const float om = __shfl_xor(mx, o, 64), os = __shfl_xor(se, o, 64);
           const float nm = fmaxf(mx, om);
           se = (nm == -INFINITY) ? 0.f : se * __expf(mx - nm) + os * __expf(om - nm);
           mx = nm;
         }
-        if (seg == 0 && m < M) epi.row(m, bn, mx, se);
+        if (sg == 0 && m < M) epi.row(m, bn, mx, se);
       }
     }
     __syncthreads();
@@ -505,8 +520,8 @@ inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t
 // Block-tile configurations (block tile, waves, K-tile bytes, LDS stages):
 //   1 = 128 x 128, 4 waves, 128 B, 2      2 = 256 x 256, 4 waves (2 x 2), 128 B, 2
 //   3 = 256 x 256, 8 waves (2 x 4), 128 B, 2   4 = 256 x 256, 8 waves (4 x 2), 128 B, 2
-//   5 = 256 x 256, 8 waves (2 x 4), 64 B, 4    6 = 256 x 256, 8 waves (4 x 2), 64 B, 4
-//   7 = 128 x 128, 4 waves, 64 B, 4
+//   5 = 256 x 256, 8 waves (2 x 4), 64 B, 3    6 = 256 x 256, 8 waves (4 x 2), 64 B, 3
+//   7 = 128 x 128, 4 waves, 64 B, 3
 // e4m3 needs 128-byte K tiles (32 bytes of K per lane per MFMA): 5, 6, 7 fall back to 3, 4, 1.
 // 0 = automatic (gemm_config_override()).
 template <class ET, class Epi>
@@ -524,17 +539,17 @@ inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* 
     case 4: return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
     default:
       if constexpr (sizeof(ET) != 1) {
-        if (cfg == 5) return launch_gemm_cfg<ET, 256, 256, 2, 4, 64, 4>(A, lda, B, ldb, M, N, K, epi, o, s);
-        if (cfg == 6) return launch_gemm_cfg<ET, 256, 256, 4, 2, 64, 4>(A, lda, B, ldb, M, N, K, epi, o, s);
-        if (cfg == 7) return launch_gemm_cfg<ET, 128, 128, 2, 2, 64, 4>(A, lda, B, ldb, M, N, K, epi, o, s);
+        if (cfg == 5) return launch_gemm_cfg<ET, 256, 256, 2, 4, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
+        if (cfg == 6) return launch_gemm_cfg<ET, 256, 256, 4, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
+        if (cfg == 7) return launch_gemm_cfg<ET, 128, 128, 2, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
       }
       return launch_gemm_cfg<ET, 256, 256, 2, 4, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
   }
 }
 
 // Picks the block tile from the wave quantisation on 256 CUs: 256 x 256 with 8 waves (measured
-// ~15% faster per FLOP than 128 x 128 on the layer's shapes) unless its last wave of blocks leaves
-// so many CUs idle that 128 x 128 finishes first. Requirements (checked by the callers): K a multiple of the K tile for K-major
+// ~25% faster per FLOP than 128 x 128 on the layer's shapes) unless its last wave of blocks
+// leaves so many CUs idle that 128 x 128 finishes first. Requirements (checked by the callers): K a multiple of the K tile for K-major
 // operands (64 bf16, 128 e4m3, 32 fp32) or rows zero-padded to it; MN-major operands bf16 with M
 // (or N) a multiple of 8 and >= 8, and a zero row for the K tail; N a multiple of 8.
 template <class ET, class Epi>
@@ -545,8 +560,9 @@ inline hipError_t launch_gemm(const ET* A, int64_t lda, const ET* B, int64_t ldb
   if (cfg == 0) {
     const int64_t t256 = cdiv(M, 256) * cdiv(N, 256), t128 = cdiv(M, 128) * cdiv(N, 128);
     const double e256 = (double)t256 / (double)(cdiv(t256, 256) * 256);
-    const double e128 = 0.85 * (double)t128 / (double)(cdiv(t128, 256) * 256);
-    cfg = e256 >= e128 ? 3 : 1;
+    const double e128 = 0.75 * (double)t128 / (double)(cdiv(t128, 256) * 256);
+    // 4 x 2 waves, except 2 x 4 when B is MN-major (measured ~3% faster there)
+    cfg = e256 >= e128 ? (o.b_kmajor ? 4 : 3) : 1;
   }
   return launch_gemm_with(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
 }
