@@ -7,8 +7,8 @@ cross-entropy (softcap 15, 50304-padded vocab) on its output with loss and both 
 layer backward from that gradient. Every kernel is libll's (HIP, gfx950); inputs are resident in
 HBM before the timed region. Prints one JSON line on stdout; progress goes to stderr.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload layer_lce|layer|layer_ve_2k|lce]
-                    [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload layer_lce|layer|layer_ve_2k|lce|model] [--no-cpu-baseline]
 
 FLOP accounting (algorithmic, not executed work): per token of one layer, fwd + bwd,
 6 * P_mm + 6 * Hq * Dh * (T + 1) with P_mm = 100,663,296 matrix weights (causal attention counted
@@ -58,6 +58,10 @@ WORKLOADS = {
     "lce": dict(batch=40, seq=1024, ve=False, layer=False, lce=True,
                 desc="fused linear cross-entropy fwd+bwd (hidden 40960x3072 bf16 N(0,1), head 50304x3072 "
                      "N(0,0.02), softcap 15)"),
+    "model": dict(batch=40, seq=1024, ve=True, layer=True, lce=True, layers=28,
+                  desc="full 3.848B model fwd+bwd (token embedding 50304x3072, 28 decoder layers with value "
+                       "embeddings on the 14 even layers, FP8 e4m3 MLPs, final RMSNorm, untied head + fused "
+                       "linear cross-entropy softcap 15; 40x1024 tokens)"),
 }
 
 
@@ -65,15 +69,17 @@ def step_flops(w: dict) -> int:
     n = w["batch"] * w["seq"]
     f = 0
     if w["layer"]:
-        f += layer_flops_per_token(w["seq"]) * n
+        f += w.get("layers", 1) * layer_flops_per_token(w["seq"]) * n
     if w["lce"]:
         f += lce_flops(n)
     return f
 
 
-def cpu_baseline(seq: int, ve: bool, with_layer: bool, with_lce: bool) -> dict:
+def cpu_baseline(seq: int, ve: bool, with_layer: bool, with_lce: bool, layers: int = 1) -> dict:
     """The oracle, as it stands, on a bounded sample: one sequence of `seq` tokens through the same
-    step (layer fwd -> loss -> layer bwd) at full model width, float64 numpy on the host."""
+    step (layer fwd -> loss -> layer bwd) at full model width, float64 numpy on the host. With
+    layers > 1 the layer part is timed once and counted `layers` times (the whole model would not
+    finish in minutes on the host)."""
     import synth
     from oracle import lce as olce
     from oracle import model as om
@@ -87,19 +93,27 @@ def cpu_baseline(seq: int, ve: bool, with_layer: bool, with_lce: bool) -> dict:
     if with_lce:
         w_head = synth.normal((V, D), 0.02, 0, synth.K_WHEAD, "bf16")
         tg = synth.uniform_ints((seq,), V_REAL, 0, synth.K_TARGETS)
-    t0 = time.perf_counter()                      # inputs drawn; time the oracle only
     y, dy = inp.x, inp.dy
+    t_layer = t_lce = 0.0
     if with_layer:
+        t0 = time.perf_counter()                  # inputs drawn; time the oracle only
         p, d = om.params_from_inputs(inp), om.dims_from_shape(s)
         y, cache = om.layer_fwd(p, inp.x, inp.ids, d)
+        t_layer += time.perf_counter() - t0
     if with_lce:
+        t0 = time.perf_counter()
         dy = olce.lce_fwd_bwd(y, w_head, tg, softcap=15.0, mode="bf16")["dh"]
+        t_lce = time.perf_counter() - t0
     if with_layer:
+        t0 = time.perf_counter()
         om.layer_bwd(p, cache, dy, d)
-    sec = time.perf_counter() - t0
+        t_layer += time.perf_counter() - t0
+    sec = layers * t_layer + t_lce
+    what = f"1 sequence x {seq} tokens of the same step at full width (float64 numpy)"
+    if layers > 1:
+        what += f"; one layer timed ({t_layer:.1f} s) and counted {layers} times, plus the loss ({t_lce:.1f} s)"
     return {"value": round(seq / sec, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"1 sequence x {seq} tokens of the same step at full width (float64 numpy), "
-                      f"{sec:.1f} s", "seconds": round(sec, 2)}
+            "sample": f"{what}, {sec:.1f} s", "seconds": round(sec, 2)}
 
 
 def main():
@@ -120,7 +134,7 @@ def main():
     import synth
     import transformer_train_step_amd as ll
     from transformer_train_step_amd import _lib as L
-    from transformer_train_step_amd.ops import FusedLCE, Layer, LayerConfig
+    from transformer_train_step_amd.ops import FusedLCE, Layer, LayerConfig, Model
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -136,6 +150,38 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).to(dev)
 
     t_in = time.perf_counter()
+    if args.workload == "model":
+        step, n_launch_trace = model_step(w, dev, torch, synth, LayerConfig, Model)
+    else:
+        step, n_launch_trace = layer_lce_step(w, dev, torch, synth, LayerConfig, Layer, FusedLCE, to_dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t_in:.1f} s to generate)")
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+
+    # timed region: K steps, synchronised on both sides
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
+    report(args, w, ms, step, stream, ev0, ev1, L, n_launch_trace)
+
+
+def layer_lce_step(w, dev, torch, synth, LayerConfig, Layer, FusedLCE, to_dev):
+    """Inputs and the step closure of the layer / loss workloads (inputs drawn by synth)."""
+    B, T = w["batch"], w["seq"]
+    N = B * T
     s = synth.LayerShape(batch=B, seq=T, value_embed=w["ve"])
     inp = synth.layer_inputs(s, seed=0)
     x = to_dev(inp.x)
@@ -163,8 +209,6 @@ def main():
         dh_buf = torch.empty_like(x)
         dw_head = torch.empty_like(w_head)
     del inp
-    torch.cuda.synchronize()
-    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t_in:.1f} s to generate)")
 
     def step():
         h = x
@@ -178,25 +222,50 @@ def main():
         if layer is not None:
             layer.backward(p, x, ids, g, dx=dx, grads=grads)
 
-    for i in range(args.warmup):
-        step()
-        torch.cuda.synchronize()
-        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+    return step, 4096
 
-    # timed region: K steps, synchronised on both sides
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
 
+def model_step(w, dev, torch, synth, LayerConfig, Model):
+    """Inputs and the step closure of the whole model. Its ~3.9B weights are drawn on the GPU with
+    torch's seeded generator (N(0, 0.02), bf16; gains and residual scalars 1); token ids and
+    targets come from synth."""
+    B, T, n_layers = w["batch"], w["seq"], w["layers"]
+    N = B * T
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+
+    def rn(*shape):
+        t = torch.empty(shape, dtype=torch.float32, device=dev)
+        t.normal_(0.0, 0.02, generator=gen)
+        return t.to(torch.bfloat16)
+
+    qkv = (HQ + 2 * HKV) * DH
+    layers = []
+    for i in range(n_layers):
+        lp = {"attn_norm_w": torch.ones(D, device=dev), "mlp_norm_w": torch.ones(D, device=dev),
+              "w_qkv": rn(qkv, D), "w_o": rn(D, HQ * DH), "w_fc": rn(F, D), "w_proj": rn(D, F),
+              "resid_attn": torch.ones(1, device=dev), "resid_mlp": torch.ones(1, device=dev)}
+        if i % 2 == 0:
+            lp["ve_table"] = rn(V, HKV * DH)
+        layers.append(lp)
+    params = {"embed": rn(V, D), "layers": layers, "final_norm_w": torch.ones(D, device=dev), "head": rn(V, D)}
+    model = Model(LayerConfig(batch=B, seq=T), n_layers, V, token_chunk=10240, device=dev)
+    grads = model.new_grads(params)
+    ids = torch.from_numpy(synth.uniform_ints((N,), V_REAL, 0, synth.K_IDS)).to(dev)
+    targets = torch.from_numpy(synth.uniform_ints((N,), V_REAL, 0, synth.K_TARGETS)).to(dev)
+    log(f"[bench] model buffers: saved {model.saved_bytes / 2**30:.1f} GiB, workspace "
+        f"{model.ws_bytes / 2**30:.1f} GiB, device memory in use {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+
+    def step():
+        model(params, ids, targets, grads)
+
+    return step, 16384
+
+
+def report(args, w, ms, step, stream, ev0, ev1, L, n_launch_trace):
+    import torch
+    B, T = w["batch"], w["seq"]
+    N = B * T
     flops = step_flops(w)
     tok_s = N / (ms * 1e-3)
     out = {
@@ -212,15 +281,17 @@ def main():
 
     # traced pass: the same K steps with every launch bracketed by HIP events on its stream
     if not args.no_trace:
-        L.llt_trace_begin(4096)
+        # as many steps as the launch trace holds (the whole model issues ~2,000 launches a step)
+        tsteps = args.steps if n_launch_trace == 4096 else 1
+        L.llt_trace_begin(n_launch_trace)
         torch.cuda.synchronize()
         ev0.record(stream)
-        for _ in range(args.steps):
+        for _ in range(tsteps):
             step()
         ev1.record(stream)
         torch.cuda.synchronize()
         L.llt_trace_end()
-        traced_ms = ev0.elapsed_time(ev1) / args.steps
+        traced_ms = ev0.elapsed_time(ev1) / tsteps
         recs = L.llt_trace_read()
         per = {}
         for tag, t, mnk in recs:
@@ -237,16 +308,16 @@ def main():
         out["roofline"] = {"kernel": dom_tag, "bound": "mfma", "achieved": round(achieved, 1),
                            "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved * 1e12 / peak, 4),
                            "traffic": None, "avg_launch_ms": round(avg_ms, 4),
-                           "flops_per_launch": int(flops_launch), "launches_per_step": dom["launches"] / args.steps}
-        out["kernel_breakdown_ms_per_step"] = {k: round(v["ms"] / args.steps, 3) for k, v in top[:12]}
+                           "flops_per_launch": int(flops_launch), "launches_per_step": dom["launches"] / tsteps}
+        out["kernel_breakdown_ms_per_step"] = {k: round(v["ms"] / tsteps, 3) for k, v in top[:12]}
         out["traced_ms_per_step"] = round(traced_ms, 4)
         log("[bench] per-kernel time per step (ms): " +
-            ", ".join(f"{k} {v['ms'] / args.steps:.2f}" for k, v in top[:12]))
+            ", ".join(f"{k} {v['ms'] / tsteps:.2f}" for k, v in top[:12]))
 
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (bounded sample)...")
         seq = T if w["layer"] else 1024
-        out["cpu_baseline"] = cpu_baseline(seq, w["ve"], w["layer"], w["lce"])
+        out["cpu_baseline"] = cpu_baseline(seq, w["ve"], w["layer"], w["lce"], w.get("layers", 1))
         log(f"[bench] oracle: {out['cpu_baseline']['value']} tokens/s on {out['cpu_baseline']['cores']} threads")
     print(json.dumps(out), flush=True)
 

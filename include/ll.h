@@ -138,6 +138,50 @@ int ll_fused_lce_fwd_bwd(int32_t dtype, const void* hidden, const void* weight,
                          float* lse, void* d_hidden, void* d_weight, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* Parameters of the whole model (read only). */
+typedef struct {
+  const void* embed;               /* [vocab, D] in cfg.dtype: token embedding table */
+  const ll_layer_params* layers;   /* host array [n_layers]; layers[i].ve_table != NULL makes layer i a
+                                      value-embedding layer (table [vocab, Hkv * Dh]) */
+  const float* final_norm_w;       /* fp32 [D]: gain of the final RMSNorm */
+  const void* head;                /* [vocab, D] in cfg.dtype: untied LM head */
+} ll_model_params;
+
+/* Gradients of the whole model. */
+typedef struct {
+  float* embed;                    /* fp32 [vocab, D], ACCUMULATED into (the caller zeroes it) */
+  const ll_layer_grads* layers;    /* host array [n_layers], as for ll_layer_bwd (ve_table non-NULL exactly
+                                      on the value-embedding layers) */
+  float* final_norm_w;             /* fp32 [D], written */
+  void* head;                      /* [vocab, D] in cfg.dtype, written */
+} ll_model_grads;
+
+/* Bytes of the `saved` buffer (activations of every layer) and of the workspace of
+ * ll_model_fwd_bwd; 0 if the arguments are invalid. cfg.has_value_embed and cfg.ve_rows are
+ * ignored (see below). */
+size_t ll_model_saved_bytes(const ll_layer_cfg* cfg, int32_t n_layers, int64_t vocab);
+size_t ll_model_workspace_bytes(const ll_layer_cfg* cfg, int32_t n_layers, int64_t vocab, int64_t token_chunk);
+
+/* Forward and backward of the whole little-lm model on one micro-batch [hn.213312.xyz
+ * translation, 设置 / Setup, parameter table: token embeddings, 28 decoder layers, 14
+ * value-embedding tables on every other layer, untied LM head; youdonthavefriends cost analysis,
+ * "config appendix": loss LigerFusedLinearCrossEntropyLoss(softcap=15.0)]:
+ *   x_0 = embed[token_ids];  x_{i+1} = layer_i(x_i)  (ll_layer_fwd with cfg, and
+ *   has_value_embed = (layers[i].ve_table != NULL), ve_rows = vocab);
+ *   hn = RMSNorm(x_L) final_norm_w  (eps cfg.rms_eps; a final norm before the head is the
+ *   Llama-style reading, its gain fits the parameter table);
+ *   loss, dhn, d_head = ll_fused_lce_fwd_bwd(hn, head, targets, softcap, ignore_index,
+ *   grad_scale, token_chunk);
+ * then the backward chain: final-norm backward, ll_layer_bwd from the last layer to the first,
+ * and d_embed[token_ids[n]] += dL/dx_0[n] in fp32. token_ids must lie in [0, vocab) (the
+ * value-embedding layers index their tables with them unchecked); targets follow
+ * ll_fused_lce_fwd_bwd. token_ids, targets: int32 [cfg.batch * cfg.seq] device arrays; loss:
+ * device fp32 scalar. */
+int ll_model_fwd_bwd(const ll_layer_cfg* cfg, int32_t n_layers, int64_t vocab, const ll_model_params* p,
+                     const int32_t* token_ids, const int32_t* targets, float softcap, int32_t ignore_index,
+                     float grad_scale, int64_t token_chunk, float* loss, const ll_model_grads* g, void* saved,
+                     size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes of ll_fp8_quant_tensorwise (a few bytes for the amax). */
 size_t ll_fp8_quant_workspace_bytes(void);
 

@@ -39,6 +39,27 @@ int llt_gemm(int32_t op_dtype, int32_t a_kmajor, int32_t b_kmajor, const void* A
  * (configurations 1 and 7 select 3 there). */
 int llt_set_gemm_config(int32_t cfg);
 
+/* Token-embedding gather and its gradient [hn.213312.xyz translation, 设置 / Setup: token
+ * embedding table; the same kernels serve the model's embedding]:
+ *   out[i, :] = table[ids[i], :] (zeros for ids outside [0, rows));
+ *   d_table[ids[i], :] += d_out[i, :] in fp32 (ids outside [0, rows) skipped; atomic adds).
+ * dtype: LL_F32 or LL_BF16 for table/out/d_out; d % 8 == 0, d <= 4096. */
+int llt_embedding_gather(int32_t dtype, const void* table, int64_t rows, int32_t d, const int32_t* ids, int64_t n,
+                         void* out, void* stream);
+int llt_embedding_scatter_add(int32_t dtype, const void* d_out, const int32_t* ids, int64_t n, int32_t d,
+                              float* d_table, int64_t rows, void* stream);
+
+/* RMSNorm of x [n, d] with fp32 gain g [hn.213312.xyz translation, 设置 / Setup; rms_norm_eps
+ * 1e-6 in the "config appendix" of the youdonthavefriends cost analysis]:
+ *   rstd = 1 / sqrt(mean(x^2) + eps) (fp32 [n]), y = round(x rstd g);
+ * backward: dx = round(rstd (g dy) - x rstd^3 mean(x g dy)), dg = sum over rows of dy x rstd
+ * (fp32 [d], written). d % 8 == 0, d <= 4096. */
+int llt_rmsnorm_fwd(int32_t dtype, const void* x, const float* g, int64_t n, int32_t d, float eps, void* y,
+                    float* rstd, void* stream);
+size_t llt_rmsnorm_bwd_workspace_bytes(int64_t n, int32_t d);
+int llt_rmsnorm_bwd(int32_t dtype, const void* dy, const void* x, const float* g, const float* rstd, int64_t n,
+                    int32_t d, void* dx, float* dg, void* ws, size_t ws_bytes, void* stream);
+
 /* Launch trace: while tracing is on, every kernel launch of the library is bracketed by two HIP
  * events recorded on the launch's own stream and tagged with the kernel's name (GEMMs as
  * "gemm_<operand type>_<epilogue>"). Up to `capacity` launches are recorded per begin; later ones

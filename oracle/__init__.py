@@ -15,7 +15,9 @@ What it computes, and where the pages state it (citations name the page and the 
   linear [hn.213312.xyz translation, "提升吞吐量 / Increasing throughput"; linlog.top article,
   "吞吐量优化"];
 * the fused linear cross-entropy with tanh logit softcap 15 over the 50304-padded vocabulary
-  [youdonthavefriends cost analysis, "Increasing throughput" and "config appendix"].
+  [youdonthavefriends cost analysis, "Increasing throughput" and "config appendix"];
+* the whole model around the layers — token embedding, final RMSNorm, untied head, and the
+  backward chain through them ([hn.213312.xyz translation, "设置 / Setup", parameter table]).
 
 Everything is evaluated in float64 numpy. In bf16 mode the oracle rounds to bf16 exactly where
 the GPU path stores a bf16 tensor (the rounding contract in ``oracle.model``), and FP8 operands go
@@ -27,4 +29,4 @@ Functions without an independent pin say "parity unpinned" in their docstring:
   * ``model.layer_fwd``/``layer_bwd`` residual-scalar placement — the pages say only
     "learnable per-layer residual scalars" / ``layer_scale: true``.
 """
-from . import numerics, model, lce  # noqa: F401
+from . import numerics, model, lce, full_model  # noqa: F401

@@ -159,3 +159,35 @@ def lce_inputs(n_tokens: int, d: int, vocab: int, real_vocab: int, dtype: str = 
         idx = rng(seed, K_TARGETS + 1).choice(n_tokens, size=n_ignored, replace=False)
         t[idx] = ignore_index
     return LceInputs(h, w, t)
+
+
+@dataclass
+class ModelInputs:
+    shape: LayerShape
+    n_layers: int
+    embed: np.ndarray            # [vocab, D]
+    layers: list                 # [LayerInputs]; layer i carries a value-embedding table iff i is even
+    g_final: np.ndarray          # [D] fp32
+    head: np.ndarray             # [vocab, D]
+    ids: np.ndarray              # int32 [N]
+    targets: np.ndarray          # int32 [N]
+
+
+def model_inputs(s: LayerShape, n_layers: int, seed: int = 0, perturb: bool = False,
+                 w_std: float = 0.02) -> ModelInputs:
+    """Inputs of the whole model: per-layer tensors as in layer_inputs(layer=i) (their x / dy are
+    unused), value-embedding tables on the even layers, the token embedding and untied head drawn
+    N(0, w_std), the final-norm gain 1 (or 1 + N(0, 0.1) with perturb), token ids from layer 0's
+    generator and targets uniform in [0, real_vocab)."""
+    from dataclasses import replace
+    layers = [layer_inputs(replace(s, value_embed=(i % 2 == 0)), seed, layer=i, perturb=perturb, w_std=w_std)
+              for i in range(n_layers)]
+    embed = normal((s.vocab, s.d_model), w_std, seed, K_EMB, s.dtype)
+    head = normal((s.vocab, s.d_model), w_std, seed, K_WHEAD, s.dtype)
+    if perturb:
+        g_final = (1.0 + 0.1 * rng(seed, K_GFINAL).standard_normal(s.d_model)).astype(np.float32)
+    else:
+        g_final = np.ones(s.d_model, np.float32)
+    ids = layers[0].ids
+    targets = uniform_ints((s.tokens,), s.real_vocab, seed, K_TARGETS)
+    return ModelInputs(s, n_layers, embed, layers, g_final, head, ids, targets)

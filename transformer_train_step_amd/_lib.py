@@ -47,6 +47,16 @@ class LayerGrads(ctypes.Structure):
                 ("ve_table", c_void_p), ("resid_attn", c_void_p), ("resid_mlp", c_void_p)]
 
 
+class ModelParams(ctypes.Structure):
+    _fields_ = [("embed", c_void_p), ("layers", ctypes.POINTER(LayerParams)), ("final_norm_w", c_void_p),
+                ("head", c_void_p)]
+
+
+class ModelGrads(ctypes.Structure):
+    _fields_ = [("embed", c_void_p), ("layers", ctypes.POINTER(LayerGrads)), ("final_norm_w", c_void_p),
+                ("head", c_void_p)]
+
+
 _lib = None
 _load_error = None
 
@@ -69,6 +79,21 @@ _SIGS = {
     "ll_fused_lce_fwd_bwd": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, c_int64, c_int32,
                                        c_int64, c_float, c_int32, c_float, c_int64, c_void_p,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "ll_model_saved_bytes": (c_size_t, [ctypes.POINTER(LayerCfg), c_int32, c_int64]),
+    "ll_model_workspace_bytes": (c_size_t, [ctypes.POINTER(LayerCfg), c_int32, c_int64, c_int64]),
+    "ll_model_fwd_bwd": (c_int32, [ctypes.POINTER(LayerCfg), c_int32, c_int64, ctypes.POINTER(ModelParams),
+                                   c_void_p, c_void_p, c_float, c_int32, c_float, c_int64, c_void_p,
+                                   ctypes.POINTER(ModelGrads), c_void_p, c_size_t, c_void_p, c_size_t,
+                                   c_void_p]),
+    "llt_embedding_gather": (c_int32, [c_int32, c_void_p, c_int64, c_int32, c_void_p, c_int64, c_void_p,
+                                       c_void_p]),
+    "llt_embedding_scatter_add": (c_int32, [c_int32, c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_int64,
+                                            c_void_p]),
+    "llt_rmsnorm_fwd": (c_int32, [c_int32, c_void_p, c_void_p, c_int64, c_int32, c_float, c_void_p, c_void_p,
+                                  c_void_p]),
+    "llt_rmsnorm_bwd_workspace_bytes": (c_size_t, [c_int64, c_int32]),
+    "llt_rmsnorm_bwd": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p,
+                                  c_void_p, c_void_p, c_size_t, c_void_p]),
     "llt_gemm": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_int64, c_int32,
                            c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
                            c_size_t, c_void_p]),
@@ -189,6 +214,46 @@ def ll_fused_lce_fwd_bwd(dtype, hidden, weight, targets, n, d, v, softcap, ignor
     return _call("ll_fused_lce_fwd_bwd", dtype, ptr(hidden), ptr(weight), ptr(targets), n, d, v,
                  softcap, ignore_index, grad_scale, token_chunk, ptr(loss), ptr(lse), ptr(d_hidden),
                  ptr(d_weight), ptr(ws), ws_bytes, stream_handle(stream), raise_on_error=raise_on_error)
+
+
+def ll_model_saved_bytes(cfg: LayerCfg, n_layers: int, vocab: int) -> int:
+    return lib().ll_model_saved_bytes(ctypes.byref(cfg), n_layers, vocab)
+
+
+def ll_model_workspace_bytes(cfg: LayerCfg, n_layers: int, vocab: int, token_chunk: int) -> int:
+    return lib().ll_model_workspace_bytes(ctypes.byref(cfg), n_layers, vocab, token_chunk)
+
+
+def ll_model_fwd_bwd(cfg, n_layers, vocab, params: ModelParams, token_ids, targets, softcap, ignore_index,
+                     grad_scale, token_chunk, loss, grads: ModelGrads, saved, saved_bytes, ws, ws_bytes,
+                     stream=None, raise_on_error=True):
+    return _call("ll_model_fwd_bwd", ctypes.byref(cfg), n_layers, vocab, ctypes.byref(params), ptr(token_ids),
+                 ptr(targets), softcap, ignore_index, grad_scale, token_chunk, ptr(loss), ctypes.byref(grads),
+                 ptr(saved), saved_bytes, ptr(ws), ws_bytes, stream_handle(stream), raise_on_error=raise_on_error)
+
+
+def llt_embedding_gather(dtype, table, rows, d, ids, n, out, stream=None, raise_on_error=True):
+    return _call("llt_embedding_gather", dtype, ptr(table), rows, d, ptr(ids), n, ptr(out), stream_handle(stream),
+                 raise_on_error=raise_on_error)
+
+
+def llt_embedding_scatter_add(dtype, d_out, ids, n, d, d_table, rows, stream=None, raise_on_error=True):
+    return _call("llt_embedding_scatter_add", dtype, ptr(d_out), ptr(ids), n, d, ptr(d_table), rows,
+                 stream_handle(stream), raise_on_error=raise_on_error)
+
+
+def llt_rmsnorm_fwd(dtype, x, g, n, d, eps, y, rstd, stream=None, raise_on_error=True):
+    return _call("llt_rmsnorm_fwd", dtype, ptr(x), ptr(g), n, d, eps, ptr(y), ptr(rstd), stream_handle(stream),
+                 raise_on_error=raise_on_error)
+
+
+def llt_rmsnorm_bwd_workspace_bytes(n: int, d: int) -> int:
+    return lib().llt_rmsnorm_bwd_workspace_bytes(n, d)
+
+
+def llt_rmsnorm_bwd(dtype, dy, x, g, rstd, n, d, dx, dg, ws, ws_bytes, stream=None, raise_on_error=True):
+    return _call("llt_rmsnorm_bwd", dtype, ptr(dy), ptr(x), ptr(g), ptr(rstd), n, d, ptr(dx), ptr(dg), ptr(ws),
+                 ws_bytes, stream_handle(stream), raise_on_error=raise_on_error)
 
 
 def llt_gemm(op_dtype, a_kmajor, b_kmajor, A, lda, B, ldb, M, N, K, out_dtype, C, ldc, inv_a=None,

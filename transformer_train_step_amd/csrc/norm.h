@@ -58,7 +58,8 @@ inline hipError_t launch_rmsnorm_fwd(const T* x, const float* g, T* y, float* rs
 }
 
 // RMSNorm backward fused with the residual add (and optionally the next branch scaling):
-//   out  = round(resid + r (g d) - x r^3 mean(x g d))       (d = dL/d(normed), x = norm input)
+//   out  = round(resid + r (g d) - x r^3 mean(x g d))       (d = dL/d(normed), x = norm input;
+//                                                             resid NULL reads as 0)
 //   dg   : per-wave partial sums of d * x * r  -> dg_part[wave_global][D]
 //   if bout: bout = round(a * out) and *dot += sum(out * aux)   (next residual branch)
 // Waves own whole rows; ROWS_PER_WAVE rows each.
@@ -111,7 +112,12 @@ rmsnorm_bwd_kernel(const T* __restrict__ d, const T* __restrict__ x, const float
         Vec8<T>::load(dr + c, dv);
         Vec8<T>::load(xr + c, xv);
         Vec8<float>::load(g + c, gv);
-        Vec8<T>::load(resid + row * D + c, rv);
+        if (resid) {
+          Vec8<T>::load(resid + row * D + c, rv);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) rv[k] = 0.f;
+        }
 #pragma unroll
         for (int k = 0; k < 8; ++k) rv[k] = Elem<T>::rnd(rv[k] + (r * (gv[k] * dv[k]) - xv[k] * r3s));
         Vec8<T>::store(out + row * D + c, rv);

@@ -127,3 +127,54 @@ class FusedLCE:
                                grad_scale, self.chunk, self.loss, lse, d_hidden if grads else None,
                                d_weight if grads else None, self.ws, self.ws_bytes, stream)
         return self.loss, d_hidden, d_weight
+
+
+class Model:
+    """The whole model (embedding, n_layers decoder layers, final RMSNorm, untied head + fused
+    linear cross-entropy) bound to a per-layer configuration: owns the `saved` and workspace
+    buffers of ll_model_fwd_bwd. Layer i is a value-embedding layer iff its parameter dict holds a
+    "ve_table" (in the 3.8B model: the even layers)."""
+
+    def __init__(self, cfg: LayerConfig, n_layers: int, vocab: int, token_chunk: int = 0, device="cuda"):
+        self.cfg, self.n_layers, self.vocab, self.chunk = cfg, n_layers, vocab, token_chunk
+        self.c = cfg.c_struct()
+        self.saved_bytes = L.ll_model_saved_bytes(self.c, n_layers, vocab)
+        self.ws_bytes = L.ll_model_workspace_bytes(self.c, n_layers, vocab, token_chunk)
+        if self.saved_bytes == 0 or self.ws_bytes == 0:
+            raise L.LLError(L.LL_ERR_INVALID_ARG, "ll_model_*_bytes", L.ll_last_error())
+        self.saved = torch.empty(self.saved_bytes, dtype=torch.uint8, device=device)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.loss = torch.empty(1, dtype=torch.float32, device=device)
+        self.device = device
+
+    def layer_shapes(self, value_embed: bool) -> dict:
+        c = LayerConfig(**{**self.cfg.__dict__, "value_embed": value_embed, "ve_rows": self.vocab})
+        return param_shapes(c)
+
+    def new_grads(self, params: dict) -> dict:
+        dt = self.cfg.torch_dtype
+        D = self.cfg.d_model
+        layers = []
+        for lp in params["layers"]:
+            g = {}
+            for k, shp in self.layer_shapes("ve_table" in lp and lp["ve_table"] is not None).items():
+                gdt = torch.float32 if (_is_fp32_param(k) or k == "ve_table") else dt
+                g[k] = (torch.zeros if k == "ve_table" else torch.empty)(shp, dtype=gdt, device=self.device)
+            layers.append(g)
+        return {"embed": torch.zeros((self.vocab, D), dtype=torch.float32, device=self.device),
+                "layers": layers,
+                "final_norm_w": torch.empty(D, dtype=torch.float32, device=self.device),
+                "head": torch.empty((self.vocab, D), dtype=dt, device=self.device)}
+
+    def __call__(self, params: dict, token_ids, targets, grads: dict, softcap=15.0, ignore_index=-100,
+                 grad_scale=1.0, stream=None):
+        lp = (L.LayerParams * self.n_layers)(*[L.LayerParams(**{k: L.ptr(p.get(k)) for k in PARAM_NAMES})
+                                               for p in params["layers"]])
+        lg = (L.LayerGrads * self.n_layers)(*[L.LayerGrads(**{k: L.ptr(g.get(k)) for k in PARAM_NAMES})
+                                              for g in grads["layers"]])
+        mp = L.ModelParams(L.ptr(params["embed"]), lp, L.ptr(params["final_norm_w"]), L.ptr(params["head"]))
+        mg = L.ModelGrads(L.ptr(grads["embed"]), lg, L.ptr(grads["final_norm_w"]), L.ptr(grads["head"]))
+        L.ll_model_fwd_bwd(self.c, self.n_layers, self.vocab, mp, token_ids, targets, softcap, ignore_index,
+                           grad_scale, self.chunk, self.loss, mg, self.saved, self.saved_bytes, self.ws,
+                           self.ws_bytes, stream)
+        return self.loss
