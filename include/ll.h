@@ -128,7 +128,9 @@ size_t ll_fused_lce_workspace_bytes(int32_t dtype, int64_t n, int32_t d, int64_t
  *   dtype: LL_F32 or LL_BF16 for hidden, weight, d_hidden, d_weight.
  *   hidden [n, d], weight [v, d] (all v rows take part in the softmax, padded rows included),
  *   targets int32 [n] in [0, v) or == ignore_index.  token_chunk: rows per chunk (memory of the
- *   per-chunk logits is token_chunk * v * 2 bytes (bf16) of ws); 0 picks 10240.
+ *   per-chunk logits is token_chunk * v * 2 bytes (bf16) of ws); 0 picks 10240. With several
+ *   chunks d_weight is accumulated in an fp32 buffer of ws and rounded once at the end; when one
+ *   chunk holds all n rows the whole contraction is rounded straight into d_weight.
  *   loss: device fp32 scalar (0 if no row is valid).  lse: device fp32 [n] or NULL.
  *   d_hidden [n, d] and d_weight [v, d]: both NULL (forward only) or both non-NULL (overwritten).
  *   Requires d % 64 == 0 (bf16) / d % 32 == 0 (fp32), v % 8 == 0. */

@@ -178,6 +178,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
 // C[m, n] = sum_k A(m, k) B(n, k), A(m, k) = AK ? A[m * lda + k] : A[k * lda + m] (likewise B).
 // WGM x WGN waves; wave tile (BM/WGM) x (BN/WGN) in 16 x 16 MFMA fragments. K advances KB bytes
 // per tile through an NS-stage LDS ring: tile kt + NS - 1 is in flight while tile kt is multiplied.
@@ -195,6 +202,8 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   constexpr int NC = KB / 64;
   constexpr int STAGE = (BM + BN) * KB;
   constexpr int NIW = STAGE / 1024 / NW;                    // load instructions per wave per tile
+  // register-prefetch schedule: one wave per SIMD (4 waves, 128 x 128 each), 64-byte K tiles, 3 stages
+  constexpr bool RP = (NW == 4 && NS == 3 && KB == 64 && BM == 256 && BN == 256);
   // One LDS array per stage: distinct objects let the compiler see that the direct loads into the
   // next stages do not alias the fragment reads of the current one (a single array indexed by
   // stage makes it wait for every load in flight before the first read of each tile).
@@ -266,16 +275,69 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
     }
   };
 
-  if (nk > 0) {
-    issue(0, st0);
-    if constexpr (NS > 2) issue(min(1, nk - 1), st1);
-    if constexpr (NS > 3) issue(min(2, nk - 1), st2);
-  }
-  for (int kb = 0; kb < nk; kb += NS) {
-    step(std::integral_constant<int, 0>{}, kb);
-    if (kb + 1 < nk) step(std::integral_constant<int, 1>{}, kb + 1);
-    if constexpr (NS > 2) if (kb + 2 < nk) step(std::integral_constant<int, 2>{}, kb + 2);
-    if constexpr (NS > 3) if (kb + 3 < nk) step(std::integral_constant<int, 3>{}, kb + 3);
+  if constexpr (!RP) {
+    if (nk > 0) {
+      issue(0, st0);
+      if constexpr (NS > 2) issue(min(1, nk - 1), st1);
+      if constexpr (NS > 3) issue(min(2, nk - 1), st2);
+    }
+    for (int kb = 0; kb < nk; kb += NS) {
+      step(std::integral_constant<int, 0>{}, kb);
+      if (kb + 1 < nk) step(std::integral_constant<int, 1>{}, kb + 1);
+      if constexpr (NS > 2) if (kb + 2 < nk) step(std::integral_constant<int, 2>{}, kb + 2);
+      if constexpr (NS > 3) if (kb + 3 < nk) step(std::integral_constant<int, 3>{}, kb + 3);
+    }
+  } else {
+    // When step kt starts, the fragments of tile kt are in registers (read during step kt - 1)
+    // and tiles kt + 1, kt + 2 are loading. Step kt waits for tile kt + 1, refills the stage of
+    // tile kt (its fragments are already in registers) with tile kt + 3, and reads the fragments
+    // of tile kt + 1 into the other register set between its MFMAs, so the MFMA pipe does not
+    // wait on LDS after the barrier. (Three LDS arrays: the compiler keeps apart the loads and
+    // reads of at most three of them.)
+    u32x4 fa[2][FM][2], fb[2][FN][2];
+    auto stepr = [&](auto si, int kt) {
+      constexpr int S = decltype(si)::value, P = S & 1, Q = P ^ 1;
+      // this wave's loads of tile kt + 1 have landed and its fragment reads of tile kt are done
+      wait_vmcnt_lgkm0<NIW>();
+      asm volatile("s_barrier" ::: "memory");
+      const unsigned char* sn = stage(std::integral_constant<int, (S + 1) % 3>{});
+#pragma unroll
+      for (int i = 0; i < FN; ++i) read_frag<BK, BN, KB>(sn, BM * KB, wn * TN + i * 16, lane, fb[Q][i]);
+#pragma unroll
+      for (int j = 0; j < FM; ++j) read_frag<AK, BM, KB>(sn, 0, wm * TM + j * 16, lane, fa[Q][j]);
+      // the reads go out before this step's loads, so no load of this step is in flight behind them
+      __builtin_amdgcn_sched_barrier(0);
+      issue(min(kt + 3, nk - 1), stage(std::integral_constant<int, S % 3>{}));
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) Mma<ET>::template run<NC>(acc[i][j], fb[P][i], fa[P][j]);
+    };
+    if (nk > 0) {
+      issue(0, st0);
+      issue(min(1, nk - 1), st1);
+      issue(min(2, nk - 1), st2);
+      wait_vmcnt<2 * NIW>();                                // tile 0 has landed
+      asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < FN; ++i) read_frag<BK, BN, KB>(st0, BM * KB, wn * TN + i * 16, lane, fb[0][i]);
+#pragma unroll
+      for (int j = 0; j < FM; ++j) read_frag<AK, BM, KB>(st0, 0, wm * TM + j * 16, lane, fa[0][j]);
+    }
+    int kb = 0;
+    for (; kb + 6 <= nk; kb += 6) {                         // straight-line body: six full steps
+      stepr(std::integral_constant<int, 0>{}, kb);
+      stepr(std::integral_constant<int, 1>{}, kb + 1);
+      stepr(std::integral_constant<int, 2>{}, kb + 2);
+      stepr(std::integral_constant<int, 3>{}, kb + 3);
+      stepr(std::integral_constant<int, 4>{}, kb + 4);
+      stepr(std::integral_constant<int, 5>{}, kb + 5);
+    }
+    if (kb < nk) stepr(std::integral_constant<int, 0>{}, kb);
+    if (kb + 1 < nk) stepr(std::integral_constant<int, 1>{}, kb + 1);
+    if (kb + 2 < nk) stepr(std::integral_constant<int, 2>{}, kb + 2);
+    if (kb + 3 < nk) stepr(std::integral_constant<int, 3>{}, kb + 3);
+    if (kb + 4 < nk) stepr(std::integral_constant<int, 4>{}, kb + 4);
   }
   wait_vmcnt<0>();                                          // drain the repeated tail loads
   __syncthreads();
@@ -522,6 +584,8 @@ inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t
 //   3 = 256 x 256, 8 waves (2 x 4), 128 B, 2   4 = 256 x 256, 8 waves (4 x 2), 128 B, 2
 //   5 = 256 x 256, 8 waves (2 x 4), 64 B, 3    6 = 256 x 256, 8 waves (4 x 2), 64 B, 3
 //   7 = 128 x 128, 4 waves, 64 B, 3
+//   8 = 256 x 256, 4 waves (2 x 2, one per SIMD), 64 B, 3, fragments of the next K tile prefetched
+//       into registers across the barrier
 // e4m3 needs 128-byte K tiles (32 bytes of K per lane per MFMA): 5, 6, 7 fall back to 3, 4, 1.
 // 0 = automatic (gemm_config_override()).
 template <class ET, class Epi>
@@ -531,6 +595,7 @@ inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* 
     if (cfg == 5) cfg = 3;
     if (cfg == 6) cfg = 4;
     if (cfg == 7) cfg = 1;
+    if (cfg == 8) cfg = 4;
   }
   switch (cfg) {
     case 1: return launch_gemm_cfg<ET, 128, 128, 2, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
@@ -542,6 +607,7 @@ inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* 
         if (cfg == 5) return launch_gemm_cfg<ET, 256, 256, 2, 4, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
         if (cfg == 6) return launch_gemm_cfg<ET, 256, 256, 4, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
         if (cfg == 7) return launch_gemm_cfg<ET, 128, 128, 2, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
+        if (cfg == 8) return launch_gemm_cfg<ET, 256, 256, 2, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
       }
       return launch_gemm_cfg<ET, 256, 256, 2, 4, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
   }

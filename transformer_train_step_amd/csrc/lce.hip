@@ -21,7 +21,8 @@ struct LcePlan {
   void* dzt = nullptr;      // fp32 only: dz^T [Vpad, chunk_pad]
   void* ht = nullptr;       // fp32 only: H_c^T [D, chunk_pad]
   void* zrow = nullptr;     // 256 zero bytes (K tails of MN-major operands)
-  float* dw32 = nullptr;    // [V, D]
+  float* dw32 = nullptr;    // [V, D] fp32 accumulator (several chunks, or the fp32 path)
+  bool single = false;      // one chunk holds every token
   float* lse = nullptr;     // [chunk]
   float* loss_acc = nullptr;
   int* nv = nullptr;
@@ -32,6 +33,9 @@ LcePlan plan_lce(void* ws, int es, int64_t n, int d, int64_t v, int64_t token_ch
   LcePlan p;
   p.chunk = token_chunk > 0 ? token_chunk : kDefaultChunk;
   if (p.chunk > n) p.chunk = n > 0 ? n : 1;
+  // one chunk holds every token: the weight gradient is one contraction over all of them and is
+  // rounded straight into d_weight (no fp32 accumulator across chunks)
+  p.single = n > 0 && p.chunk >= n;
   p.chunk_pad = round_up(p.chunk, 64);
   p.vpad = round_up(v, 64);
   p.nparts = (int)cdiv(v, kLceBN);
@@ -48,7 +52,7 @@ LcePlan plan_lce(void* ws, int es, int64_t n, int d, int64_t v, int64_t token_ch
       p.dzt = c.take<char>((size_t)p.vpad * p.chunk_pad * es);
       p.ht = c.take<char>((size_t)d * p.chunk_pad * es);
     }
-    p.dw32 = c.take<float>((size_t)v * d);
+    if (!p.single || es == 4) p.dw32 = c.take<float>((size_t)v * d);
   }
   p.bytes = c.bytes();
   return p;
@@ -101,9 +105,16 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     if constexpr (kMN) {
       // dH_c = dz W: A = dz [rows, Vpad] (K-major), B(n = d, k = v) = W[v, d] (MN-major), K = V
       LL_HIP(launch_gemm(z, p.vpad, W, (int64_t)d, rows, d, (int)v, eh, GemmOps{true, false, p.zrow}, s));
-      // dW += dz^T H_c: A(m = v, k = c) = dz[c, v], B(n = d, k = c) = H_c[c, d], both MN-major, K = rows
-      LL_HIP(launch_gemm(static_cast<const T*>(z), p.vpad, Hc, (int64_t)d, (int)v, d, rows, ew,
-                         GemmOps{false, false, p.zrow}, s));
+      // dW += dz^T H_c: A(m = v, k = c) = dz[c, v], B(n = d, k = c) = H_c[c, d], both MN-major, K = rows;
+      // with one chunk the exact fp32 sum over all tokens is rounded straight into dW
+      if (p.single) {
+        EpiStore<T> ewd{dW, (int64_t)d, Deq{nullptr, nullptr}};
+        LL_HIP(launch_gemm(static_cast<const T*>(z), p.vpad, Hc, (int64_t)d, (int)v, d, rows, ewd,
+                           GemmOps{false, false, p.zrow}, s));
+      } else {
+        LL_HIP(launch_gemm(static_cast<const T*>(z), p.vpad, Hc, (int64_t)d, (int)v, d, rows, ew,
+                           GemmOps{false, false, p.zrow}, s));
+      }
     } else {
       LL_HIP(launch_gemm_nt(z, p.vpad, static_cast<const T*>(p.wt), p.vpad, rows, d, (int)p.vpad, eh, s));
       LL_HIP(transpose2d(Hc, rows, d, (int64_t)d, static_cast<T*>(p.ht), (int64_t)rows_pad, (int64_t)rows_pad, s));
@@ -111,7 +122,7 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
                             (int64_t)rows_pad, (int)v, d, rows_pad, ew, s));
     }
   }
-  if (grads) {
+  if (grads && p.dw32) {
     if (n == 0) LL_HIP(fill_f32(p.dw32, 0.f, v * d, s));     // no chunk ran: dW = 0
     LL_HIP(launch_convert(p.dw32, dW, v * d, s));
   }

@@ -158,20 +158,31 @@ inline hipError_t launch_rmsnorm_bwd(const T* d, const T* x, const float* g, con
   return hipGetLastError();
 }
 
-// out[c] = sum_p part[p][c]
-__global__ void colsum_kernel(const float* __restrict__ part, int64_t P, int D, float* __restrict__ out) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= D) return;
+// out[c] = sum_p part[p][c]. One block of 16 waves per 64 columns: wave w sums rows w, w + 16, ...
+// (coalesced 256-byte rows), then the 16 wave sums are added in a fixed order (deterministic).
+__global__ void __launch_bounds__(1024)
+colsum_kernel(const float* __restrict__ part, int64_t P, int D, float* __restrict__ out) {
+  __shared__ float red[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
   float s = 0.f;
-  for (int64_t p = 0; p < P; ++p) s += part[p * D + c];
-  out[c] = s;
+  if (c < D)
+    for (int64_t p = w; p < P; p += 16) s += part[p * D + c];
+  red[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && c < D) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += red[i][lane];
+    out[c] = t;
+  }
 }
+
 inline hipError_t launch_colsum(const float* part, int64_t P, int D, float* out, hipStream_t s) {
-  LL_LAUNCH("colsum", colsum_kernel, dim3((unsigned)cdiv(D, 256)), dim3(256), 0, s, part, P, D, out);
+  LL_LAUNCH("colsum", colsum_kernel, dim3((unsigned)cdiv(D, 64)), dim3(1024), 0, s, part, P, D, out);
   return hipGetLastError();
 }
 
-// out = round(a * dy); *dot += sum(dy * aux); optional amax of out. (dm = a_mlp dy, da_mlp = sum dy m)
 template <class T>
 __global__ void __launch_bounds__(256)
 scale_dot_kernel(const T* __restrict__ dy, const T* __restrict__ aux, const float* a, T* __restrict__ out,
