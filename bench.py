@@ -35,6 +35,34 @@ D, HQ, HKV, DH, F, V, V_REAL = 3072, 24, 8, 128, 12288, 50304, 50257
 P_MM = D * (HQ + 2 * HKV) * DH + D * HQ * DH + 2 * D * F          # 100,663,296
 
 
+# HBM bytes per launch of a kernel from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by
+# the same counters on a 1 GiB device copy; valid only for the kernel sources they were taken on
+# (sha256 of the listed files, first 16 hex digits), else the roofline reports traffic null.
+TRAFFIC = {
+    "gemm_bf16_lce_logits_kk": {
+        "sources": ("transformer_train_step_amd/csrc/gemm.h", "transformer_train_step_amd/csrc/lce.h",
+                    "transformer_train_step_amd/csrc/common.h"),
+        "sha256_16": "bc40f6860283091f", "read_bytes": 5.538e9, "write_bytes": 1.062e9,
+        "profile": "profiles/gemm_bf16_lce_logits_kk_hbm_bytes_layer_lce_40x1024.md"},
+}
+
+
+def measured_traffic(tag: str):
+    import hashlib
+    t = TRAFFIC.get(tag)
+    if t is None:
+        return None
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        src = b"".join(open(os.path.join(here, f), "rb").read() for f in t["sources"])
+    except OSError:
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != t["sha256_16"]:
+        return None
+    return {"read_bytes": t["read_bytes"], "write_bytes": t["write_bytes"],
+            "bytes": t["read_bytes"] + t["write_bytes"], "profile": t["profile"]}
+
+
 def layer_flops_per_token(seq: int, hq: int = HQ, dh: int = DH, p_mm: int = P_MM) -> int:
     return 6 * p_mm + 6 * hq * dh * (seq + 1)
 
@@ -124,6 +152,9 @@ def main():
     ap.add_argument("--workload", default="layer_lce", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="skip the traced pass (roofline)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the steps, copy a MIB-MiB device buffer once (a plain copy of known size, "
+                         "the reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -149,6 +180,15 @@ def main():
     def to_dev(a, dt=torch.bfloat16):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).to(dev)
 
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {n} bytes done")
+        del src, dst
     t_in = time.perf_counter()
     if args.workload == "model":
         step, n_launch_trace = model_step(w, dev, torch, synth, LayerConfig, Model)
@@ -309,6 +349,10 @@ def report(args, w, ms, step, stream, ev0, ev1, L, n_launch_trace):
                            "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved * 1e12 / peak, 4),
                            "traffic": None, "avg_launch_ms": round(avg_ms, 4),
                            "flops_per_launch": int(flops_launch), "launches_per_step": dom["launches"] / tsteps}
+        tr = measured_traffic(dom_tag)
+        if tr is not None:   # HBM bytes per launch (rocprofv3 counters, copy-calibrated)
+            out["roofline"].update(traffic=tr["bytes"], traffic_read_bytes=tr["read_bytes"],
+                                   traffic_write_bytes=tr["write_bytes"], traffic_profile=tr["profile"])
         out["kernel_breakdown_ms_per_step"] = {k: round(v["ms"] / tsteps, 3) for k, v in top[:12]}
         out["traced_ms_per_step"] = round(traced_ms, 4)
         log("[bench] per-kernel time per step (ms): " +

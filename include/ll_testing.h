@@ -62,7 +62,7 @@ int llt_rmsnorm_bwd(int32_t dtype, const void* dy, const void* x, const float* g
 
 /* Launch trace: while tracing is on, every kernel launch of the library is bracketed by two HIP
  * events recorded on the launch's own stream and tagged with the kernel's name (GEMMs as
- * "gemm_<operand type>_<epilogue>"). Up to `capacity` launches are recorded per begin; later ones
+ * "gemm_<operand type>_<epilogue>_<A layout><B layout>", layout k = K-major, m = MN-major). Up to `capacity` launches are recorded per begin; later ones
  * are not traced. The events are created by llt_trace_begin (the only call here that creates
  * HIP objects) and reused until the capacity changes. Not thread-safe across concurrent
  * begin/get on different threads beyond the internal lock; host-side bookkeeping only.

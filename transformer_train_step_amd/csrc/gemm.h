@@ -537,10 +537,12 @@ template <> struct OpName<float> { static constexpr const char* s = "f32"; };
 template <> struct OpName<bf16> { static constexpr const char* s = "bf16"; };
 template <> struct OpName<fp8> { static constexpr const char* s = "e4m3"; };
 
-// trace tag of a GEMM instantiation: "gemm_<operand type>_<epilogue>"
-template <class ET, class Epi>
+// trace tag of a GEMM instantiation: "gemm_<operand type>_<epilogue>_<layouts>", layouts "k" (K-major)
+// or "m" (MN-major) for A then B
+template <class ET, class Epi, bool AK, bool BK>
 inline const char* gemm_tag() {
-  static const std::string t = std::string("gemm_") + OpName<ET>::s + "_" + Epi::kName;
+  static const std::string t = std::string("gemm_") + OpName<ET>::s + "_" + Epi::kName + "_" + (AK ? "k" : "m") +
+                               (BK ? "k" : "m");
   return t.c_str();
 }
 
@@ -554,26 +556,29 @@ template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, class Epi>
 inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
                                   const Epi& epi, const GemmOps& o, hipStream_t s) {
   const int64_t nb = cdiv(M, BM) * cdiv(N, BN);
-  const char* tag = gemm_tag<ET, Epi>();
   const ET* z = static_cast<const ET*>(o.zrow);
   constexpr int NT = 64 * WGM * WGN;
   if constexpr (sizeof(ET) == 2) {
     if (!o.a_kmajor && !o.b_kmajor) {
+      const char* tag = gemm_tag<ET, Epi, false, false>();
       LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, false, Epi>), dim3((unsigned)nb), dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
     if (!o.a_kmajor) {
+      const char* tag = gemm_tag<ET, Epi, false, true>();
       LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, true, Epi>), dim3((unsigned)nb), dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
     if (!o.b_kmajor) {
+      const char* tag = gemm_tag<ET, Epi, true, false>();
       LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, false, Epi>), dim3((unsigned)nb), dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
   }
+  const char* tag = gemm_tag<ET, Epi, true, true>();
   LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, true, Epi>), dim3((unsigned)nb), dim3(NT), 0, s,
                 A, lda, B, ldb, M, N, K, z, epi);
   return hipGetLastError();
