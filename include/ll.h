@@ -2,7 +2,8 @@
  * ll.h — C ABI of the little-lm training-step hot path on AMD Instinct MI355X (gfx950).
  *
  * One decoder layer of the little-lm 3.8B model, forward and backward, its FP8 e4m3 tensorwise
- * quantiser, and the fused linear cross-entropy LM-head loss. The model is stated on the
+ * quantiser, the fused linear cross-entropy LM-head loss, and the whole model (embedding, layers,
+ * final norm, head) for one micro-batch built from them. The model is stated on the
  * "hn.213312.xyz translation" page (section 设置 / Setup: RMSNorm, RoPE, GQA 24 query / 8 KV
  * heads, relu^2 MLP, QK-norm, logit softcap, per-layer learnable residual scalars, ResFormer-style
  * value embeddings) and on the "youdonthavefriends cost analysis" page (section "config
