@@ -131,7 +131,8 @@ size_t ll_fused_lce_workspace_bytes(int32_t dtype, int64_t n, int32_t d, int64_t
  *   targets int32 [n] in [0, v) or == ignore_index.  token_chunk: rows per chunk (memory of the
  *   per-chunk logits is token_chunk * v * 2 bytes (bf16) of ws); 0 picks 10240. With several
  *   chunks d_weight is accumulated in an fp32 buffer of ws and rounded once at the end; when one
- *   chunk holds all n rows the whole contraction is rounded straight into d_weight.
+ *   chunk holds all n rows the whole contraction is rounded straight into d_weight. With
+ *   gradients, ws also holds one transposed copy of weight ([d, v rounded up to 64]).
  *   loss: device fp32 scalar (0 if no row is valid).  lse: device fp32 [n] or NULL.
  *   d_hidden [n, d] and d_weight [v, d]: both NULL (forward only) or both non-NULL (overwritten).
  *   Requires d % 64 == 0 (bf16) / d % 32 == 0 (fp32), v % 8 == 0. */

@@ -81,7 +81,7 @@ template <> struct Mma<fp8> {
   }
 };
 
-enum EpiKind { kEpiPlain = 0, kEpiAmax = 1, kEpiRowLse = 2 };
+enum EpiKind { kEpiPlain = 0, kEpiAmax = 1, kEpiRowSum = 2 };
 
 constexpr int kGemmThreads = 256;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -394,17 +394,12 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
       } else if constexpr (Epi::kKind == kEpiAmax) {
         if (ok) red_amax = fmaxf(red_amax, epi.seg(m, n, v));
       } else {
-        float mx = -INFINITY, se = 0.f;
-        if (ok) epi.seg(m, n, v, mx, se);
-        // combine the SPR segments of this row (consecutive lanes)
+        float se = 0.f;
+        if (ok) se = epi.seg(m, n, v);
+        // add the SPR segment sums of this row (consecutive lanes)
 #pragma unroll
-        for (int o = 1; o < SPR; o <<= 1) {
-          const float om = __shfl_xor(mx, o, 64), os = __shfl_xor(se, o, 64);
-          const float nm = fmaxf(mx, om);
-          se = (nm == -INFINITY) ? 0.f : se * __expf(mx - nm) + os * __expf(om - nm);
-          mx = nm;
-        }
-        if (sg == 0 && m < M) epi.row(m, bn, mx, se);
+        for (int o = 1; o < SPR; o <<= 1) se += __shfl_xor(se, o, 64);
+        if (sg == 0 && m < M) epi.row(m, bn, se);
       }
     }
     __syncthreads();

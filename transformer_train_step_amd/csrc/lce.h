@@ -2,12 +2,13 @@
 // "Increasing throughput" (the fused loss chunks the LM-head matmul so the (B*T, vocab) logits are
 // never materialised) and "config appendix" (LigerFusedLinearCrossEntropyLoss(softcap=15.0))].
 // Per chunk of C rows:
-//   1. z = H_c W^T on MFMA; the epilogue rounds z to the storage type, stores it, and reduces
-//      c = s tanh(z/s) over each 128-column vocabulary tile to an online (max, sum exp) pair;
-//   2. one wave per row combines the pairs into lse and adds lse - c[target] to the loss;
+//   1. z = H_c W^T on MFMA; the epilogue rounds z to the storage type, stores it, and sums
+//      exp(c), c = s tanh(z/s), over each 256-column vocabulary tile of each row;
+//   2. one wave per row adds the tile sums into lse and adds lse - c[target] to the loss;
 //   3. dz = grad_scale/n_valid (exp(c - lse) - onehot)(1 - (c/s)^2), rounded, stored in place of z;
-//   4. dH_c = dz W and dW += dz^T H_c (fp32 accumulation across chunks); in bf16 both GEMMs read
-//      W, dz and H_c where they are (MN-major operands through LDS transpose reads).
+//   4. dH_c = dz W and dW += dz^T H_c (fp32 accumulation across chunks). In bf16 the dH GEMM reads
+//      W^T, transposed once per call, so both of its operands are K-major; the dW GEMM reads dz
+//      and H_c where they are (MN-major operands through LDS transpose reads).
 #pragma once
 #include "common.h"
 #include "gemm.h"
@@ -24,28 +25,25 @@ __device__ __forceinline__ float softcap_tanh(float z, float s, float inv_s) {
   return copysignf(s * t, z);
 }
 
+// Logits epilogue: z = round(acc) is stored and each row's sum of exp(c) over the block tile's
+// columns goes to part[m][bn]. The softcap bounds |c| by s = 15, so exp(c) <= 3.3e6 and a row's
+// sum over the 50304 columns stays far inside fp32 range: no running maximum is needed and the
+// partial sums of the tiles simply add (the relative rounding of the sum is the same as with a
+// maximum subtracted).
 template <class T> struct EpiLceLogits {
   static constexpr const char* kName = "lce_logits";
-  static constexpr int kKind = kEpiRowLse;
-  T* z; int64_t ldz; float2* part; int nparts; float softcap; float inv_softcap;
-  __device__ __forceinline__ void seg(int m, int n, float (&v)[8], float& mx, float& se) const {
+  static constexpr int kKind = kEpiRowSum;
+  T* z; int64_t ldz; float* part; int nparts; float softcap; float inv_softcap;
+  __device__ __forceinline__ float seg(int m, int n, float (&v)[8]) const {
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = Elem<T>::rnd(v[k]);
     Vec8<T>::store(z + (int64_t)m * ldz + n, v);
-    float c[8];
-    mx = -INFINITY;
+    float se = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      c[k] = softcap_tanh(v[k], softcap, inv_softcap);
-      mx = fmaxf(mx, c[k]);
-    }
-    se = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) se += __expf(c[k] - mx);
+    for (int k = 0; k < 8; ++k) se += __expf(softcap_tanh(v[k], softcap, inv_softcap));
+    return se;
   }
-  __device__ __forceinline__ void row(int m, int bn, float mx, float se) const {
-    part[(int64_t)m * nparts + bn] = make_float2(mx, se);
-  }
+  __device__ __forceinline__ void row(int m, int bn, float se) const { part[(int64_t)m * nparts + bn] = se; }
 };
 
 __global__ void count_valid_kernel(const int32_t* __restrict__ y, int64_t n, int32_t ignore, int* __restrict__ nv) {
@@ -57,23 +55,20 @@ __global__ void count_valid_kernel(const int32_t* __restrict__ y, int64_t n, int
   if ((threadIdx.x & 63) == 0 && c) atomicAdd(nv, c);
 }
 
-// one wave per row of the chunk: lse = M + log(sum_t se_t exp(m_t - M)); loss += lse - c[y]
+// one wave per row of the chunk: lse = log(sum_t S_t) over the tiles' partial sums; loss += lse - c[y]
 template <class T>
 __global__ void __launch_bounds__(256)
-lce_lse_kernel(const float2* __restrict__ part, int nparts, const T* __restrict__ z, int64_t ldz,
+lce_lse_kernel(const float* __restrict__ part, int nparts, const T* __restrict__ z, int64_t ldz,
                const int32_t* __restrict__ y, int rows, int32_t ignore, float softcap, float* __restrict__ lse_out,
                float* __restrict__ lse_chunk, float* __restrict__ loss_acc) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const float2* pr = part + (int64_t)row * nparts;
-  float M = -INFINITY;
-  for (int t = lane; t < nparts; t += 64) M = fmaxf(M, pr[t].x);
-  M = wave_max(M);
+  const float* pr = part + (int64_t)row * nparts;
   float S = 0.f;
-  for (int t = lane; t < nparts; t += 64) S += pr[t].y * __expf(pr[t].x - M);
+  for (int t = lane; t < nparts; t += 64) S += pr[t];
   S = wave_sum(S);
-  const float l = M + __logf(S);
+  const float l = __logf(S);
   if (lane == 0) {
     lse_chunk[row] = l;
     if (lse_out) lse_out[row] = l;

@@ -15,9 +15,9 @@ constexpr int64_t kDefaultChunk = 10240;
 struct LcePlan {
   int64_t chunk, chunk_pad, vpad;
   int nparts;
-  float2* part = nullptr;
+  float* part = nullptr;
   void* z = nullptr;        // [chunk_pad, Vpad]  (z, then dz in place)
-  void* wt = nullptr;       // fp32 only: W^T [D, Vpad]
+  void* wt = nullptr;       // W^T [D, Vpad], zero past V
   void* dzt = nullptr;      // fp32 only: dz^T [Vpad, chunk_pad]
   void* ht = nullptr;       // fp32 only: H_c^T [D, chunk_pad]
   void* zrow = nullptr;     // 256 zero bytes (K tails of MN-major operands)
@@ -44,11 +44,11 @@ LcePlan plan_lce(void* ws, int es, int64_t n, int d, int64_t v, int64_t token_ch
   p.nv = c.take<int>(4);
   p.zrow = c.take<char>(256);
   p.lse = c.take<float>(p.chunk_pad);
-  p.part = c.take<float2>(p.chunk_pad * p.nparts);
+  p.part = c.take<float>(p.chunk_pad * p.nparts);
   p.z = c.take<char>((size_t)p.chunk_pad * p.vpad * es);
   if (grads) {
+    p.wt = c.take<char>((size_t)d * p.vpad * es);   // W^T [D, Vpad] (K-major B of the dH GEMM)
     if (es == 4) {
-      p.wt = c.take<char>((size_t)d * p.vpad * es);
       p.dzt = c.take<char>((size_t)p.vpad * p.chunk_pad * es);
       p.ht = c.take<char>((size_t)d * p.chunk_pad * es);
     }
@@ -72,7 +72,7 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
               y, n, ignore, p.nv);
     LL_HIP(hipGetLastError());
   }
-  if (grads && !kMN) LL_HIP(transpose2d(W, v, d, (int64_t)d, static_cast<T*>(p.wt), p.vpad, p.vpad, s));
+  if (grads) LL_HIP(transpose2d(W, v, d, (int64_t)d, static_cast<T*>(p.wt), p.vpad, p.vpad, s));
   T* z = static_cast<T*>(p.z);
   for (int64_t r0 = 0; r0 < n; r0 += p.chunk) {
     const int rows = (int)std::min<int64_t>(p.chunk, n - r0);
@@ -103,8 +103,8 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     EpiStore<T> eh{dH + r0 * d, (int64_t)d, Deq{nullptr, nullptr}};
     EpiAcc32 ew{p.dw32, (int64_t)d, r0 > 0 ? 1 : 0};
     if constexpr (kMN) {
-      // dH_c = dz W: A = dz [rows, Vpad] (K-major), B(n = d, k = v) = W[v, d] (MN-major), K = V
-      LL_HIP(launch_gemm(z, p.vpad, W, (int64_t)d, rows, d, (int)v, eh, GemmOps{true, false, p.zrow}, s));
+      // dH_c = dz W: A = dz [rows, Vpad] (K-major), B(n = d, k = v) = W^T[d, v] (K-major, zero past V)
+      LL_HIP(launch_gemm(z, p.vpad, static_cast<const T*>(p.wt), p.vpad, rows, d, (int)p.vpad, eh, GemmOps{}, s));
       // dW += dz^T H_c: A(m = v, k = c) = dz[c, v], B(n = d, k = c) = H_c[c, d], both MN-major, K = rows;
       // with one chunk the exact fp32 sum over all tokens is rounded straight into dW
       if (p.single) {
