@@ -120,10 +120,11 @@ qk_post_kernel(const float* __restrict__ dqh, const float* __restrict__ dkh, con
 }
 
 // ------------------------------------------------------------------ Delta = rowsum(dO * O)
+// delta [B, Hq, ldl], ldl >= T
 template <class T, int DH>
 __global__ void __launch_bounds__(256)
-attn_delta_kernel(const T* __restrict__ dO, const T* __restrict__ O, float* __restrict__ delta, int64_t N,
-                  int T_, int Hq) {
+attn_delta_kernel(const T* __restrict__ dO, const T* __restrict__ O, float* __restrict__ delta, int64_t ldl,
+                  int64_t N, int T_, int Hq) {
   constexpr int P = DH / 2;                         // 2 elements per thread
   const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   const int i = (int)(gid % P);
@@ -140,7 +141,7 @@ attn_delta_kernel(const T* __restrict__ dO, const T* __restrict__ O, float* __re
   const int64_t n = ht / Hq;
   const int h = (int)(ht % Hq);
   const int64_t b = n / T_, t = n % T_;
-  delta[(b * Hq + h) * T_ + t] = s;
+  delta[(b * Hq + h) * ldl + t] = s;
 }
 
 // ------------------------------------------------------------------ value-embedding gradient

@@ -6,6 +6,7 @@
 // multiple of 128 and zero-filled.
 #include "api.h"
 #include "attn.h"
+#include "flash.h"
 #include "gemm.h"
 #include "norm.h"
 #include "quant.h"
@@ -69,7 +70,7 @@ size_t carve_saved(void* base, const Dims& d, Saved& s) {
   s.rq = c.take<float>(d.N * d.Hq);
   s.rk = c.take<float>(d.N * d.Hkv);
   s.o = c.take<char>(d.N * d.QD * e);
-  s.lse = c.take<float>(d.N * d.Hq);
+  s.lse = c.take<float>(d.B * d.Hq * d.Tp);     // [B, Hq, Tp] (bf16) / [B, Hq, T] (fp32)
   s.attn_out = c.take<char>(d.N * d.D * e);
   s.h = c.take<char>(d.N * d.D * e);
   s.u = c.take<char>(d.N * d.F * e);
@@ -100,7 +101,7 @@ struct FwdWs {
 size_t carve_fwd(void* base, const Dims& d, FwdWs& w) {
   Carver c(base);
   w.cs = c.take<float2>(d.T * (d.DH / 2) + 1);
-  w.vt = c.take<char>(d.B * d.KVD * d.Tp * d.es);
+  w.vt = d.bf ? nullptr : c.take<char>(d.B * d.KVD * d.Tp * d.es);   // fp32 kernels read V^T
   w.hn = w.r = nullptr;
   w.r8 = nullptr;
   if (d.fp8) {
@@ -133,10 +134,13 @@ size_t carve_bwd(void* base, const Dims& d, BwdWs& w) {
   w.dh = c.take<char>(d.N * d.D * e);
   w.dattn = c.take<char>(d.N * d.D * e);
   w.dout = c.take<char>(d.N * d.QD * e);
-  w.qt = c.take<char>(d.B * d.QD * d.Tp * e);
-  w.kt = c.take<char>(d.B * d.KVD * d.Tp * e);
-  w.dot = c.take<char>(d.B * d.QD * d.Tp * e);
-  w.delta = c.take<float>(d.N * d.Hq);
+  w.qt = w.kt = w.dot = nullptr;
+  if (!d.bf) {   // fp32 kernels read Q^T, K^T, dO^T
+    w.qt = c.take<char>(d.B * d.QD * d.Tp * e);
+    w.kt = c.take<char>(d.B * d.KVD * d.Tp * e);
+    w.dot = c.take<char>(d.B * d.QD * d.Tp * e);
+  }
+  w.delta = c.take<float>(d.B * d.Hq * d.Tp);
   w.dqh = c.take<float>(d.N * d.QD);
   w.dkh = c.take<float>(d.N * d.KVD);
   w.dqkv = c.take<char>(d.N * d.QKVD * e);
@@ -227,11 +231,18 @@ int layer_fwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
     LL_LAUNCH("qk_prep", (qk_prep_kernel<T, DH>), dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, s, CP<T>(sv.qkv),
                        (int64_t)d.QKVD, w.cs, P<T>(sv.qh), P<T>(sv.kh), sv.rq, sv.rk, N, (int)d.T, d.Hq, d.Hkv, d.eps);
     LL_HIP(hipGetLastError());
-    LL_HIP(launch_transpose(CP<T>(sv.qkv) + d.vcol0, d.T, DH, (int64_t)d.QKVD, P<T>(w.vt), d.Tp, d.Tp,
-                            (int)(d.B * d.Hkv), d.Hkv, d.T * d.QKVD, (int64_t)DH, (int64_t)DH * d.Tp, s));
     const int nqb = (int)cdiv(d.T, 128);
-    LL_LAUNCH("attn_fwd", (attn_fwd_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nqb)), dim3(256), 0, s, CP<T>(sv.qh),
-                       CP<T>(sv.kh), CP<T>(w.vt), P<T>(sv.o), sv.lse, (int)d.B, (int)d.T, (int)d.Tp, d.Hq, d.Hkv);
+    if constexpr (std::is_same<T, bf16>::value) {
+      LL_LAUNCH("attn_fwd", (fa_fwd_kernel<true>), dim3((unsigned)(d.B * d.Hq * nqb)), dim3(256), 0, s, CP<T>(sv.qh),
+                CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, P<T>(sv.o), sv.lse, d.Tp, (int)d.B,
+                (int)d.T, d.Hq, d.Hkv);
+    } else {
+      LL_HIP(launch_transpose(CP<T>(sv.qkv) + d.vcol0, d.T, DH, (int64_t)d.QKVD, P<T>(w.vt), d.Tp, d.Tp,
+                              (int)(d.B * d.Hkv), d.Hkv, d.T * d.QKVD, (int64_t)DH, (int64_t)DH * d.Tp, s));
+      LL_LAUNCH("attn_fwd", (attn_fwd_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nqb)), dim3(256), 0, s,
+                CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(w.vt), P<T>(sv.o), sv.lse, (int)d.B, (int)d.T, (int)d.Tp, d.Hq,
+                d.Hkv);
+    }
     LL_HIP(hipGetLastError());
   }
   {
@@ -357,25 +368,38 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   T* dqkv = P<T>(w.dqkv);
   if (N > 0) {
     const int64_t dthreads = N * d.Hq * (DH / 2);
+    const int64_t ldl = d.bf ? d.Tp : d.T;   // row stride of lse and delta
     LL_LAUNCH("attn_delta", (attn_delta_kernel<T, DH>), dim3((unsigned)cdiv(dthreads, 256)), dim3(256), 0, s,
-                       CP<T>(w.dout), CP<T>(sv.o), w.delta, N, (int)d.T, d.Hq);
+                       CP<T>(w.dout), CP<T>(sv.o), w.delta, ldl, N, (int)d.T, d.Hq);
     LL_HIP(hipGetLastError());
-    LL_HIP(launch_transpose(CP<T>(sv.qh), d.T, DH, (int64_t)d.QD, P<T>(w.qt), d.Tp, d.Tp, (int)(d.B * d.Hq), d.Hq,
-                            d.T * d.QD, (int64_t)DH, (int64_t)DH * d.Tp, s));
-    LL_HIP(launch_transpose(CP<T>(sv.kh), d.T, DH, (int64_t)d.KVD, P<T>(w.kt), d.Tp, d.Tp, (int)(d.B * d.Hkv), d.Hkv,
-                            d.T * d.KVD, (int64_t)DH, (int64_t)DH * d.Tp, s));
-    LL_HIP(launch_transpose(CP<T>(w.dout), d.T, DH, (int64_t)d.QD, P<T>(w.dot), d.Tp, d.Tp, (int)(d.B * d.Hq), d.Hq,
-                            d.T * d.QD, (int64_t)DH, (int64_t)DH * d.Tp, s));
-    const int nkb = (int)cdiv(d.T, 64);
-    LL_LAUNCH("attn_bwd_dkdv", (attn_bwd_dkdv_kernel<T, DH>), dim3((unsigned)(d.B * d.Hkv * nkb)), dim3(256), 0, s,
-                       CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout),
-                       CP<T>(w.qt), CP<T>(w.dot), sv.lse, w.delta, w.dkh, dqkv + d.vcol0, (int64_t)d.QKVD,
-                       (int)d.B, (int)d.T, (int)d.Tp, d.Hq, d.Hkv);
-    LL_HIP(hipGetLastError());
-    LL_LAUNCH("attn_bwd_dq", (attn_bwd_dq_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nkb)), dim3(256), 0, s,
-                       CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout),
-                       CP<T>(w.kt), sv.lse, w.delta, w.dqh, (int)d.B, (int)d.T, (int)d.Tp, d.Hq, d.Hkv);
-    LL_HIP(hipGetLastError());
+    if constexpr (std::is_same<T, bf16>::value) {
+      const int nb128 = (int)cdiv(d.T, 128);
+      LL_LAUNCH("attn_bwd_dkdv", fa_dkdv_kernel, dim3((unsigned)(d.B * d.Hkv * nb128)), dim3(256), 0, s,
+                CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), sv.lse,
+                w.delta, ldl, w.dkh, dqkv + d.vcol0, (int64_t)d.QKVD, (int)d.B, (int)d.T, d.Hq, d.Hkv);
+      LL_HIP(hipGetLastError());
+      LL_LAUNCH("attn_bwd_dq", fa_dq_kernel, dim3((unsigned)(d.B * d.Hq * nb128)), dim3(256), 0, s, CP<T>(sv.qh),
+                CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), sv.lse, w.delta, ldl,
+                w.dqh, (int)d.B, (int)d.T, d.Hq, d.Hkv);
+      LL_HIP(hipGetLastError());
+    } else {
+      LL_HIP(launch_transpose(CP<T>(sv.qh), d.T, DH, (int64_t)d.QD, P<T>(w.qt), d.Tp, d.Tp, (int)(d.B * d.Hq), d.Hq,
+                              d.T * d.QD, (int64_t)DH, (int64_t)DH * d.Tp, s));
+      LL_HIP(launch_transpose(CP<T>(sv.kh), d.T, DH, (int64_t)d.KVD, P<T>(w.kt), d.Tp, d.Tp, (int)(d.B * d.Hkv),
+                              d.Hkv, d.T * d.KVD, (int64_t)DH, (int64_t)DH * d.Tp, s));
+      LL_HIP(launch_transpose(CP<T>(w.dout), d.T, DH, (int64_t)d.QD, P<T>(w.dot), d.Tp, d.Tp, (int)(d.B * d.Hq),
+                              d.Hq, d.T * d.QD, (int64_t)DH, (int64_t)DH * d.Tp, s));
+      const int nkb = (int)cdiv(d.T, 64);
+      LL_LAUNCH("attn_bwd_dkdv", (attn_bwd_dkdv_kernel<T, DH>), dim3((unsigned)(d.B * d.Hkv * nkb)), dim3(256), 0, s,
+                CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), CP<T>(w.qt),
+                CP<T>(w.dot), sv.lse, w.delta, w.dkh, dqkv + d.vcol0, (int64_t)d.QKVD, (int)d.B, (int)d.T,
+                (int)d.Tp, d.Hq, d.Hkv);
+      LL_HIP(hipGetLastError());
+      LL_LAUNCH("attn_bwd_dq", (attn_bwd_dq_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nkb)), dim3(256), 0, s,
+                CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), CP<T>(w.kt),
+                sv.lse, w.delta, w.dqh, (int)d.B, (int)d.T, (int)d.Tp, d.Hq, d.Hkv);
+      LL_HIP(hipGetLastError());
+    }
     const int64_t pthreads = N * (d.Hq + d.Hkv) * (DH / 2);
     LL_LAUNCH("qk_post", (qk_post_kernel<T, DH>), dim3((unsigned)cdiv(pthreads, 256)), dim3(256), 0, s, w.dqh, w.dkh,
                        CP<T>(sv.qkv), (int64_t)d.QKVD, w.cs, sv.rq, sv.rk, dqkv, N, (int)d.T, d.Hq, d.Hkv);
