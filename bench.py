@@ -152,6 +152,8 @@ def main():
     ap.add_argument("--workload", default="layer_lce", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="skip the traced pass (roofline)")
+    ap.add_argument("--kernels", action="store_true",
+                    help="print every traced kernel (ms per step, launches, TFLOP/s of its algorithmic work)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, copy a MIB-MiB device buffer once (a plain copy of known size, "
                          "the reference for HBM byte counters)")
@@ -357,6 +359,10 @@ def report(args, w, ms, step, stream, ev0, ev1, L, n_launch_trace):
         out["traced_ms_per_step"] = round(traced_ms, 4)
         log("[bench] per-kernel time per step (ms): " +
             ", ".join(f"{k} {v['ms'] / tsteps:.2f}" for k, v in top[:12]))
+        if args.kernels:
+            for k, v in top:
+                tf = f"{v['flops'] / (v['ms'] * 1e-3) / 1e12:8.1f} TFLOP/s" if v["flops"] and v["ms"] > 0 else ""
+                log(f"[bench]   {k:40s} {v['ms'] / tsteps:8.3f} ms/step {v['launches'] / tsteps:6.1f} launches {tf}")
 
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (bounded sample)...")

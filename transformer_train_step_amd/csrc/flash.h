@@ -25,10 +25,11 @@ namespace {
 constexpr float kFaLog2e = 1.4426950408889634f;
 constexpr float kFaLn2 = 0.6931471805599453f;
 
-// Chunk swizzle of a 256-byte row: 16 consecutive rows read at one logical chunk hit 16 distinct
-// chunk slots, and the 4-row groups of a transpose read (rows 4a..4a+3, two adjacent chunks each)
-// land on 8 distinct chunk pairs, as do two such groups 4 rows apart.
-__device__ __forceinline__ int fa_swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+// Chunk swizzle of a 256-byte row (XOR of chunk bits 1..3 with row bits 0..2, and of chunk bit 1
+// with row bit 3): the 16-row read at one logical chunk and the 4-row transpose reads (two adjacent
+// chunks per row) both run without bank-conflict cycles, as measured with the LDS bank-conflict
+// counter (a row bit 3 on chunk bit 0 costs the 16-row read 4 extra cycles).
+__device__ __forceinline__ int fa_swz(int row) { return ((row & 7) << 1) ^ ((row >> 2) & 2); }
 
 __device__ __forceinline__ floatx4 fa_mma(floatx4 acc, u32x4 first, u32x4 second) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, first),

@@ -232,15 +232,18 @@ int layer_fwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
                        (int64_t)d.QKVD, w.cs, P<T>(sv.qh), P<T>(sv.kh), sv.rq, sv.rk, N, (int)d.T, d.Hq, d.Hkv, d.eps);
     LL_HIP(hipGetLastError());
     const int nqb = (int)cdiv(d.T, 128);
+    // algorithmic work, traced as 2 M N K: causal (query, key) pairs x head_dim x 2 products
+    const int64_t pairs = d.B * d.Hq * d.T * (d.T + 1) / 2;
     if constexpr (std::is_same<T, bf16>::value) {
-      LL_LAUNCH("attn_fwd", (fa_fwd_kernel<true>), dim3((unsigned)(d.B * d.Hq * nqb)), dim3(256), 0, s, CP<T>(sv.qh),
+      LL_LAUNCH_MNK("attn_fwd", pairs, DH, 2, (fa_fwd_kernel<true>), dim3((unsigned)(d.B * d.Hq * nqb)), dim3(256), 0, s,
+                    CP<T>(sv.qh),
                 CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, P<T>(sv.o), sv.lse, d.Tp, (int)d.B,
                 (int)d.T, d.Hq, d.Hkv);
     } else {
       LL_HIP(launch_transpose(CP<T>(sv.qkv) + d.vcol0, d.T, DH, (int64_t)d.QKVD, P<T>(w.vt), d.Tp, d.Tp,
                               (int)(d.B * d.Hkv), d.Hkv, d.T * d.QKVD, (int64_t)DH, (int64_t)DH * d.Tp, s));
-      LL_LAUNCH("attn_fwd", (attn_fwd_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nqb)), dim3(256), 0, s,
-                CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(w.vt), P<T>(sv.o), sv.lse, (int)d.B, (int)d.T, (int)d.Tp, d.Hq,
+      LL_LAUNCH_MNK("attn_fwd", pairs, DH, 2, (attn_fwd_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nqb)), dim3(256),
+                    0, s, CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(w.vt), P<T>(sv.o), sv.lse, (int)d.B, (int)d.T, (int)d.Tp, d.Hq,
                 d.Hkv);
     }
     LL_HIP(hipGetLastError());
@@ -369,16 +372,18 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   if (N > 0) {
     const int64_t dthreads = N * d.Hq * (DH / 2);
     const int64_t ldl = d.bf ? d.Tp : d.T;   // row stride of lse and delta
+    // algorithmic work, traced as 2 M N K: dK/dV holds the dP, dV and dK products, dQ the dQ product
+    const int64_t pairs = d.B * d.Hq * d.T * (d.T + 1) / 2;
     LL_LAUNCH("attn_delta", (attn_delta_kernel<T, DH>), dim3((unsigned)cdiv(dthreads, 256)), dim3(256), 0, s,
                        CP<T>(w.dout), CP<T>(sv.o), w.delta, ldl, N, (int)d.T, d.Hq);
     LL_HIP(hipGetLastError());
     if constexpr (std::is_same<T, bf16>::value) {
       const int nb128 = (int)cdiv(d.T, 128);
-      LL_LAUNCH("attn_bwd_dkdv", fa_dkdv_kernel, dim3((unsigned)(d.B * d.Hkv * nb128)), dim3(256), 0, s,
+      LL_LAUNCH_MNK("attn_bwd_dkdv", pairs, DH, 3, fa_dkdv_kernel, dim3((unsigned)(d.B * d.Hkv * nb128)), dim3(256), 0, s,
                 CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), sv.lse,
                 w.delta, ldl, w.dkh, dqkv + d.vcol0, (int64_t)d.QKVD, (int)d.B, (int)d.T, d.Hq, d.Hkv);
       LL_HIP(hipGetLastError());
-      LL_LAUNCH("attn_bwd_dq", fa_dq_kernel, dim3((unsigned)(d.B * d.Hq * nb128)), dim3(256), 0, s, CP<T>(sv.qh),
+      LL_LAUNCH_MNK("attn_bwd_dq", pairs, DH, 1, fa_dq_kernel, dim3((unsigned)(d.B * d.Hq * nb128)), dim3(256), 0, s, CP<T>(sv.qh),
                 CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), sv.lse, w.delta, ldl,
                 w.dqh, (int)d.B, (int)d.T, d.Hq, d.Hkv);
       LL_HIP(hipGetLastError());
@@ -390,12 +395,12 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
       LL_HIP(launch_transpose(CP<T>(w.dout), d.T, DH, (int64_t)d.QD, P<T>(w.dot), d.Tp, d.Tp, (int)(d.B * d.Hq),
                               d.Hq, d.T * d.QD, (int64_t)DH, (int64_t)DH * d.Tp, s));
       const int nkb = (int)cdiv(d.T, 64);
-      LL_LAUNCH("attn_bwd_dkdv", (attn_bwd_dkdv_kernel<T, DH>), dim3((unsigned)(d.B * d.Hkv * nkb)), dim3(256), 0, s,
+      LL_LAUNCH_MNK("attn_bwd_dkdv", pairs, DH, 3, (attn_bwd_dkdv_kernel<T, DH>), dim3((unsigned)(d.B * d.Hkv * nkb)), dim3(256), 0, s,
                 CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), CP<T>(w.qt),
                 CP<T>(w.dot), sv.lse, w.delta, w.dkh, dqkv + d.vcol0, (int64_t)d.QKVD, (int)d.B, (int)d.T,
                 (int)d.Tp, d.Hq, d.Hkv);
       LL_HIP(hipGetLastError());
-      LL_LAUNCH("attn_bwd_dq", (attn_bwd_dq_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nkb)), dim3(256), 0, s,
+      LL_LAUNCH_MNK("attn_bwd_dq", pairs, DH, 1, (attn_bwd_dq_kernel<T, DH>), dim3((unsigned)(d.B * d.Hq * nkb)), dim3(256), 0, s,
                 CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), CP<T>(w.kt),
                 sv.lse, w.delta, w.dqh, (int)d.B, (int)d.T, (int)d.Tp, d.Hq, d.Hkv);
       LL_HIP(hipGetLastError());
