@@ -38,12 +38,17 @@ P_MM = D * (HQ + 2 * HKV) * DH + D * HQ * DH + 2 * D * F          # 100,663,296
 # HBM bytes per launch of a kernel from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by
 # the same counters on a 1 GiB device copy; valid only for the kernel sources they were taken on
 # (sha256 of the listed files, first 16 hex digits), else the roofline reports traffic null.
+SOURCES = ("transformer_train_step_amd/csrc/gemm.h", "transformer_train_step_amd/csrc/lce.h",
+           "transformer_train_step_amd/csrc/common.h")
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated (valid while the sources
+# hash to sha256_16; otherwise the roofline reports traffic null)
 TRAFFIC = {
-    "gemm_bf16_lce_logits_kk": {
-        "sources": ("transformer_train_step_amd/csrc/gemm.h", "transformer_train_step_amd/csrc/lce.h",
-                    "transformer_train_step_amd/csrc/common.h"),
-        "sha256_16": "bc40f6860283091f", "read_bytes": 5.538e9, "write_bytes": 1.062e9,
-        "profile": "profiles/gemm_bf16_lce_logits_kk_hbm_bytes_layer_lce_40x1024.md"},
+    "gemm_bf16_acc32_mm": {"sources": SOURCES, "sha256_16": "2c1f56e1687f6e3b", "read_bytes": 6.2464e+09,
+                           "write_bytes": 6.1833e+08,
+                           "profile": "profiles/gemm_bf16_acc32_mm_hbm_bytes_layer_lce_40x1024.md"},
+    "gemm_bf16_lce_logits_kk": {"sources": SOURCES, "sha256_16": "2c1f56e1687f6e3b", "read_bytes": 5.4086e+09,
+                                "write_bytes": 1.0548e+09,
+                                "profile": "profiles/gemm_bf16_lce_logits_kk_hbm_bytes_layer_lce_40x1024.md"},
 }
 
 
