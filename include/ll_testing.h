@@ -33,10 +33,13 @@ int llt_gemm(int32_t op_dtype, int32_t a_kmajor, int32_t b_kmajor, const void* A
 /* Process-wide override of the GEMM configuration (for measurements). Block tile, waves, bytes of K
  * per LDS tile row, LDS stages: 1 = 128 x 128, 4 waves, 128 B, 2; 2 = 256 x 256, 4 waves, 128 B, 2;
  * 3 = 256 x 256, 8 waves (2 x 4), 128 B, 2; 4 = 256 x 256, 8 waves (4 x 2), 128 B, 2;
- * 5 = 256 x 256, 8 waves (2 x 4), 64 B, 4; 6 = 256 x 256, 8 waves (4 x 2), 64 B, 4;
- * 7 = 128 x 128, 4 waves, 64 B, 4. e4m3 GEMMs need 128-byte K tiles and run 5, 6, 7 as 3, 4, 1.
- * 0 = automatic choice per GEMM shape. The LCE logits GEMM always uses a 256-wide vocabulary tile
- * (configurations 1 and 7 select 3 there). */
+ * 5 = 256 x 256, 8 waves (2 x 4), 64 B, 3; 6 = 256 x 256, 8 waves (4 x 2), 64 B, 3;
+ * 7 = 128 x 128, 4 waves, 64 B, 3; 8 = 256 x 256, 4 waves (2 x 2), 64 B, 3, next-tile fragments
+ * prefetched into registers; 9 = 256 x 256, 8 waves (4 x 2), 128 B, 2, split-phase K loop (the
+ * fragments of one half of a K tile are read while the MFMAs of the other half run); 10 = the
+ * same with 4 waves (2 x 2). e4m3 GEMMs need 128-byte K tiles and run 5, 6, 7 as 3, 4, 1 and 8, 9,
+ * 10 as 4; fp32 runs 9 and 10 as 4. 0 = automatic choice per GEMM shape. The LCE logits GEMM
+ * always uses a 256-wide vocabulary tile (configurations 1, 7 and 8 select 9 there). */
 int llt_set_gemm_config(int32_t cfg);
 
 /* Token-embedding gather and its gradient [hn.213312.xyz translation, 设置 / Setup: token

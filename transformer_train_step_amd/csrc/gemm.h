@@ -174,6 +174,32 @@ __device__ __forceinline__ void read_frag(const unsigned char* t, int off, int f
   }
 }
 
+// Chunk C (16 bytes of K per lane, elements 8 C .. of the lane's 8 NC) of the same fragment:
+// one MFMA's operand.
+template <bool KMAJ, int ROWS, int KB, int C>
+__device__ __forceinline__ u32x4 read_chunk(const unsigned char* t, int off, int f0, int lane) {
+  constexpr int NC = KB / 64;
+  const int g = lane >> 4;
+  if constexpr (KMAJ) {
+    const int row = f0 + (lane & 15), sw = kmaj_swz<KB>(row);
+    return *reinterpret_cast<const u32x4*>(t + (off + row * KB + ((NC * g + C) ^ sw) * 16));
+  } else {
+    constexpr int RB = ROWS * 2;
+    const int li = lane & 15, r = li >> 2, j = li & 3;
+    const int col = f0 + 4 * j;
+    const int chunk = col >> 3, within = (col & 7) * 2;
+    u32x2 h[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int k = 8 * NC * g + 8 * C + 4 * q + r;
+      const unsigned char* a = t + (off + k * RB + ((chunk ^ mn_swz(k)) * 16) + within);
+      h[q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                            (__attribute__((address_space(3))) shortx4*)(a)));
+    }
+    return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3);
+  }
+}
+
 // s_waitcnt vmcnt(N) only (expcnt and lgkmcnt fields at their no-wait maxima). Issued through the
 // builtin so that the compiler's own wait insertion knows which loads have completed.
 template <int N>
@@ -181,6 +207,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+// s_waitcnt lgkmcnt(0) only
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0)
 template <int N>
@@ -220,7 +249,7 @@ __device__ __forceinline__ void sched_step() {
 // C[m, n] = sum_k A(m, k) B(n, k), A(m, k) = AK ? A[m * lda + k] : A[k * lda + m] (likewise B).
 // WGM x WGN waves; wave tile (BM/WGM) x (BN/WGN) in 16 x 16 MFMA fragments. K advances KB bytes
 // per tile through an NS-stage LDS ring: tile kt + NS - 1 is in flight while tile kt is multiplied.
-template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, bool AK, bool BK, class Epi>
+template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, bool AK, bool BK, class Epi, bool SP = false>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int64_t ldb, int M, int N, int K,
             const ET* __restrict__ zrow, Epi epi) {
@@ -324,7 +353,70 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
     }
   };
 
-  if constexpr (!RP) {
+  if constexpr (SP) {
+    // Split-phase K loop (bf16, 2 stages, 128-byte K tiles): each K tile is two MFMA chunks. The
+    // fragments of a chunk are read while the MFMAs of the other chunk run: chunk 1 of tile kt is
+    // read ahead of the chunk-0 MFMAs of kt, and after the barrier in the middle of step kt chunk
+    // 0 of tile kt + 1 is read ahead of the chunk-1 MFMAs of kt. The barrier also hands the stage
+    // of tile kt (fully read by then) to the loads of tile kt + 2.
+    static_assert(NS == 2 && KB == 128 && sizeof(ET) == 2, "split-phase loop: bf16, 2 stages, 128-byte K tiles");
+    u32x4 fa[2][FM], fb[2][FN];
+    auto rd = [&](const unsigned char* sa, auto ci, auto hi) __attribute__((always_inline)) {
+      constexpr int C = decltype(ci)::value, H = decltype(hi)::value;
+#pragma unroll
+      for (int i = 0; i < FN; ++i) fb[H][i] = read_chunk<BK, BN, KB, C>(sa, BM * KB, wn * TN + i * 16, lane);
+#pragma unroll
+      for (int j = 0; j < FM; ++j) fa[H][j] = read_chunk<AK, BM, KB, C>(sa, 0, wm * TM + j * 16, lane);
+    };
+    auto mm = [&](auto hi) __attribute__((always_inline)) {
+      constexpr int H = decltype(hi)::value;
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fb[H][i]),
+                                                              __builtin_bit_cast(bf16x8_t, fa[H][j]), acc[i][j], 0, 0, 0);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    auto half_step = [&](auto si, int kt) __attribute__((always_inline)) {
+      constexpr int S = decltype(si)::value;
+      unsigned char* sa = stage(std::integral_constant<int, S>{});
+      unsigned char* sn = stage(std::integral_constant<int, S ^ 1>{});
+      // sched_barrier(0) keeps each group where it is written: the reads ahead of the MFMAs they
+      // overlap, the MFMAs ahead of the wait, the loads right after the barrier (the scheduler
+      // would otherwise sink them to the next wait, which then waits for them too).
+      // The chunk-0 fragments were read during the previous half step and have landed; waiting
+      // for them here, before the next reads, keeps the count of LDS reads in flight small enough
+      // (the counter holds 15) for the MFMAs below not to wait for the reads issued next.
+      wait_lgkm0();
+      rd(sa, I1{}, I1{});
+      __builtin_amdgcn_sched_barrier(0);
+      mm(I0{});
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt_lgkm0<0>();              // tile kt + 1 has landed (this wave's part), tile kt is read
+      asm volatile("s_barrier" ::: "memory");
+      issue(min(kt + 2, nk - 1), sa);
+      __builtin_amdgcn_sched_barrier(0);
+      rd(sn, I0{}, I0{});
+      __builtin_amdgcn_sched_barrier(0);
+      mm(I1{});
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (nk > 0) {
+      issue(0, st0);
+      issue(min(1, nk - 1), st1);
+      wait_vmcnt<NIW>();
+      asm volatile("s_barrier" ::: "memory");
+      rd(st0, I0{}, I0{});
+    }
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+      half_step(I0{}, kt);
+      half_step(I1{}, kt + 1);
+    }
+    if (kt < nk) half_step(I0{}, kt);
+  } else if constexpr (!RP) {
     if (nk > 0) {
       issue(0, st0);
       if constexpr (NS > 2) issue(min(1, nk - 1), st1);
@@ -596,7 +688,7 @@ struct GemmOps {
   const void* zrow = nullptr;       // >= 16 zero bytes: K-tail rows of MN-major operands
 };
 
-template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, class Epi>
+template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, bool SP = false, class Epi>
 inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
                                   const Epi& epi, const GemmOps& o, hipStream_t s) {
   const int64_t nb = cdiv(M, BM) * cdiv(N, BN);
@@ -605,25 +697,25 @@ inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t
   if constexpr (sizeof(ET) == 2) {
     if (!o.a_kmajor && !o.b_kmajor) {
       const char* tag = gemm_tag<ET, Epi, false, false>();
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, false, Epi>), dim3((unsigned)nb), dim3(NT),
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, false, Epi, SP>), dim3((unsigned)nb), dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
     if (!o.a_kmajor) {
       const char* tag = gemm_tag<ET, Epi, false, true>();
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, true, Epi>), dim3((unsigned)nb), dim3(NT),
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, true, Epi, SP>), dim3((unsigned)nb), dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
     if (!o.b_kmajor) {
       const char* tag = gemm_tag<ET, Epi, true, false>();
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, false, Epi>), dim3((unsigned)nb), dim3(NT),
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, false, Epi, SP>), dim3((unsigned)nb), dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
   }
   const char* tag = gemm_tag<ET, Epi, true, true>();
-  LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, true, Epi>), dim3((unsigned)nb), dim3(NT), 0, s,
+  LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, true, Epi, SP>), dim3((unsigned)nb), dim3(NT), 0, s,
                 A, lda, B, ldb, M, N, K, z, epi);
   return hipGetLastError();
 }
@@ -635,6 +727,8 @@ inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t
 //   7 = 128 x 128, 4 waves, 64 B, 3
 //   8 = 256 x 256, 4 waves (2 x 2, one per SIMD), 64 B, 3, fragments of the next K tile prefetched
 //       into registers across the barrier
+//   9 = 256 x 256, 8 waves (4 x 2), 128 B, 2, split-phase K loop (bf16; e4m3 falls back to 4)
+//  10 = 256 x 256, 4 waves (2 x 2, one per SIMD), 128 B, 2, split-phase K loop (bf16; e4m3: 4)
 // e4m3 needs 128-byte K tiles (32 bytes of K per lane per MFMA): 5, 6, 7 fall back to 3, 4, 1.
 // 0 = automatic (gemm_config_override()).
 template <class ET, class Epi>
@@ -644,7 +738,7 @@ inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* 
     if (cfg == 5) cfg = 3;
     if (cfg == 6) cfg = 4;
     if (cfg == 7) cfg = 1;
-    if (cfg == 8) cfg = 4;
+    if (cfg == 8 || cfg == 9 || cfg == 10) cfg = 4;
   }
   switch (cfg) {
     case 1: return launch_gemm_cfg<ET, 128, 128, 2, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
@@ -657,6 +751,14 @@ inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* 
         if (cfg == 6) return launch_gemm_cfg<ET, 256, 256, 4, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
         if (cfg == 7) return launch_gemm_cfg<ET, 128, 128, 2, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
         if (cfg == 8) return launch_gemm_cfg<ET, 256, 256, 2, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
+        if (cfg == 9) {
+          if constexpr (sizeof(ET) == 2) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, true>(A, lda, B, ldb, M, N, K, epi, o, s);
+          else return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+        }
+        if (cfg == 10) {
+          if constexpr (sizeof(ET) == 2) return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2, true>(A, lda, B, ldb, M, N, K, epi, o, s);
+          else return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+        }
       }
       return launch_gemm_cfg<ET, 256, 256, 2, 4, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
   }
@@ -676,8 +778,10 @@ inline hipError_t launch_gemm(const ET* A, int64_t lda, const ET* B, int64_t ldb
     const int64_t t256 = cdiv(M, 256) * cdiv(N, 256), t128 = cdiv(M, 128) * cdiv(N, 128);
     const double e256 = (double)t256 / (double)(cdiv(t256, 256) * 256);
     const double e128 = 0.75 * (double)t128 / (double)(cdiv(t128, 256) * 256);
-    // 4 x 2 waves, except 2 x 4 when B is MN-major (measured ~3% faster there)
-    cfg = e256 >= e128 ? (o.b_kmajor ? 4 : 3) : 1;
+    // 4 x 2 waves, except 2 x 4 when B is MN-major (measured ~3% faster there); bf16 with both
+    // operands K-major takes the split-phase K loop (measured 2-5% faster than config 4)
+    const bool kk16 = sizeof(ET) == 2 && o.a_kmajor && o.b_kmajor;
+    cfg = e256 >= e128 ? (kk16 ? 9 : o.b_kmajor ? 4 : 3) : 1;
   }
   return launch_gemm_with(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
 }

@@ -81,7 +81,7 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     {
       // the row-LSE partials assume 256 vocabulary columns per block tile
       const int oc = gemm_config_override();
-      const hipError_t e = launch_gemm_with(oc >= 2 && oc <= 6 ? oc : 4,
+      const hipError_t e = launch_gemm_with((oc >= 2 && oc <= 6) || oc == 9 || oc == 10 ? oc : 9,
                                             Hc, (int64_t)d, W, (int64_t)d, rows, (int)v, d, epi, GemmOps{}, s);
       LL_HIP(e);
     }

@@ -54,7 +54,7 @@ extern "C" int llt_gemm(int32_t op_dtype, int32_t a_kmajor, int32_t b_kmajor, co
 }
 
 extern "C" int llt_set_gemm_config(int32_t cfg) {
-  LL_CHECK(cfg >= 0 && cfg <= 8, LL_ERR_INVALID_ARG, "cfg must be in [0, 8]");
+  LL_CHECK(cfg >= 0 && cfg <= 10, LL_ERR_INVALID_ARG, "cfg must be in [0, 10]");
   set_gemm_config_override(cfg);
   return LL_OK;
 }
