@@ -6,9 +6,9 @@
 //      exp(c), c = s tanh(z/s), over each 256-column vocabulary tile of each row;
 //   2. one wave per row adds the tile sums into lse and adds lse - c[target] to the loss;
 //   3. dz = grad_scale/n_valid (exp(c - lse) - onehot)(1 - (c/s)^2), rounded, stored in place of z;
-//   4. dH_c = dz W and dW += dz^T H_c (fp32 accumulation across chunks). In bf16 the dH GEMM reads
-//      W^T, transposed once per call, so both of its operands are K-major; the dW GEMM reads dz
-//      and H_c where they are (MN-major operands through LDS transpose reads).
+//   4. dH_c = dz W and dW += dz^T H_c (fp32 accumulation across chunks). Both GEMMs take K-major
+//      operands: dH reads W^T, transposed once per call, and dW reads dz^T (written by the dz
+//      kernel beside dz) and H_c^T (transposed per chunk).
 #pragma once
 #include "common.h"
 #include "gemm.h"
@@ -116,40 +116,56 @@ lce_dz_kernel(const T* __restrict__ z, int64_t ldz, const float* __restrict__ ls
   }
 }
 
-// In-place dz over rows [0, rows) x cols [0, Vpad) of z (ld = Vpad, a multiple of 8): each
-// thread turns 8 consecutive logits into 8 gradient values (16-byte loads and stores); columns at
-// or beyond V become 0.
-template <class T>
+// bf16 dz over a 64 (rows) x 64 (vocabulary) tile, in place over z (rows < rows_valid), and its
+// transpose into dzt [Vpad, ldt] (rows_valid <= r < rows_pad and columns >= V give 0): each thread
+// turns two 8-column segments into gradients (16-byte loads and stores) and writes two 8-row
+// segments of the transpose from an LDS tile. Grid (Vpad / 64, rows_pad / 64).
 __global__ void __launch_bounds__(256)
-lce_dz_inplace_kernel(T* __restrict__ z, int64_t ldz, const float* __restrict__ lse, const int32_t* __restrict__ y,
-                      int rows, int V, int32_t ignore, float softcap, float grad_scale, const int* __restrict__ nv) {
+lce_dz_t_kernel(bf16* __restrict__ z, int64_t ldz, const float* __restrict__ lse, const int32_t* __restrict__ y,
+                int rows_valid, int V, int32_t ignore, float softcap, float grad_scale, const int* __restrict__ nv,
+                bf16* __restrict__ dzt, int64_t ldt) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const int n_valid = *nv;
   const float gs = n_valid > 0 ? grad_scale / (float)n_valid : 0.f;
   const float inv_s = 1.f / softcap;
-  const int segs = (int)(ldz / 8);
-  const int64_t total = (int64_t)rows * segs;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int r = (int)(i / segs);
-    const int c0 = (int)(i - (int64_t)r * segs) * 8;
-    T* p = z + (int64_t)r * ldz + c0;
-    const int32_t t = y[r];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int item = threadIdx.x + 256 * k, row = item >> 3, c = c0 + 8 * (item & 7);
+    const int r = r0 + row;
     float v[8];
+    const int32_t t = r < rows_valid ? y[r] : ignore;
+    bf16* p = z + (int64_t)r * ldz + c;
     if (t == ignore) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = 0.f;
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
     } else {
-      Vec8<T>::load(p, v);
+      Vec8<bf16>::load(p, v);
       const float l = lse[r];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int c = c0 + k;
-        const float cv = softcap_tanh(v[k], softcap, inv_s);
+      for (int e = 0; e < 8; ++e) {
+        const float cv = softcap_tanh(v[e], softcap, inv_s);
         const float w = cv * inv_s;
-        const float pr = __expf(cv - l) - (c == t ? 1.f : 0.f);
-        v[k] = c < V ? Elem<T>::rnd(gs * pr * (1.f - w * w)) : 0.f;
+        const float pr = __expf(cv - l) - (c + e == t ? 1.f : 0.f);
+        v[e] = c + e < V ? Elem<bf16>::rnd(gs * pr * (1.f - w * w)) : 0.f;
       }
     }
-    Vec8<T>::store(p, v);
+    if (r < rows_valid) Vec8<bf16>::store(p, v);
+    uint4 u;
+    u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    u.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+    u.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+    *reinterpret_cast<uint4*>(&tile[row][8 * (item & 7)]) = u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int item = threadIdx.x + 256 * k, col = item >> 3, rs = 8 * (item & 7);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[rs + 2 * e][col] | ((uint32_t)tile[rs + 2 * e + 1][col] << 16);
+    *reinterpret_cast<uint4*>(dzt + (int64_t)(c0 + col) * ldt + r0 + rs) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 

@@ -18,8 +18,8 @@ struct LcePlan {
   float* part = nullptr;
   void* z = nullptr;        // [chunk_pad, Vpad]  (z, then dz in place)
   void* wt = nullptr;       // W^T [D, Vpad], zero past V
-  void* dzt = nullptr;      // fp32 only: dz^T [Vpad, chunk_pad]
-  void* ht = nullptr;       // fp32 only: H_c^T [D, chunk_pad]
+  void* dzt = nullptr;      // dz^T [Vpad, chunk_pad]
+  void* ht = nullptr;       // H_c^T [D, chunk_pad]
   void* zrow = nullptr;     // 256 zero bytes (K tails of MN-major operands)
   float* dw32 = nullptr;    // [V, D] fp32 accumulator (several chunks, or the fp32 path)
   bool single = false;      // one chunk holds every token
@@ -47,11 +47,9 @@ LcePlan plan_lce(void* ws, int es, int64_t n, int d, int64_t v, int64_t token_ch
   p.part = c.take<float>(p.chunk_pad * p.nparts);
   p.z = c.take<char>((size_t)p.chunk_pad * p.vpad * es);
   if (grads) {
-    p.wt = c.take<char>((size_t)d * p.vpad * es);   // W^T [D, Vpad] (K-major B of the dH GEMM)
-    if (es == 4) {
-      p.dzt = c.take<char>((size_t)p.vpad * p.chunk_pad * es);
-      p.ht = c.take<char>((size_t)d * p.chunk_pad * es);
-    }
+    p.wt = c.take<char>((size_t)d * p.vpad * es);           // W^T [D, Vpad] (K-major B of the dH GEMM)
+    p.dzt = c.take<char>((size_t)p.vpad * p.chunk_pad * es);  // dz^T and H_c^T: K-major operands
+    p.ht = c.take<char>((size_t)d * p.chunk_pad * es);        // of the dW GEMM
     if (!p.single || es == 4) p.dw32 = c.take<float>((size_t)v * d);
   }
   p.bytes = c.bytes();
@@ -63,7 +61,7 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
             int32_t ignore, float grad_scale, const LcePlan& p, float* loss, float* lse_out, T* dH, T* dW,
             hipStream_t s) {
   const bool grads = dH != nullptr;
-  constexpr bool kMN = std::is_same<T, bf16>::value;   // bf16 reads W, dz and H in place (MN-major)
+  constexpr bool kBf16 = std::is_same<T, bf16>::value;
   LL_HIP(fill_f32(p.loss_acc, 0.f, 4, s));
   LL_HIP(fill_f32(reinterpret_cast<float*>(p.nv), 0.f, 4, s));
   LL_HIP(fill_f32(static_cast<float*>(p.zrow), 0.f, 64, s));
@@ -90,10 +88,10 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     LL_HIP(hipGetLastError());
     if (!grads) continue;
     const int rows_pad = (int)round_up(rows, 64);
-    if constexpr (kMN) {
-      const int64_t work = (int64_t)rows * (p.vpad / 8);
-      LL_LAUNCH("lce_dz", (lce_dz_inplace_kernel<T>), dim3((unsigned)std::min<int64_t>(cdiv(work, 256), 16384)),
-                dim3(256), 0, s, z, p.vpad, p.lse, y + r0, rows, (int)v, ignore, softcap, grad_scale, p.nv);
+    if constexpr (kBf16) {
+      LL_LAUNCH("lce_dz", lce_dz_t_kernel, dim3((unsigned)(p.vpad / 64), (unsigned)(rows_pad / 64)), dim3(256), 0, s,
+                z, p.vpad, p.lse, y + r0, rows, (int)v, ignore, softcap, grad_scale, p.nv,
+                static_cast<T*>(p.dzt), (int64_t)rows_pad);
     } else {
       dim3 g((unsigned)cdiv(p.vpad, 64), (unsigned)cdiv(rows_pad, 64));
       LL_LAUNCH("lce_dz", (lce_dz_kernel<T>), g, dim3(256), 0, s, z, p.vpad, p.lse, y + r0, rows, rows_pad, (int)v,
@@ -102,24 +100,19 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     LL_HIP(hipGetLastError());
     EpiStore<T> eh{dH + r0 * d, (int64_t)d, Deq{nullptr, nullptr}};
     EpiAcc32 ew{p.dw32, (int64_t)d, r0 > 0 ? 1 : 0};
-    if constexpr (kMN) {
-      // dH_c = dz W: A = dz [rows, Vpad] (K-major), B(n = d, k = v) = W^T[d, v] (K-major, zero past V)
-      LL_HIP(launch_gemm(z, p.vpad, static_cast<const T*>(p.wt), p.vpad, rows, d, (int)p.vpad, eh, GemmOps{}, s));
-      // dW += dz^T H_c: A(m = v, k = c) = dz[c, v], B(n = d, k = c) = H_c[c, d], both MN-major, K = rows;
-      // with one chunk the exact fp32 sum over all tokens is rounded straight into dW
-      if (p.single) {
-        EpiStore<T> ewd{dW, (int64_t)d, Deq{nullptr, nullptr}};
-        LL_HIP(launch_gemm(static_cast<const T*>(z), p.vpad, Hc, (int64_t)d, (int)v, d, rows, ewd,
-                           GemmOps{false, false, p.zrow}, s));
-      } else {
-        LL_HIP(launch_gemm(static_cast<const T*>(z), p.vpad, Hc, (int64_t)d, (int)v, d, rows, ew,
-                           GemmOps{false, false, p.zrow}, s));
-      }
+    // dH_c = dz W: A = dz [rows, Vpad] (K-major), B(n = d, k = v) = W^T[d, v] (K-major, zero past V)
+    LL_HIP(launch_gemm(z, p.vpad, static_cast<const T*>(p.wt), p.vpad, rows, d, (int)p.vpad, eh, GemmOps{}, s));
+    // dW += dz^T H_c: A = dz^T [Vpad, rows_pad], B = H_c^T [D, rows_pad], both K-major over the
+    // chunk's tokens (zero past rows); with one chunk (bf16) the exact fp32 sum over all tokens is
+    // rounded straight into dW
+    LL_HIP(transpose2d(Hc, rows, d, (int64_t)d, static_cast<T*>(p.ht), (int64_t)rows_pad, (int64_t)rows_pad, s));
+    const T* dzt = static_cast<const T*>(p.dzt);
+    const T* ht = static_cast<const T*>(p.ht);
+    if (p.single && !p.dw32) {
+      EpiStore<T> ewd{dW, (int64_t)d, Deq{nullptr, nullptr}};
+      LL_HIP(launch_gemm(dzt, (int64_t)rows_pad, ht, (int64_t)rows_pad, (int)v, d, rows_pad, ewd, GemmOps{}, s));
     } else {
-      LL_HIP(launch_gemm_nt(z, p.vpad, static_cast<const T*>(p.wt), p.vpad, rows, d, (int)p.vpad, eh, s));
-      LL_HIP(transpose2d(Hc, rows, d, (int64_t)d, static_cast<T*>(p.ht), (int64_t)rows_pad, (int64_t)rows_pad, s));
-      LL_HIP(launch_gemm_nt(static_cast<const T*>(p.dzt), (int64_t)rows_pad, static_cast<const T*>(p.ht),
-                            (int64_t)rows_pad, (int)v, d, rows_pad, ew, s));
+      LL_HIP(launch_gemm(dzt, (int64_t)rows_pad, ht, (int64_t)rows_pad, (int)v, d, rows_pad, ew, GemmOps{}, s));
     }
   }
   if (grads && p.dw32) {
