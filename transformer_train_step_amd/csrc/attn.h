@@ -234,10 +234,10 @@ template <> struct PMma<bf16> {
     const uint2 a1 = *reinterpret_cast<const uint2*>(u1);
     const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
     uint4 b;
-    b.x = (uint32_t)f2bf(p[0]) | ((uint32_t)f2bf(p[1]) << 16);
-    b.y = (uint32_t)f2bf(p[2]) | ((uint32_t)f2bf(p[3]) << 16);
-    b.z = (uint32_t)f2bf(p[4]) | ((uint32_t)f2bf(p[5]) << 16);
-    b.w = (uint32_t)f2bf(p[6]) | ((uint32_t)f2bf(p[7]) << 16);
+    b.x = f2bf2(p[0], p[1]);
+    b.y = f2bf2(p[2], p[3]);
+    b.z = f2bf2(p[4], p[5]);
+    b.w = f2bf2(p[6], p[7]);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                    acc, 0, 0, 0);
   }
@@ -290,8 +290,8 @@ __device__ __forceinline__ void store4(ET* p, const floatx4& v, float s);
 template <>
 __device__ __forceinline__ void store4<bf16>(bf16* p, const floatx4& v, float s) {
   uint2 w;
-  w.x = (uint32_t)f2bf(v[0] * s) | ((uint32_t)f2bf(v[1] * s) << 16);
-  w.y = (uint32_t)f2bf(v[2] * s) | ((uint32_t)f2bf(v[3] * s) << 16);
+  w.x = f2bf2(v[0] * s, v[1] * s);
+  w.y = f2bf2(v[2] * s, v[3] * s);
   *reinterpret_cast<uint2*>(p) = w;
 }
 template <>

@@ -12,11 +12,13 @@ typedef uint8_t fp8;                   // e4m3fn byte
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// Round a finite fp32 to the nearest bf16, ties to even.
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Round a finite fp32 to the nearest bf16, ties to even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two values rounded to bf16 and packed (first in the low half), one instruction
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 __device__ __forceinline__ float round_bf(float f) { return bf2f(f2bf(f)); }
 
@@ -46,10 +48,10 @@ template <> struct Vec8<bf16> {
   }
   __device__ __forceinline__ static void store(bf16* p, const float (&v)[8]) {
     uint4 r;
-    r.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-    r.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-    r.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-    r.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+    r.x = f2bf2(v[0], v[1]);
+    r.y = f2bf2(v[2], v[3]);
+    r.z = f2bf2(v[4], v[5]);
+    r.w = f2bf2(v[6], v[7]);
     *reinterpret_cast<uint4*>(p) = r;
   }
 };
@@ -74,8 +76,8 @@ template <> struct Vec4<bf16> {
   }
   __device__ __forceinline__ static void store(bf16* p, const float (&v)[4]) {
     uint2 r;
-    r.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-    r.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    r.x = f2bf2(v[0], v[1]);
+    r.y = f2bf2(v[2], v[3]);
     *reinterpret_cast<uint2*>(p) = r;
   }
 };
@@ -118,6 +120,28 @@ __device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
 }
 
 // ------------------------------------------------------------------ reductions
+// Lane movement by DPP (no LDS round trip): CTRL is the dpp_ctrl code (quad_perm 0x00-0xFF,
+// row_mirror 0x140, row_half_mirror 0x141).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// Sum over aligned groups of W consecutive lanes (W = 1, 2, 4, .., 64), in every lane of the group:
+// quad swaps (lane ^ 1, lane ^ 2), then the mirrors within 8 and 16 lanes (the quads, then the
+// halves, already hold their sums), ds_swizzle for lane ^ 16 and one permute for lane ^ 32.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "W is a power of two up to 64");
+  if constexpr (W >= 2) v += dpp_move<0xB1>(v);        // quad_perm [1, 0, 3, 2]
+  if constexpr (W >= 4) v += dpp_move<0x4E>(v);        // quad_perm [2, 3, 0, 1]
+  if constexpr (W >= 8) v += dpp_move<0x141>(v);       // row_half_mirror
+  if constexpr (W >= 16) v += dpp_move<0x140>(v);      // row_mirror
+  if constexpr (W >= 32)                               // bit-mode swizzle: lane ^ 16 within 32
+    v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+  if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
