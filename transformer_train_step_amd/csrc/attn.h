@@ -37,107 +37,142 @@ __global__ void rope_table_kernel(float2* cs, int T, int half, double theta) {
 }
 
 // ------------------------------------------------------------------ QK-norm + RoPE (forward)
-// One thread per rotation pair (i, i + DH/2) of one (token, head); heads 0..Hq-1 are q heads,
-// Hq..Hq+Hkv-1 are k heads. The DH/2 threads of a head are consecutive lanes of one wave.
+// A head vector is handled by DH/16 consecutive lanes, each owning 8 consecutive rotation pairs
+// (i, i + DH/2), i = i0 .. i0 + 7: 16-byte loads and stores, the sum of squares reduced across the
+// head's lanes by DPP. Heads 0..Hq-1 of a token are q heads, Hq..Hq+Hkv-1 k heads.
 template <class T, int DH>
 __global__ void __launch_bounds__(256)
 qk_prep_kernel(const T* __restrict__ qkv, int64_t ldqkv, const float2* __restrict__ cs, T* __restrict__ qh,
                T* __restrict__ kh, float* __restrict__ rq, float* __restrict__ rk, int64_t N, int T_, int Hq,
                int Hkv, float eps) {
-  constexpr int P = DH / 2;
+  constexpr int P = DH / 2, TPH = P / 8;
+  static_assert(P % 8 == 0 && 64 % TPH == 0, "head_dim a multiple of 16, at most 128 per 8 lanes");
   const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   const int H = Hq + Hkv;
-  const int i = (int)(gid % P);
-  const int64_t ht = gid / P;
+  const int i0 = (int)(gid % TPH) * 8;
+  const int64_t ht = gid / TPH;
   const bool valid = ht < N * H;
   const int64_t n = valid ? ht / H : 0;
   const int hh = valid ? (int)(ht % H) : 0;
-  float a = 0.f, b = 0.f;
+  float a[8], b[8];
   if (valid) {
     const T* src = qkv + n * ldqkv + (int64_t)hh * DH;
-    a = Elem<T>::ld(src, i);
-    b = Elem<T>::ld(src, i + P);
-  }
-  float ss = a * a + b * b;
+    Vec8<T>::load(src + i0, a);
+    Vec8<T>::load(src + P + i0, b);
+  } else {
 #pragma unroll
-  for (int o = 1; o < P; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    for (int k = 0; k < 8; ++k) a[k] = b[k] = 0.f;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ss += a[k] * a[k] + b[k] * b[k];
+  ss = group_sum<TPH>(ss);
   const float r = 1.0f / sqrtf(ss / (float)DH + eps);
   if (!valid) return;
   const int t = (int)(n % T_);
-  const float2 c = cs[(int64_t)t * P + i];
-  const float x0 = a * r, x1 = b * r;
-  const float y0 = x0 * c.x - x1 * c.y, y1 = x0 * c.y + x1 * c.x;
-  if (hh < Hq) {
-    T* dst = qh + (n * Hq + hh) * DH;
-    Elem<T>::st(dst, i, y0);
-    Elem<T>::st(dst, i + P, y1);
-    if (i == 0) rq[n * Hq + hh] = r;
-  } else {
-    T* dst = kh + (n * Hkv + (hh - Hq)) * DH;
-    Elem<T>::st(dst, i, y0);
-    Elem<T>::st(dst, i + P, y1);
-    if (i == 0) rk[n * Hkv + (hh - Hq)] = r;
+  const float4* c4 = reinterpret_cast<const float4*>(cs + (int64_t)t * P + i0);
+  float y0[8], y1[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 cc = c4[q];                 // (cos, sin) of pairs i0 + 2q, i0 + 2q + 1
+    const float cv[2] = {cc.x, cc.z}, sv[2] = {cc.y, cc.w};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int k = 2 * q + e;
+      const float x0 = a[k] * r, x1 = b[k] * r;
+      y0[k] = x0 * cv[e] - x1 * sv[e];
+      y1[k] = x0 * sv[e] + x1 * cv[e];
+    }
+  }
+  T* dst = hh < Hq ? qh + (n * Hq + hh) * DH : kh + (n * Hkv + (hh - Hq)) * DH;
+  Vec8<T>::store(dst + i0, y0);
+  Vec8<T>::store(dst + P + i0, y1);
+  if (i0 == 0) {
+    if (hh < Hq) rq[n * Hq + hh] = r;
+    else rk[n * Hkv + (hh - Hq)] = r;
   }
 }
 
 // ------------------------------------------------------------------ backward of QK-norm + RoPE
 // dq = r * dqt - q * r^3 * mean(q * dqt) with dqt = RoPE^T(dq^); written into the q/k columns of
-// dqkv. dqh [N, Hq DH] and dkh [N, Hkv DH] are fp32.
+// dqkv. dqh [N, Hq DH] and dkh [N, Hkv DH] are fp32. Lane layout as in the forward.
 template <class T, int DH>
 __global__ void __launch_bounds__(256)
 qk_post_kernel(const float* __restrict__ dqh, const float* __restrict__ dkh, const T* __restrict__ qkv,
                int64_t ldqkv, const float2* __restrict__ cs, const float* __restrict__ rq,
                const float* __restrict__ rk, T* __restrict__ dqkv, int64_t N, int T_, int Hq, int Hkv) {
-  constexpr int P = DH / 2;
+  constexpr int P = DH / 2, TPH = P / 8;
   const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   const int H = Hq + Hkv;
-  const int i = (int)(gid % P);
-  const int64_t ht = gid / P;
+  const int i0 = (int)(gid % TPH) * 8;
+  const int64_t ht = gid / TPH;
   const bool valid = ht < N * H;
   const int64_t n = valid ? ht / H : 0;
   const int hh = valid ? (int)(ht % H) : 0;
-  float d0 = 0.f, d1 = 0.f, x0 = 0.f, x1 = 0.f, r = 0.f;
-  float2 c = make_float2(1.f, 0.f);
+  float t0[8], t1[8], x0[8], x1[8], r = 0.f;
   if (valid) {
     const float* ds = hh < Hq ? dqh + (n * Hq + hh) * DH : dkh + (n * Hkv + (hh - Hq)) * DH;
-    d0 = ds[i];
-    d1 = ds[i + P];
+    float d0[8], d1[8];
+    Vec8<float>::load(ds + i0, d0);
+    Vec8<float>::load(ds + P + i0, d1);
     const T* xs = qkv + n * ldqkv + (int64_t)hh * DH;
-    x0 = Elem<T>::ld(xs, i);
-    x1 = Elem<T>::ld(xs, i + P);
+    Vec8<T>::load(xs + i0, x0);
+    Vec8<T>::load(xs + P + i0, x1);
     r = hh < Hq ? rq[n * Hq + hh] : rk[n * Hkv + (hh - Hq)];
-    c = cs[(int64_t)(n % T_) * P + i];
-  }
-  const float t0 = d0 * c.x + d1 * c.y, t1 = -d0 * c.y + d1 * c.x;     // rotation by -phi
-  float dot = x0 * t0 + x1 * t1;
+    const float4* c4 = reinterpret_cast<const float4*>(cs + (int64_t)(n % T_) * P + i0);
 #pragma unroll
-  for (int o = 1; o < P; o <<= 1) dot += __shfl_xor(dot, o, 64);
+    for (int q = 0; q < 4; ++q) {
+      const float4 cc = c4[q];
+      const float cv[2] = {cc.x, cc.z}, sv[2] = {cc.y, cc.w};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int k = 2 * q + e;
+        t0[k] = d0[k] * cv[e] + d1[k] * sv[e];            // rotation by -phi
+        t1[k] = -d0[k] * sv[e] + d1[k] * cv[e];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t0[k] = t1[k] = x0[k] = x1[k] = 0.f;
+  }
+  float dot = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) dot += x0[k] * t0[k] + x1[k] * t1[k];
+  dot = group_sum<TPH>(dot);
   if (!valid) return;
   const float k3 = r * r * r * dot / (float)DH;
+  float o0[8], o1[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    o0[k] = r * t0[k] - x0[k] * k3;
+    o1[k] = r * t1[k] - x1[k] * k3;
+  }
   T* dst = dqkv + n * ldqkv + (int64_t)hh * DH;
-  Elem<T>::st(dst, i, r * t0 - x0 * k3);
-  Elem<T>::st(dst, i + P, r * t1 - x1 * k3);
+  Vec8<T>::store(dst + i0, o0);
+  Vec8<T>::store(dst + P + i0, o1);
 }
 
 // ------------------------------------------------------------------ Delta = rowsum(dO * O)
-// delta [B, Hq, ldl], ldl >= T
+// delta [B, Hq, ldl], ldl >= T. DH/8 consecutive lanes per (token, head), 8 elements each.
 template <class T, int DH>
 __global__ void __launch_bounds__(256)
 attn_delta_kernel(const T* __restrict__ dO, const T* __restrict__ O, float* __restrict__ delta, int64_t ldl,
                   int64_t N, int T_, int Hq) {
-  constexpr int P = DH / 2;                         // 2 elements per thread
+  constexpr int TPH = DH / 8;
   const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  const int i = (int)(gid % P);
-  const int64_t ht = gid / P;
+  const int i0 = (int)(gid % TPH) * 8;
+  const int64_t ht = gid / TPH;
   const bool valid = ht < N * Hq;
   float s = 0.f;
   if (valid) {
-    const int64_t off = ht * DH + 2 * i;
-    s = Elem<T>::ld(dO, off) * Elem<T>::ld(O, off) + Elem<T>::ld(dO, off + 1) * Elem<T>::ld(O, off + 1);
-  }
+    float a[8], b[8];
+    Vec8<T>::load(dO + ht * DH + i0, a);
+    Vec8<T>::load(O + ht * DH + i0, b);
 #pragma unroll
-  for (int o = 1; o < P; o <<= 1) s += __shfl_xor(s, o, 64);
-  if (!valid || i != 0) return;
+    for (int k = 0; k < 8; ++k) s += a[k] * b[k];
+  }
+  s = group_sum<TPH>(s);
+  if (!valid || i0 != 0) return;
   const int64_t n = ht / Hq;
   const int h = (int)(ht % Hq);
   const int64_t b = n / T_, t = n % T_;

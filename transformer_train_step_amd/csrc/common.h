@@ -142,6 +142,38 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "W is a power of two up to 64");
+  if constexpr (W >= 2) v = fmaxf(v, dpp_move<0xB1>(v));
+  if constexpr (W >= 4) v = fmaxf(v, dpp_move<0x4E>(v));
+  if constexpr (W >= 8) v = fmaxf(v, dpp_move<0x141>(v));
+  if constexpr (W >= 16) v = fmaxf(v, dpp_move<0x140>(v));
+  if constexpr (W >= 32)
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F)));
+  if constexpr (W >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+// Sum (max) of v over the 4 waves of a 256-thread block, added (maxed, v >= 0) into *addr with one
+// atomic per block instead of one per wave: thousands of atomics on one address serialise.
+// Every thread of the block must call it, at most once per kernel.
+__device__ __forceinline__ void block_atomic_add(float* addr, float v) {
+  __shared__ float red_add[4];
+  v = group_sum<64>(v);
+  if ((threadIdx.x & 63) == 0) red_add[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicAdd(addr, (red_add[0] + red_add[1]) + (red_add[2] + red_add[3]));
+}
+__device__ __forceinline__ void atomic_max_nonneg(float* addr, float v);
+__device__ __forceinline__ void block_atomic_max_nonneg(float* addr, float v) {
+  __shared__ float red_max[4];
+  v = group_max<64>(v);
+  if ((threadIdx.x & 63) == 0) red_max[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) atomic_max_nonneg(addr, fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3])));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

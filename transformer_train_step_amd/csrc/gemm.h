@@ -545,8 +545,17 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
     __syncthreads();
   }
   if constexpr (Epi::kKind == kEpiAmax) {
-    red_amax = wave_max(red_amax);
-    if (lane == 0) atomic_max_nonneg(epi.amax, red_amax);
+    // one atomic per block (one per wave serialises ~60,000 atomics on one address per GEMM)
+    __shared__ float red_w[NW];
+    red_amax = group_max<64>(red_amax);
+    if (lane == 0) red_w[wave] = red_amax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float m = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) m = fmaxf(m, red_w[w]);
+      atomic_max_nonneg(epi.amax, m);
+    }
   }
 }
 

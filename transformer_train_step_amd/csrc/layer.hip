@@ -145,7 +145,7 @@ size_t carve_bwd(void* base, const Dims& d, BwdWs& w) {
   w.dkh = c.take<float>(d.N * d.KVD);
   w.dqkv = c.take<char>(d.N * d.QKVD * e);
   w.dxn = c.take<char>(d.N * d.D * e);
-  w.dgp = c.take<float>(rmsnorm_bwd_partials(d.N) * d.D + 1);
+  w.dgp = c.take<float>(rmsnorm_bwd_partials(d.N) * d.D + colsum_scratch_floats(d.D) + 1);
   w.t0 = w.t1 = nullptr;
   w.dm8 = w.dm8t = w.du8 = w.du8t = nullptr;
   if (!d.bf) {
@@ -227,7 +227,7 @@ int layer_fwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
     LL_HIP(launch_gemm_nt(CP<T>(sv.xn), d.D, CP<T>(p->w_qkv), d.D, (int)N, d.QKVD, d.D, e, s));
   }
   if (N > 0) {
-    const int64_t threads = N * (d.Hq + d.Hkv) * (DH / 2);
+    const int64_t threads = N * (d.Hq + d.Hkv) * (DH / 16);   // 8 rotation pairs per lane
     LL_LAUNCH("qk_prep", (qk_prep_kernel<T, DH>), dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, s, CP<T>(sv.qkv),
                        (int64_t)d.QKVD, w.cs, P<T>(sv.qh), P<T>(sv.kh), sv.rq, sv.rk, N, (int)d.T, d.Hq, d.Hkv, d.eps);
     LL_HIP(hipGetLastError());
@@ -357,7 +357,8 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   // MLP RMSNorm backward + residual, fused with the attention-branch scaling
   LL_HIP(launch_rmsnorm_bwd(CP<T>(w.dhn), CP<T>(sv.h), g2, sv.r2, dy, P<T>(w.dh), w.dgp, N, d.D, p->resid_attn,
                             P<T>(w.dattn), CP<T>(sv.attn_out), g->resid_attn, s));
-  LL_HIP(launch_colsum(w.dgp, rmsnorm_bwd_partials(N), d.D, P<float>(g->mlp_norm_w), s));
+  LL_HIP(launch_colsum(w.dgp, rmsnorm_bwd_partials(N), d.D, P<float>(g->mlp_norm_w),
+                       w.dgp + rmsnorm_bwd_partials(N) * d.D, s));
   // O projection: do = dattn W_o, dW_o = dattn^T o
   {
     EpiStore<T> e{P<T>(w.dout), (int64_t)d.QD, Deq{nullptr, nullptr}};
@@ -370,7 +371,7 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   // attention core
   T* dqkv = P<T>(w.dqkv);
   if (N > 0) {
-    const int64_t dthreads = N * d.Hq * (DH / 2);
+    const int64_t dthreads = N * d.Hq * (DH / 8);   // 8 elements per lane
     const int64_t ldl = d.bf ? d.Tp : d.T;   // row stride of lse and delta
     // algorithmic work, traced as 2 M N K: dK/dV holds the dP, dV and dK products, dQ the dQ product
     const int64_t pairs = d.B * d.Hq * d.T * (d.T + 1) / 2;
@@ -405,7 +406,7 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
                 sv.lse, w.delta, w.dqh, (int)d.B, (int)d.T, (int)d.Tp, d.Hq, d.Hkv);
       LL_HIP(hipGetLastError());
     }
-    const int64_t pthreads = N * (d.Hq + d.Hkv) * (DH / 2);
+    const int64_t pthreads = N * (d.Hq + d.Hkv) * (DH / 16);
     LL_LAUNCH("qk_post", (qk_post_kernel<T, DH>), dim3((unsigned)cdiv(pthreads, 256)), dim3(256), 0, s, w.dqh, w.dkh,
                        CP<T>(sv.qkv), (int64_t)d.QKVD, w.cs, sv.rq, sv.rk, dqkv, N, (int)d.T, d.Hq, d.Hkv);
     LL_HIP(hipGetLastError());
@@ -428,7 +429,8 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   // input RMSNorm backward + residual
   LL_HIP(launch_rmsnorm_bwd(CP<T>(w.dxn), x, g1, sv.r1, CP<T>(w.dh), dx, w.dgp, N, d.D, (const float*)nullptr,
                             (T*)nullptr, (const T*)nullptr, (float*)nullptr, s));
-  LL_HIP(launch_colsum(w.dgp, rmsnorm_bwd_partials(N), d.D, P<float>(g->attn_norm_w), s));
+  LL_HIP(launch_colsum(w.dgp, rmsnorm_bwd_partials(N), d.D, P<float>(g->attn_norm_w),
+                       w.dgp + rmsnorm_bwd_partials(N) * d.D, s));
   return LL_OK;
 }
 

@@ -56,29 +56,36 @@ __global__ void count_valid_kernel(const int32_t* __restrict__ y, int64_t n, int
   if ((threadIdx.x & 63) == 0 && c) atomicAdd(nv, c);
 }
 
-// one wave per row of the chunk: lse = log(sum_t S_t) over the tiles' partial sums; loss += lse - c[y]
+// lse = log(sum_t S_t) over the tiles' partial sums of a row, and the row's loss term lse - c[y].
+// A block of 4 waves takes kLseRows rows (a wave per row at a time); the block's loss terms are
+// added in LDS and reach the loss accumulator with one atomic per block.
+constexpr int kLseRows = 16;
 template <class T>
 __global__ void __launch_bounds__(256)
 lce_lse_kernel(const float* __restrict__ part, int nparts, const T* __restrict__ z, int64_t ldz,
                const int32_t* __restrict__ y, int rows, int32_t ignore, float softcap, float* __restrict__ lse_out,
                float* __restrict__ lse_chunk, float* __restrict__ loss_acc) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const float* pr = part + (int64_t)row * nparts;
-  float S = 0.f;
-  for (int t = lane; t < nparts; t += 64) S += pr[t];
-  S = wave_sum(S);
-  const float l = __logf(S);
-  if (lane == 0) {
-    lse_chunk[row] = l;
-    if (lse_out) lse_out[row] = l;
-    const int32_t t = y[row];
-    if (t != ignore) {
-      const float zt = Elem<T>::ld(z, (int64_t)row * ldz + t);
-      atomicAdd(loss_acc, l - softcap_tanh(zt, softcap, 1.f / softcap));
+  __shared__ float red[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float acc = 0.f;
+  for (int i = wave; i < kLseRows; i += 4) {
+    const int row = blockIdx.x * kLseRows + i;
+    if (row >= rows) break;
+    const float* pr = part + (int64_t)row * nparts;
+    float S = 0.f;
+    for (int t = lane; t < nparts; t += 64) S += pr[t];
+    S = group_sum<64>(S);
+    const float l = __logf(S);
+    if (lane == 0) {
+      lse_chunk[row] = l;
+      if (lse_out) lse_out[row] = l;
+      const int32_t t = y[row];
+      if (t != ignore) acc += l - softcap_tanh(Elem<T>::ld(z, (int64_t)row * ldz + t), softcap, 1.f / softcap);
     }
   }
+  if (lane == 0) red[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicAdd(loss_acc, (red[0] + red[1]) + (red[2] + red[3]));
 }
 
 // dz / dz^T over a 64 (rows) x 64 (vocab) tile; rows >= rows_valid or cols >= V give 0.

@@ -83,7 +83,7 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
                                             Hc, (int64_t)d, W, (int64_t)d, rows, (int)v, d, epi, GemmOps{}, s);
       LL_HIP(e);
     }
-    LL_LAUNCH("lce_lse", (lce_lse_kernel<T>), dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, s, p.part, p.nparts, z,
+    LL_LAUNCH("lce_lse", (lce_lse_kernel<T>), dim3((unsigned)cdiv(rows, kLseRows)), dim3(256), 0, s, p.part, p.nparts, z,
               p.vpad, y + r0, rows, ignore, softcap, lse_out ? lse_out + r0 : nullptr, p.lse, p.loss_acc);
     LL_HIP(hipGetLastError());
     if (!grads) continue;

@@ -87,12 +87,12 @@ int norm_bwd(const void* dy, const void* x, const float* g, const float* rstd, i
   LL_HIP(launch_rmsnorm_bwd(static_cast<const T*>(dy), static_cast<const T*>(x), g, rstd, (const T*)nullptr,
                             static_cast<T*>(dx), dgp, N, D, (const float*)nullptr, (T*)nullptr, (const T*)nullptr,
                             (float*)nullptr, s));
-  LL_HIP(launch_colsum(dgp, rmsnorm_bwd_partials(N), D, dg, s));
+  LL_HIP(launch_colsum(dgp, rmsnorm_bwd_partials(N), D, dg, dgp + rmsnorm_bwd_partials(N) * D, s));
   return LL_OK;
 }
 
 size_t norm_bwd_ws_bytes(int64_t N, int D) {
-  return (size_t)std::max<int64_t>(rmsnorm_bwd_partials(N), 1) * D * sizeof(float);
+  return ((size_t)std::max<int64_t>(rmsnorm_bwd_partials(N), 1) * D + colsum_scratch_floats(D)) * sizeof(float);
 }
 
 int check_norm_shape(int32_t dtype, int64_t n, int32_t d) {

@@ -11,59 +11,93 @@ namespace {
 
 constexpr int kMaxDChunks = 8;   // D <= 8 * 512 = 4096 (one wave covers 512 columns per pass)
 
-// y = round(x * r * g), r = 1 / sqrt(mean(x^2) + eps); one wave per row; optional amax of y.
+// y = round(x * r * g), r = 1 / sqrt(mean(x^2) + eps); one wave per row, kNormFwdRows rows per
+// block; optional amax of y. The row is loaded once into registers (every 16-byte load of the row
+// issued before the first use).
+constexpr int kNormFwdRows = 16;
 template <class T>
 __global__ void __launch_bounds__(256)
 rmsnorm_fwd_kernel(const T* __restrict__ x, const float* __restrict__ g, T* __restrict__ y,
                    float* __restrict__ rstd, int64_t N, int D, float eps, float* amax) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   float mx = 0.f;
-  if (row < N) {
+  for (int i = threadIdx.x >> 6; i < kNormFwdRows; i += 4) {
+    const int64_t row = (int64_t)blockIdx.x * kNormFwdRows + i;
+    if (row >= N) break;
     const T* xr = x + row * D;
-    float ss = 0.f;
-    for (int c = lane * 8; c < D; c += 512) {
-      float v[8];
-      Vec8<T>::load(xr + c, v);
+    float v[kMaxDChunks][8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) ss += v[k] * v[k];
+    for (int j = 0; j < kMaxDChunks; ++j) {
+      const int c = lane * 8 + j * 512;
+      if (c < D) Vec8<T>::load(xr + c, v[j]);
     }
-    ss = wave_sum(ss);
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxDChunks; ++j)
+      if (lane * 8 + j * 512 < D)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ss += v[j][k] * v[j][k];
+    ss = group_sum<64>(ss);
     const float r = 1.0f / sqrtf(ss / (float)D + eps);
     if (lane == 0) rstd[row] = r;
-    for (int c = lane * 8; c < D; c += 512) {
-      float v[8], gv[8];
-      Vec8<T>::load(xr + c, v);
-      Vec8<float>::load(g + c, gv);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        v[k] = Elem<T>::rnd(v[k] * r * gv[k]);
-        mx = fmaxf(mx, fabsf(v[k]));
+    for (int j = 0; j < kMaxDChunks; ++j) {
+      const int c = lane * 8 + j * 512;
+      if (c < D) {
+        float gv[8];
+        Vec8<float>::load(g + c, gv);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          v[j][k] = Elem<T>::rnd(v[j][k] * r * gv[k]);
+          mx = fmaxf(mx, fabsf(v[j][k]));
+        }
+        Vec8<T>::store(y + row * D + c, v[j]);
       }
-      Vec8<T>::store(y + row * D + c, v);
     }
   }
-  if (amax) {
-    mx = wave_max(mx);
-    if (lane == 0) atomic_max_nonneg(amax, mx);
-  }
+  if (amax) block_atomic_max_nonneg(amax, mx);
 }
 
 template <class T>
 inline hipError_t launch_rmsnorm_fwd(const T* x, const float* g, T* y, float* rstd, int64_t N, int D,
                                      float eps, float* amax, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  LL_LAUNCH("rmsnorm_fwd", (rmsnorm_fwd_kernel<T>), dim3((unsigned)cdiv(N, 4)), dim3(256), 0, s, x, g, y, rstd, N, D, eps, amax);
+  LL_LAUNCH("rmsnorm_fwd", (rmsnorm_fwd_kernel<T>), dim3((unsigned)cdiv(N, kNormFwdRows)), dim3(256), 0, s, x, g, y,
+            rstd, N, D, eps, amax);
   return hipGetLastError();
 }
+
+// 8 consecutive elements kept in their storage format (16 bytes of bf16 or 32 of fp32).
+template <class T> struct Seg8;
+template <> struct Seg8<bf16> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float operator[](int k) const {
+    const uint32_t w = k < 2 ? u.x : k < 4 ? u.y : k < 6 ? u.z : u.w;
+    return (k & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  }
+};
+template <> struct Seg8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ float operator[](int k) const {
+    const float4& h = k < 4 ? a : b;
+    const int q = k & 3;
+    return q == 0 ? h.x : q == 1 ? h.y : q == 2 ? h.z : h.w;
+  }
+};
 
 // RMSNorm backward fused with the residual add (and optionally the next branch scaling):
 //   out  = round(resid + r (g d) - x r^3 mean(x g d))       (d = dL/d(normed), x = norm input;
 //                                                             resid NULL reads as 0)
 //   dg   : per-wave partial sums of d * x * r  -> dg_part[wave_global][D]
 //   if bout: bout = round(a * out) and *dot += sum(out * aux)   (next residual branch)
-// Waves own whole rows; ROWS_PER_WAVE rows each.
-constexpr int kNormBwdRowsPerWave = 16;
+// Waves own whole rows, kNormBwdRowsPerWave each; a row's d, x and resid are loaded once, all
+// loads of the row issued together, and kept in their storage format.
+constexpr int kNormBwdRowsPerWave = 4;
 
 template <class T>
 __global__ void __launch_bounds__(256)
@@ -84,42 +118,41 @@ rmsnorm_bwd_kernel(const T* __restrict__ d, const T* __restrict__ x, const float
     const int64_t row = wg * kNormBwdRowsPerWave + i;
     if (row >= N) break;
     const float r = rstd[row];
-    const T* dr = d + row * D;
-    const T* xr = x + row * D;
+    Seg8<T> ds[kMaxDChunks], xs[kMaxDChunks], rs[kMaxDChunks];
+#pragma unroll
+    for (int j = 0; j < kMaxDChunks; ++j) {
+      const int c = lane * 8 + j * 512;
+      if (c < D) {
+        ds[j].load(d + row * D + c);
+        xs[j].load(x + row * D + c);
+        if (resid) rs[j].load(resid + row * D + c);
+      }
+    }
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxDChunks; ++j) {
       const int c = lane * 8 + j * 512;
       if (c < D) {
-        float dv[8], xv[8], gv[8];
-        Vec8<T>::load(dr + c, dv);
-        Vec8<T>::load(xr + c, xv);
+        float gv[8];
         Vec8<float>::load(g + c, gv);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          s += xv[k] * gv[k] * dv[k];
-          dga[j][k] += dv[k] * xv[k] * r;
+          s += xs[j][k] * gv[k] * ds[j][k];
+          dga[j][k] += ds[j][k] * xs[j][k] * r;
         }
       }
     }
-    s = wave_sum(s) / (float)D;
+    s = group_sum<64>(s) / (float)D;
     const float r3s = r * r * r * s;
 #pragma unroll
     for (int j = 0; j < kMaxDChunks; ++j) {
       const int c = lane * 8 + j * 512;
       if (c < D) {
-        float dv[8], xv[8], gv[8], rv[8];
-        Vec8<T>::load(dr + c, dv);
-        Vec8<T>::load(xr + c, xv);
+        float gv[8], rv[8];
         Vec8<float>::load(g + c, gv);
-        if (resid) {
-          Vec8<T>::load(resid + row * D + c, rv);
-        } else {
 #pragma unroll
-          for (int k = 0; k < 8; ++k) rv[k] = 0.f;
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) rv[k] = Elem<T>::rnd(rv[k] + (r * (gv[k] * dv[k]) - xv[k] * r3s));
+        for (int k = 0; k < 8; ++k)
+          rv[k] = Elem<T>::rnd((resid ? rs[j][k] : 0.f) + (r * (gv[k] * ds[j][k]) - xs[j][k] * r3s));
         Vec8<T>::store(out + row * D + c, rv);
         if (bout) {
           float ax[8], bv[8];
@@ -139,10 +172,7 @@ rmsnorm_bwd_kernel(const T* __restrict__ d, const T* __restrict__ x, const float
     const int c = lane * 8 + j * 512;
     if (c < D) Vec8<float>::store(dg_part + wg * D + c, dga[j]);
   }
-  if (bout) {
-    dsum = wave_sum(dsum);
-    if (lane == 0) atomicAdd(dot, dsum);
-  }
+  if (bout) block_atomic_add(dot, dsum);
 }
 
 inline int64_t rmsnorm_bwd_partials(int64_t N) { return cdiv(cdiv(N, kNormBwdRowsPerWave), 4) * 4; }
@@ -158,28 +188,37 @@ inline hipError_t launch_rmsnorm_bwd(const T* d, const T* x, const float* g, con
   return hipGetLastError();
 }
 
-// out[c] = sum_p part[p][c]. One block of 16 waves per 64 columns: wave w sums rows w, w + 16, ...
-// (coalesced 256-byte rows), then the 16 wave sums are added in a fixed order (deterministic).
+// out[c] = sum_p part[p][c], in two fixed-order levels: block (x, y) of 16 waves sums the rows
+// p = y, y + S, y + 2S, .. of 64 columns (wave w takes every 16th of them, coalesced 256-byte rows)
+// into mid[y][c]; then one block per 64 columns adds the S rows of mid in order. Deterministic.
+constexpr int kColsumSlabs = 32;
 __global__ void __launch_bounds__(1024)
-colsum_kernel(const float* __restrict__ part, int64_t P, int D, float* __restrict__ out) {
+colsum_kernel(const float* __restrict__ part, int64_t P, int64_t stride, int D, float* __restrict__ out) {
   __shared__ float red[16][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + lane;
   float s = 0.f;
   if (c < D)
-    for (int64_t p = w; p < P; p += 16) s += part[p * D + c];
+    for (int64_t p = blockIdx.y + (int64_t)w * stride; p < P; p += 16 * stride) s += part[p * D + c];
   red[w][lane] = s;
   __syncthreads();
   if (w == 0 && c < D) {
     float t = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) t += red[i][lane];
-    out[c] = t;
+    out[(int64_t)blockIdx.y * D + c] = t;
   }
 }
 
-inline hipError_t launch_colsum(const float* part, int64_t P, int D, float* out, hipStream_t s) {
-  LL_LAUNCH("colsum", colsum_kernel, dim3((unsigned)cdiv(D, 64)), dim3(1024), 0, s, part, P, D, out);
+// scratch: kColsumSlabs * D floats
+inline size_t colsum_scratch_floats(int D) { return (size_t)kColsumSlabs * D; }
+inline hipError_t launch_colsum(const float* part, int64_t P, int D, float* out, float* scratch, hipStream_t s) {
+  LL_LAUNCH("colsum", colsum_kernel, dim3((unsigned)cdiv(D, 64), kColsumSlabs), dim3(1024), 0, s, part, P,
+            (int64_t)kColsumSlabs, D, scratch);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  LL_LAUNCH("colsum", colsum_kernel, dim3((unsigned)cdiv(D, 64), 1), dim3(1024), 0, s, (const float*)scratch,
+            (int64_t)kColsumSlabs, (int64_t)1, D, out);
   return hipGetLastError();
 }
 
@@ -201,12 +240,8 @@ scale_dot_kernel(const T* __restrict__ dy, const T* __restrict__ aux, const floa
     }
     Vec8<T>::store(out + i * 8, dv);
   }
-  ds = wave_sum(ds);
-  mx = wave_max(mx);
-  if ((threadIdx.x & 63) == 0) {
-    atomicAdd(dot, ds);
-    if (amax) atomic_max_nonneg(amax, mx);
-  }
+  block_atomic_add(dot, ds);
+  if (amax) block_atomic_max_nonneg(amax, mx);
 }
 template <class T>
 inline hipError_t launch_scale_dot(const T* dy, const T* aux, const float* a, T* out, int64_t n, float* dot,
@@ -245,11 +280,53 @@ transpose_kernel(const T* __restrict__ src, int64_t rows, int cols, int64_t lds,
     if (c < cols && r < rows_pad) Elem<T>::st(dst, (int64_t)c * ldd + r, tile[tx][i]);
   }
 }
+// bf16 version with 16-byte accesses on both sides (cols, lds, ldd, rows_pad and the batch strides
+// multiples of 8): each thread moves two 8-element row segments into an LDS tile and two 8-element
+// column segments out of it.
+__global__ void __launch_bounds__(256)
+transpose_bf16x8_kernel(const bf16* __restrict__ src, int64_t rows, int cols, int64_t lds, bf16* __restrict__ dst,
+                        int64_t ldd, int64_t rows_pad, int zdiv, int64_t sb_outer, int64_t sb_inner, int64_t sd) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+  const int z = blockIdx.z;
+  src += (int64_t)(z / zdiv) * sb_outer + (int64_t)(z % zdiv) * sb_inner;
+  dst += (int64_t)z * sd;
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
+  const int c0 = blockIdx.x * 64;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int item = threadIdx.x + 256 * k, row = item >> 3, seg = 8 * (item & 7);
+    const int64_t r = r0 + row;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (r < rows && c0 + seg < cols) u = *reinterpret_cast<const uint4*>(src + r * lds + c0 + seg);
+    *reinterpret_cast<uint4*>(&tile[row][seg]) = u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int item = threadIdx.x + 256 * k, col = item >> 3, rs = 8 * (item & 7);
+    const int64_t r = r0 + rs;
+    if (c0 + col >= cols || r >= rows_pad) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[rs + 2 * e][col] | ((uint32_t)tile[rs + 2 * e + 1][col] << 16);
+    *reinterpret_cast<uint4*>(dst + (int64_t)(c0 + col) * ldd + r) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 template <class T>
 inline hipError_t launch_transpose(const T* src, int64_t rows, int cols, int64_t lds, T* dst, int64_t ldd,
                                    int64_t rows_pad, int batch, int zdiv, int64_t sb_outer, int64_t sb_inner,
                                    int64_t sd, hipStream_t s) {
   if (cols <= 0 || rows_pad <= 0 || batch <= 0) return hipSuccess;
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (cols % 8 == 0 && lds % 8 == 0 && ldd % 8 == 0 && rows_pad % 8 == 0 && sb_outer % 8 == 0 &&
+        sb_inner % 8 == 0 && sd % 8 == 0 && aligned16(src) && aligned16(dst)) {
+      dim3 grid((unsigned)cdiv(cols, 64), (unsigned)cdiv(rows_pad, 64), (unsigned)batch);
+      LL_LAUNCH("transpose", transpose_bf16x8_kernel, grid, dim3(256), 0, s, src, rows, cols, lds, dst, ldd, rows_pad,
+                zdiv, sb_outer, sb_inner, sd);
+      return hipGetLastError();
+    }
+  }
   dim3 grid((unsigned)cdiv(cols, 64), (unsigned)cdiv(rows_pad, 64), (unsigned)batch);
   LL_LAUNCH("transpose", (transpose_kernel<T>), grid, dim3(256), 0, s, src, rows, cols, lds, dst, ldd, rows_pad,
                      zdiv, sb_outer, sb_inner, sd);

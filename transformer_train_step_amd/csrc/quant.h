@@ -39,17 +39,27 @@ template <class T>
 __global__ void __launch_bounds__(256) amax_kernel(const T* __restrict__ x, int64_t rows, int cols, int64_t ld, float* amax) {
   const int segs = cols / 8;
   float mx = 0.f;
-  const int64_t total = rows * segs;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i / segs;
-    const int c = (int)(i - r * segs) * 8;
-    float v[8];
-    Vec8<T>::load(x + r * ld + c, v);
+  const int64_t total = rows * segs, stride = (int64_t)gridDim.x * blockDim.x;
+  // four independent 16-byte loads in flight per thread and iteration
+  for (int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i0 < total; i0 += 4 * stride) {
+    float v[4][8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) mx = fmaxf(mx, fabsf(v[k]));
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < total) {
+        const int64_t r = i / segs;
+        Vec8<T>::load(x + r * ld + (int)(i - r * segs) * 8, v[u]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[u][k] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) mx = fmaxf(mx, fabsf(v[u][k]));
   }
-  mx = wave_max(mx);
-  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax, mx);
+  block_atomic_max_nonneg(amax, mx);
 }
 
 template <class T>
