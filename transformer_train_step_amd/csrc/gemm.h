@@ -97,8 +97,10 @@ __device__ __forceinline__ int kmaj_swz(int row) {
   // bank-conflict counter over every XOR map of the 4 row bits: this map serves a fragment read
   // with no conflict cycle, where a map over row bits 1..3 (one distinct chunk per row pair)
   // costs 4 extra cycles per read.
+  // 64-byte rows: chunk bit 1 from row bit 2 (measured the same way over all 256 maps; the former
+  // (row >> 2) & 3 cost 4 extra cycles per read)
   if constexpr (KB == 128) return (((row >> 1) & 1) << 2) | ((row >> 2) & 1);
-  else return (row >> 2) & 3;
+  else return ((row >> 2) & 1) << 1;
 }
 __device__ __forceinline__ int mn_swz(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 4) & 1)); }
 
@@ -249,7 +251,7 @@ __device__ __forceinline__ void sched_step() {
 // C[m, n] = sum_k A(m, k) B(n, k), A(m, k) = AK ? A[m * lda + k] : A[k * lda + m] (likewise B).
 // WGM x WGN waves; wave tile (BM/WGM) x (BN/WGN) in 16 x 16 MFMA fragments. K advances KB bytes
 // per tile through an NS-stage LDS ring: tile kt + NS - 1 is in flight while tile kt is multiplied.
-template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, bool AK, bool BK, class Epi, bool SP = false>
+template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, bool AK, bool BK, class Epi, int MODE = 0>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int64_t ldb, int M, int N, int K,
             const ET* __restrict__ zrow, Epi epi) {
@@ -265,6 +267,7 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   constexpr int NIW = STAGE / 1024 / NW;                    // load instructions per wave per tile
   // register-prefetch schedule: one wave per SIMD (4 waves, 128 x 128 each), 64-byte K tiles, 3 stages
   constexpr bool RP = (NW == 4 && NS == 3 && KB == 64 && BM == 256 && BN == 256);
+  constexpr bool SP = MODE == 1;   // split-phase K loop
   // One LDS array per stage: distinct objects let the compiler see that the direct loads into the
   // next stages do not alias the fragment reads of the current one (a single array indexed by
   // stage makes it wait for every load in flight before the first read of each tile).
@@ -697,7 +700,7 @@ struct GemmOps {
   const void* zrow = nullptr;       // >= 16 zero bytes: K-tail rows of MN-major operands
 };
 
-template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, bool SP = false, class Epi>
+template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, int MODE = 0, class Epi>
 inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
                                   const Epi& epi, const GemmOps& o, hipStream_t s) {
   const int64_t nb = cdiv(M, BM) * cdiv(N, BN);
@@ -706,25 +709,25 @@ inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t
   if constexpr (sizeof(ET) == 2) {
     if (!o.a_kmajor && !o.b_kmajor) {
       const char* tag = gemm_tag<ET, Epi, false, false>();
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, false, Epi, SP>), dim3((unsigned)nb), dim3(NT),
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, false, Epi, MODE>), dim3((unsigned)nb), dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
     if (!o.a_kmajor) {
       const char* tag = gemm_tag<ET, Epi, false, true>();
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, true, Epi, SP>), dim3((unsigned)nb), dim3(NT),
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, true, Epi, MODE>), dim3((unsigned)nb), dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
     if (!o.b_kmajor) {
       const char* tag = gemm_tag<ET, Epi, true, false>();
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, false, Epi, SP>), dim3((unsigned)nb), dim3(NT),
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, false, Epi, MODE>), dim3((unsigned)nb), dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
   }
   const char* tag = gemm_tag<ET, Epi, true, true>();
-  LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, true, Epi, SP>), dim3((unsigned)nb), dim3(NT), 0, s,
+  LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, true, Epi, MODE>), dim3((unsigned)nb), dim3(NT), 0, s,
                 A, lda, B, ldb, M, N, K, z, epi);
   return hipGetLastError();
 }
@@ -761,11 +764,11 @@ inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* 
         if (cfg == 7) return launch_gemm_cfg<ET, 128, 128, 2, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
         if (cfg == 8) return launch_gemm_cfg<ET, 256, 256, 2, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
         if (cfg == 9) {
-          if constexpr (sizeof(ET) == 2) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, true>(A, lda, B, ldb, M, N, K, epi, o, s);
+          if constexpr (sizeof(ET) == 2) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 1>(A, lda, B, ldb, M, N, K, epi, o, s);
           else return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
         }
         if (cfg == 10) {
-          if constexpr (sizeof(ET) == 2) return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2, true>(A, lda, B, ldb, M, N, K, epi, o, s);
+          if constexpr (sizeof(ET) == 2) return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2, 1>(A, lda, B, ldb, M, N, K, epi, o, s);
           else return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
         }
       }
