@@ -117,7 +117,7 @@ struct BwdWs {
   float2* cs;
   QScale* qs;            // [2]: dm, du
   void *dm, *du, *dhn, *dh, *dattn, *dout, *qt, *kt, *dot, *dqkv, *dxn;
-  void *t0, *t1;         // fp32 only: transposed operand copies for mm_nn / mm_tn
+  void *t0, *t1;         // transposed operand copies: W^T for mm_nn (both types), mm_tn's (fp32 only)
   const void* zrow;      // 256 zero bytes: K-tail rows of MN-major GEMM operands
   uint8_t *dm8, *dm8t, *du8, *du8t;
   float *delta, *dqh, *dkh, *dgp;
@@ -153,6 +153,9 @@ size_t carve_bwd(void* base, const Dims& d, BwdWs& w) {
     const int64_t t = std::max<int64_t>(big * d.Np, big * big);
     w.t0 = c.take<char>(t * e);
     w.t1 = c.take<char>(t * e);
+  } else {
+    // transposed weight of an input-gradient GEMM
+    w.t0 = c.take<char>(std::max<int64_t>({(int64_t)d.QKVD * d.D, (int64_t)d.F * d.D, (int64_t)d.QD * d.D}) * e);
   }
   if (d.fp8) {
     w.dm8 = c.take<uint8_t>(d.N * d.D);
@@ -183,20 +186,20 @@ hipError_t rope_table(float2* cs, const Dims& d, hipStream_t s) {
 }
 
 // Backward GEMMs whose operands are not both K-major.
-//   mm_nn: C = A W with A [M, K] K-major and W [K, N] row-major (the input-gradient GEMMs).
+//   mm_nn: C = A W with A [M, K] K-major and W [K, N] row-major (the input-gradient GEMMs): W is
+//          transposed first.
 //   mm_tn: C = X^T Y with X [K, M], Y [K, N] row-major, K = tokens (the weight-gradient GEMMs).
-// bf16 reads the row-major operands in place (MN-major, LDS transpose reads); fp32 goes through
-// transposed copies (token axis padded with zeros to Kp).
+//          bf16 reads X and Y in place (MN-major, LDS transpose reads); fp32 goes through
+//          transposed copies (token axis padded with zeros to Kp).
 template <class T, class Epi>
 hipError_t mm_nn(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const Epi& e, T* wT,
                  const void* zrow, hipStream_t s) {
-  if constexpr (std::is_same<T, bf16>::value) {
-    return launch_gemm(A, lda, W, ldw, M, N, K, e, GemmOps{true, false, zrow}, s);
-  } else {
-    hipError_t r = transpose2d(W, (int64_t)K, N, ldw, wT, (int64_t)K, (int64_t)K, s);
-    if (r != hipSuccess) return r;
-    return launch_gemm_nt(A, lda, static_cast<const T*>(wT), (int64_t)K, M, N, K, e, s);
-  }
+  // W^T first (a weight: tens of MB, microseconds), then a GEMM with both operands K-major, which
+  // runs ~20% faster than reading W through LDS transpose reads
+  (void)zrow;
+  hipError_t r = transpose2d(W, (int64_t)K, N, ldw, wT, (int64_t)K, (int64_t)K, s);
+  if (r != hipSuccess) return r;
+  return launch_gemm(A, lda, static_cast<const T*>(wT), (int64_t)K, M, N, K, e, GemmOps{}, s);
 }
 template <class T, class Epi>
 hipError_t mm_tn(const T* X, int64_t ldx, const T* Y, int64_t ldy, int M, int N, int64_t K, int64_t Kp, const Epi& e,
