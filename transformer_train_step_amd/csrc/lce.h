@@ -47,6 +47,11 @@ template <class T> struct EpiLceLogits {
   __device__ __forceinline__ void row(int m, int bn, float se) const { part[(int64_t)m * nparts + bn] = se; }
 };
 
+// The dH GEMM's epilogue: a plain store, traced under its own name
+template <class T> struct EpiLceDh : EpiStore<T> {
+  static constexpr const char* kName = "lce_dh";
+};
+
 __global__ void count_valid_kernel(const int32_t* __restrict__ y, int64_t n, int32_t ignore, int* __restrict__ nv) {
   int c = 0;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)

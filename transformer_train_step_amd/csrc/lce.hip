@@ -98,7 +98,7 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
                 (int)p.vpad, ignore, softcap, grad_scale, p.nv, z, static_cast<T*>(p.dzt), (int64_t)rows_pad);
     }
     LL_HIP(hipGetLastError());
-    EpiStore<T> eh{dH + r0 * d, (int64_t)d, Deq{nullptr, nullptr}};
+    EpiLceDh<T> eh{{dH + r0 * d, (int64_t)d, Deq{nullptr, nullptr}}};
     EpiAcc32 ew{p.dw32, (int64_t)d, r0 > 0 ? 1 : 0};
     // dH_c = dz W: A = dz [rows, Vpad] (K-major), B(n = d, k = v) = W^T[d, v] (K-major, zero past V)
     LL_HIP(launch_gemm(z, p.vpad, static_cast<const T*>(p.wt), p.vpad, rows, d, (int)p.vpad, eh, GemmOps{}, s));
