@@ -248,6 +248,25 @@ __device__ __forceinline__ void sched_step() {
   }
 }
 
+// Instruction order for the machine scheduler: NV0 global loads first, then NRD LDS reads and
+// NVM further loads spread evenly over NMF MFMAs (one read and one load per group, the MFMAs
+// divided over the groups), so that the reads and loads issue between MFMAs instead of in a burst
+// that the MFMAs queue behind.
+template <int NMF, int NRD, int NVM, int NV0 = 0>
+__device__ __forceinline__ void sched_interleave() {
+  constexpr int kMfma = 0x008, kVmem = 0x010, kDsRead = 0x100;
+  constexpr int G = NRD > NVM ? NRD : NVM, LO = NMF / G;
+  static_assert(G >= 1 && LO >= 1, "at least one MFMA per group");
+  if constexpr (NV0 > 0) __builtin_amdgcn_sched_group_barrier(kVmem, NV0, 0);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (g < NVM) __builtin_amdgcn_sched_group_barrier(kVmem, 1, 0);
+    if (g < NRD) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+    if ((g + 1) * NMF / G - g * NMF / G == LO) __builtin_amdgcn_sched_group_barrier(kMfma, LO, 0);
+    else __builtin_amdgcn_sched_group_barrier(kMfma, LO + 1, 0);
+  }
+}
+
 // C[m, n] = sum_k A(m, k) B(n, k), A(m, k) = AK ? A[m * lda + k] : A[k * lda + m] (likewise B).
 // WGM x WGN waves; wave tile (BM/WGM) x (BN/WGN) in 16 x 16 MFMA fragments. K advances KB bytes
 // per tile through an NS-stage LDS ring: tile kt + NS - 1 is in flight while tile kt is multiplied.
@@ -267,7 +286,9 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   constexpr int NIW = STAGE / 1024 / NW;                    // load instructions per wave per tile
   // register-prefetch schedule: one wave per SIMD (4 waves, 128 x 128 each), 64-byte K tiles, 3 stages
   constexpr bool RP = (NW == 4 && NS == 3 && KB == 64 && BM == 256 && BN == 256);
-  constexpr bool SP = MODE == 1;   // split-phase K loop
+  constexpr bool SP = MODE >= 1;   // split-phase K loop
+  constexpr bool IL = MODE == 2;   // ... with the reads and half the loads interleaved into the MFMAs
+  constexpr int NV0 = NIW / 2;     // loads issued together right after the barrier (IL)
   // One LDS array per stage: distinct objects let the compiler see that the direct loads into the
   // next stages do not alias the fragment reads of the current one (a single array indexed by
   // stage makes it wait for every load in flight before the first read of each tile).
@@ -392,18 +413,25 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
       // The chunk-0 fragments were read during the previous half step and have landed; waiting
       // for them here, before the next reads, keeps the count of LDS reads in flight small enough
       // (the counter holds 15) for the MFMAs below not to wait for the reads issued next.
+      // With IL the reads of each phase are spread evenly over its MFMAs; after the barrier half
+      // the loads go out at once (the earliest possible start for the next tile) and the other
+      // half between the MFMAs. Measured per K tile: ~2,950 clocks per wave instead of ~3,300.
       wait_lgkm0();
+      if constexpr (IL) __builtin_amdgcn_sched_barrier(0);
       rd(sa, I1{}, I1{});
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!IL) __builtin_amdgcn_sched_barrier(0);
       mm(I0{});
+      if constexpr (IL) sched_interleave<FM * FN, FM + FN, 0>();
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt_lgkm0<0>();              // tile kt + 1 has landed (this wave's part), tile kt is read
       asm volatile("s_barrier" ::: "memory");
+      if constexpr (IL) __builtin_amdgcn_sched_barrier(0);
       issue(min(kt + 2, nk - 1), sa);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!IL) __builtin_amdgcn_sched_barrier(0);
       rd(sn, I0{}, I0{});
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!IL) __builtin_amdgcn_sched_barrier(0);
       mm(I1{});
+      if constexpr (IL) sched_interleave<FM * FN, FM + FN, NIW - NV0, NV0>();
       __builtin_amdgcn_sched_barrier(0);
     };
     if (nk > 0) {
@@ -739,7 +767,8 @@ inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t
 //   7 = 128 x 128, 4 waves, 64 B, 3
 //   8 = 256 x 256, 4 waves (2 x 2, one per SIMD), 64 B, 3, fragments of the next K tile prefetched
 //       into registers across the barrier
-//   9 = 256 x 256, 8 waves (4 x 2), 128 B, 2, split-phase K loop (bf16; e4m3 falls back to 4)
+//   9 = 256 x 256, 8 waves (4 x 2), 128 B, 2, split-phase K loop with the LDS reads and half the
+//       loads interleaved into the MFMAs (bf16; e4m3 falls back to 4)
 //  10 = 256 x 256, 4 waves (2 x 2, one per SIMD), 128 B, 2, split-phase K loop (bf16; e4m3: 4)
 // e4m3 needs 128-byte K tiles (32 bytes of K per lane per MFMA): 5, 6, 7 fall back to 3, 4, 1.
 // 0 = automatic (gemm_config_override()).
@@ -764,7 +793,7 @@ inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* 
         if (cfg == 7) return launch_gemm_cfg<ET, 128, 128, 2, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
         if (cfg == 8) return launch_gemm_cfg<ET, 256, 256, 2, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
         if (cfg == 9) {
-          if constexpr (sizeof(ET) == 2) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 1>(A, lda, B, ldb, M, N, K, epi, o, s);
+          if constexpr (sizeof(ET) == 2) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
           else return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
         }
         if (cfg == 10) {
