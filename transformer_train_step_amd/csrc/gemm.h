@@ -690,7 +690,7 @@ template <class T> struct EpiQkv {
   }
 };
 
-// C32 = (accumulate ? C32 : 0) + acc   (fp32 accumulation across calls)
+// t = (accumulate ? C32 : 0) + acc   (fp32 accumulation across calls), stored to C32
 struct EpiAcc32 {
   static constexpr const char* kName = "acc32";
   static constexpr int kKind = kEpiPlain;
@@ -704,6 +704,21 @@ struct EpiAcc32 {
       for (int k = 0; k < 8; ++k) v[k] += o[k];
     }
     Vec8<float>::store(p, v);
+  }
+};
+
+// the last call of an fp32 accumulation: out = round(C32 + acc) (C32 is only read)
+template <class OutT> struct EpiAcc32Out {
+  static constexpr const char* kName = "acc32";
+  static constexpr int kKind = kEpiPlain;
+  const float* C; OutT* out; int64_t ldc;
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
+    const int64_t o = (int64_t)m * ldc + n;
+    float c[8];
+    Vec8<float>::load(C + o, c);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] += c[k];
+    Vec8<OutT>::store(out + o, v);
   }
 };
 

@@ -21,7 +21,7 @@ struct LcePlan {
   void* dzt = nullptr;      // dz^T [Vpad, chunk_pad]
   void* ht = nullptr;       // H_c^T [D, chunk_pad]
   void* zrow = nullptr;     // 256 zero bytes (K tails of MN-major operands)
-  float* dw32 = nullptr;    // [V, D] fp32 accumulator (several chunks, or the fp32 path)
+  float* dw32 = nullptr;    // [V, D] fp32 accumulator (several chunks)
   bool single = false;      // one chunk holds every token
   float* lse = nullptr;     // [chunk]
   float* loss_acc = nullptr;
@@ -34,7 +34,8 @@ LcePlan plan_lce(void* ws, int es, int64_t n, int d, int64_t v, int64_t token_ch
   p.chunk = token_chunk > 0 ? token_chunk : kDefaultChunk;
   if (p.chunk > n) p.chunk = n > 0 ? n : 1;
   // one chunk holds every token: the weight gradient is one contraction over all of them and is
-  // rounded straight into d_weight (no fp32 accumulator across chunks)
+  // rounded straight into d_weight (no fp32 accumulator across chunks); with several chunks the
+  // last chunk's GEMM rounds the fp32 total into d_weight
   p.single = n > 0 && p.chunk >= n;
   p.chunk_pad = round_up(p.chunk, 64);
   p.vpad = round_up(v, 64);
@@ -50,7 +51,7 @@ LcePlan plan_lce(void* ws, int es, int64_t n, int d, int64_t v, int64_t token_ch
     p.wt = c.take<char>((size_t)d * p.vpad * es);           // W^T [D, Vpad] (K-major B of the dH GEMM)
     p.dzt = c.take<char>((size_t)p.vpad * p.chunk_pad * es);  // dz^T and H_c^T: K-major operands
     p.ht = c.take<char>((size_t)d * p.chunk_pad * es);        // of the dW GEMM
-    if (!p.single || es == 4) p.dw32 = c.take<float>((size_t)v * d);
+    if (!p.single) p.dw32 = c.take<float>((size_t)v * d);
   }
   p.bytes = c.bytes();
   return p;
@@ -99,24 +100,29 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     }
     LL_HIP(hipGetLastError());
     EpiLceDh<T> eh{{dH + r0 * d, (int64_t)d, Deq{nullptr, nullptr}}};
-    EpiAcc32 ew{p.dw32, (int64_t)d, r0 > 0 ? 1 : 0};
     // dH_c = dz W: A = dz [rows, Vpad] (K-major), B(n = d, k = v) = W^T[d, v] (K-major, zero past V)
     LL_HIP(launch_gemm(z, p.vpad, static_cast<const T*>(p.wt), p.vpad, rows, d, (int)p.vpad, eh, GemmOps{}, s));
     // dW += dz^T H_c: A = dz^T [Vpad, rows_pad], B = H_c^T [D, rows_pad], both K-major over the
-    // chunk's tokens (zero past rows); with one chunk (bf16) the exact fp32 sum over all tokens is
+    // chunk's tokens (zero past rows); with one chunk the exact fp32 sum over all tokens is
     // rounded straight into dW
     LL_HIP(transpose2d(Hc, rows, d, (int64_t)d, static_cast<T*>(p.ht), (int64_t)rows_pad, (int64_t)rows_pad, s));
     const T* dzt = static_cast<const T*>(p.dzt);
     const T* ht = static_cast<const T*>(p.ht);
-    if (p.single && !p.dw32) {
+    if (p.single) {
       EpiStore<T> ewd{dW, (int64_t)d, Deq{nullptr, nullptr}};
       LL_HIP(launch_gemm(dzt, (int64_t)rows_pad, ht, (int64_t)rows_pad, (int)v, d, rows_pad, ewd, GemmOps{}, s));
+    } else if (r0 + rows < n) {
+      // fp32 sums over the chunks in dw32
+      EpiAcc32 ew{p.dw32, (int64_t)d, r0 > 0 ? 1 : 0};
+      LL_HIP(launch_gemm(dzt, (int64_t)rows_pad, ht, (int64_t)rows_pad, (int)v, d, rows_pad, ew, GemmOps{}, s));
     } else {
+      // the last chunk's GEMM rounds the fp32 total into dW
+      EpiAcc32Out<T> ew{p.dw32, dW, (int64_t)d};
       LL_HIP(launch_gemm(dzt, (int64_t)rows_pad, ht, (int64_t)rows_pad, (int)v, d, rows_pad, ew, GemmOps{}, s));
     }
   }
-  if (grads && p.dw32) {
-    if (n == 0) LL_HIP(fill_f32(p.dw32, 0.f, v * d, s));     // no chunk ran: dW = 0
+  if (grads && n == 0) {                                   // no chunk ran: dW = 0
+    LL_HIP(fill_f32(p.dw32, 0.f, v * d, s));
     LL_HIP(launch_convert(p.dw32, dW, v * d, s));
   }
   LL_LAUNCH("lce_finalize", lce_finalize_kernel, dim3(1), dim3(1), 0, s, p.loss_acc, p.nv, loss);
