@@ -144,6 +144,52 @@ def test_gemm_operand_layouts(ak, bk, M, N, K):
     assert_close(host(C), ref, 1e-5, "gemm layouts", elem_rtol=1e-4)
 
 
+@pytest.mark.parametrize("ak,bk,M,N,K,slices,out", [
+    (False, False, 3072, 3072, 40960, 7, "bf16"),   # the attention output projection's weight gradient
+    (False, False, 136, 520, 1000, 3, "fp32"),      # ragged M/N; last slice shorter, K tail reads zero rows
+    (True, True, 264, 136, 700, 4, "fp32"),         # K-major operands, K padded to 704
+    (True, False, 8, 8, 130, 5, "fp32"),            # more slices than 64-element K blocks: 3 slices run
+    (False, False, 64, 64, 0, 2, "fp32"),           # empty K: zeros
+])
+def test_gemm_splitk(ak, bk, M, N, K, slices, out):
+    """bf16 GEMM split along K into fp32 partial sums added by a second kernel: every slice boundary
+    lies on a 64-element K tile, the last slice is ragged, MN-major tails read the zero row."""
+    need_gpu()
+    print(f"gemm splitk ak={ak} bk={bk} {M}x{N}x{K} slices={slices} out={out}", flush=True)
+    a = synth.normal((M, K), 1.0, 5, 1, "bf16")
+    b = synth.normal((N, K), 0.05, 5, 2, "bf16")
+    kp = (K + 63) // 64 * 64
+    ap = np.zeros((M, kp), dtype=a.dtype)
+    bp = np.zeros((N, kp), dtype=b.dtype)
+    ap[:, :K] = a
+    bp[:, :K] = b
+    A = dev(ap if ak else np.ascontiguousarray(a.T), "bf16")
+    B = dev(bp if bk else np.ascontiguousarray(b.T), "bf16")
+    lda = kp if ak else M
+    ldb = kp if bk else N
+    C = torch.full((M, N), 7.0, dtype=torch.float32 if out == "fp32" else torch.bfloat16, device="cuda")
+    nws = ll.llt_gemm_splitk_workspace_bytes(M, N, slices)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ll.llt_gemm_splitk(ak, bk, A, lda, B, ldb, M, N, K, slices, ll.LL_F32 if out == "fp32" else ll.LL_BF16,
+                       C, N, ws, nws)
+    torch.cuda.synchronize()
+    got = host(C.float())
+    if K == 0:
+        assert np.all(got == 0.0)
+        return
+    if M * N > 1 << 20:
+        # a 3072 x 3072 x 40960 product in float64 is costly on the host: check sampled rows
+        rows = np.random.default_rng(0).choice(M, 48, replace=False)
+        ref = a[rows].astype(np.float64) @ b.astype(np.float64).T
+        got = got[rows]
+    else:
+        ref = a.astype(np.float64) @ b.astype(np.float64).T
+    if out == "fp32":
+        assert_close(got, ref, 1e-5, "gemm splitk", elem_rtol=1e-4)
+    else:
+        assert_close(got, ref, 4e-3, "gemm splitk bf16", elem_rtol=8e-3)
+
+
 def test_gemm_e4m3_subnormal_operands():
     """Subnormal e4m3 operands (|v| < 2^-6) take part in the e4m3 MFMA like normal ones: A holds
     only subnormal codes, B only normal codes, and the result equals the exact GEMM to the MFMA's

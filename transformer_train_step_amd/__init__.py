@@ -8,4 +8,4 @@ from ._lib import (LL_BF16, LL_F32, LLError, LayerCfg, LayerGrads, LayerParams, 
                    ll_fp8_quant_tensorwise, ll_fp8_quant_workspace_bytes, ll_fused_lce_fwd_bwd,
                    ll_fused_lce_workspace_bytes, ll_last_error, ll_layer_bwd, ll_layer_fwd,
                    ll_layer_saved_bytes, ll_layer_workspace_bytes, ll_status_string, ll_version,
-                   llt_gemm, llt_gemm_nt)
+                   llt_gemm, llt_gemm_nt, llt_gemm_splitk, llt_gemm_splitk_workspace_bytes)

@@ -97,6 +97,9 @@ _SIGS = {
     "llt_gemm": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_int64, c_int32,
                            c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
                            c_size_t, c_void_p]),
+    "llt_gemm_splitk_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+    "llt_gemm_splitk": (c_int32, [c_int32, c_int32, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_int32,
+                                  c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_size_t, c_void_p]),
     "llt_set_gemm_config": (c_int32, [c_int32]),
     "llt_trace_begin": (c_int32, [c_int32]),
     "llt_trace_end": (c_int32, []),
@@ -268,6 +271,16 @@ def llt_gemm_nt(op_dtype, A, lda, B, ldb, M, N, K, out_dtype, C, ldc, inv_a=None
     """llt_gemm with both operands K-major."""
     return llt_gemm(op_dtype, 1, 1, A, lda, B, ldb, M, N, K, out_dtype, C, ldc, inv_a, inv_b, None, 0, stream,
                     raise_on_error)
+
+
+def llt_gemm_splitk_workspace_bytes(M, N, slices) -> int:
+    return lib().llt_gemm_splitk_workspace_bytes(M, N, slices)
+
+
+def llt_gemm_splitk(a_kmajor, b_kmajor, A, lda, B, ldb, M, N, K, slices, out_dtype, C, ldc, ws, ws_bytes,
+                    stream=None, raise_on_error=True):
+    return _call("llt_gemm_splitk", int(a_kmajor), int(b_kmajor), ptr(A), lda, ptr(B), ldb, M, N, K, slices,
+                 out_dtype, ptr(C), ldc, ptr(ws), ws_bytes, stream_handle(stream), raise_on_error=raise_on_error)
 
 
 def llt_set_gemm_config(cfg: int):

@@ -267,6 +267,12 @@ __device__ __forceinline__ void sched_interleave() {
   }
 }
 
+// Split-K epilogues (static constexpr bool kSplitK = true, int kchunk): block row blockIdx.y of the
+// grid takes K elements [blockIdx.y kchunk, min(K, (blockIdx.y + 1) kchunk)) and the epilogue
+// stores its partial sums apart from the other slices'.
+template <class E, class = void> struct IsSplitK : std::false_type {};
+template <class E> struct IsSplitK<E, std::void_t<decltype(E::kSplitK)>> : std::bool_constant<E::kSplitK> {};
+
 // C[m, n] = sum_k A(m, k) B(n, k), A(m, k) = AK ? A[m * lda + k] : A[k * lda + m] (likewise B).
 // WGM x WGN waves; wave tile (BM/WGM) x (BN/WGN) in 16 x 16 MFMA fragments. K advances KB bytes
 // per tile through an NS-stage LDS ring: tile kt + NS - 1 is in flight while tile kt is multiplied.
@@ -312,6 +318,13 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   const char* Bb = reinterpret_cast<const char*>(B);
   const char* zb = reinterpret_cast<const char*>(zrow);
   const int64_t ldab = lda * (int64_t)sizeof(ET), ldbb = ldb * (int64_t)sizeof(ET);
+  int Kl = K;                                               // K elements of this block
+  if constexpr (IsSplitK<Epi>::value) {
+    const int k0 = (int)blockIdx.y * epi.kchunk;
+    Kl = min(K - k0, epi.kchunk);
+    Ab += AK ? (int64_t)k0 * (int64_t)sizeof(ET) : (int64_t)k0 * ldab;
+    Bb += BK ? (int64_t)k0 * (int64_t)sizeof(ET) : (int64_t)k0 * ldbb;
+  }
 
   auto stage = [&](auto si) -> unsigned char* {
     constexpr int S = decltype(si)::value;
@@ -321,8 +334,8 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
     else return st3;
   };
   auto issue = [&](int kt, unsigned char* sa) {
-    issue_tile<ET, AK, BM, KB, NW>(Ab, ldab, m0, M, kt, K, zb, sa, wave, lane);
-    issue_tile<ET, BK, BN, KB, NW>(Bb, ldbb, n0, N, kt, K, zb, sa + BM * KB, wave, lane);
+    issue_tile<ET, AK, BM, KB, NW>(Ab, ldab, m0, M, kt, Kl, zb, sa, wave, lane);
+    issue_tile<ET, BK, BN, KB, NW>(Bb, ldbb, n0, N, kt, Kl, zb, sa + BM * KB, wave, lane);
   };
 
   floatx4 acc[FN][FM];
@@ -331,7 +344,7 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (int)cdiv(K, KE);
+  const int nk = (int)cdiv(Kl, KE);
   // K tile kt lives in stage kt % NS; step<S> handles the tiles with kt % NS == S. Every step
   // issues exactly one tile (NIW loads per wave), so NS - 1 tiles are always in flight and one
   // constant wait count holds in every step: past the last tile, the loads repeat tile nk - 1
@@ -722,6 +735,36 @@ template <class OutT> struct EpiAcc32Out {
   }
 };
 
+// fp32 partial sums of K slice blockIdx.y: C[blockIdx.y slice + m ldc + n] = acc
+struct EpiSplitK32 {
+  static constexpr const char* kName = "splitk";
+  static constexpr int kKind = kEpiPlain;
+  static constexpr bool kSplitK = true;
+  float* C; int64_t ldc; int64_t slice; int kchunk;
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
+    Vec8<float>::store(C + (int64_t)blockIdx.y * slice + (int64_t)m * ldc + n, v);
+  }
+};
+
+// out[m, n] = round(sum over the S slices of part[s slice + m ldp + n]), 8 columns per thread
+template <class T>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int S, int64_t slice,
+                                                           int64_t ldp, int M, int N, T* __restrict__ out, int64_t ldo) {
+  const int nseg = N / 8;
+  const int64_t total = (int64_t)M * nseg;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(i / nseg), n = (int)(i % nseg) * 8;
+    float v[8], t[8];
+    Vec8<float>::load(part + (int64_t)m * ldp + n, v);
+    for (int sl = 1; sl < S; ++sl) {
+      Vec8<float>::load(part + sl * slice + (int64_t)m * ldp + n, t);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] += t[k];
+    }
+    Vec8<T>::store(out + (int64_t)m * ldo + n, v);
+  }
+}
+
 // ------------------------------------------------------------------ launcher
 template <class ET> struct OpName;
 template <> struct OpName<float> { static constexpr const char* s = "f32"; };
@@ -746,31 +789,34 @@ struct GemmOps {
 template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, int MODE = 0, class Epi>
 inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
                                   const Epi& epi, const GemmOps& o, hipStream_t s) {
-  const int64_t nb = cdiv(M, BM) * cdiv(N, BN);
+  const int64_t nbt = cdiv(M, BM) * cdiv(N, BN);
+  unsigned slices = 1;
+  if constexpr (IsSplitK<Epi>::value) slices = (unsigned)std::max<int64_t>(1, cdiv(K, epi.kchunk));
+  const dim3 nb((unsigned)nbt, slices);
   const ET* z = static_cast<const ET*>(o.zrow);
   constexpr int NT = 64 * WGM * WGN;
   if constexpr (sizeof(ET) == 2) {
     if (!o.a_kmajor && !o.b_kmajor) {
       const char* tag = gemm_tag<ET, Epi, false, false>();
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, false, Epi, MODE>), dim3((unsigned)nb), dim3(NT),
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, false, Epi, MODE>), nb, dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
     if (!o.a_kmajor) {
       const char* tag = gemm_tag<ET, Epi, false, true>();
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, true, Epi, MODE>), dim3((unsigned)nb), dim3(NT),
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, true, Epi, MODE>), nb, dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
     if (!o.b_kmajor) {
       const char* tag = gemm_tag<ET, Epi, true, false>();
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, false, Epi, MODE>), dim3((unsigned)nb), dim3(NT),
+      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, false, Epi, MODE>), nb, dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi);
       return hipGetLastError();
     }
   }
   const char* tag = gemm_tag<ET, Epi, true, true>();
-  LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, true, Epi, MODE>), dim3((unsigned)nb), dim3(NT), 0, s,
+  LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, true, Epi, MODE>), nb, dim3(NT), 0, s,
                 A, lda, B, ldb, M, N, K, z, epi);
   return hipGetLastError();
 }
@@ -845,6 +891,39 @@ inline hipError_t launch_gemm(const ET* A, int64_t lda, const ET* B, int64_t ldb
     cfg = e256 >= e128 ? (kk16 ? 9 : o.b_kmajor ? 4 : 3) : 1;
   }
   return launch_gemm_with(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
+}
+
+// Number of K slices (1..smax) for a GEMM of `tiles` 256 x 256 output tiles: the one that fills the
+// last wave of blocks on 256 CUs best (fewest slices within 2% of the best), each slice at least
+// 8 K tiles long.
+inline int splitk_slices(int64_t tiles, int64_t K, int ke, int smax) {
+  auto eff = [&](int sl) { return (double)(tiles * sl) / (double)(cdiv(tiles * sl, 256) * 256); };
+  int best = 1;
+  for (int sl = 2; sl <= smax; ++sl)
+    if (K >= (int64_t)sl * 8 * ke && eff(sl) > eff(best) + 0.02) best = sl;
+  return best;
+}
+
+// out = round(A B^T) (OutT) in `slices` K slices: the GEMM writes each slice's fp32 partial sums to
+// scratch [slices, M, N] and a second kernel adds them. For GEMMs with a long K and too few output
+// tiles to fill the chip (weight gradients of small projections).
+template <class ET, class OutT>
+inline hipError_t launch_gemm_splitk(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
+                                     int slices, OutT* out, int64_t ldo, float* scratch, const GemmOps& o,
+                                     hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  constexpr int KE = 128 / (int)sizeof(ET);
+  const int kchunk = (int)std::max<int64_t>(KE, round_up(cdiv(K, slices), KE));
+  const int sl = (int)std::max<int64_t>(1, cdiv(K, kchunk));
+  EpiSplitK32 e{scratch, (int64_t)N, (int64_t)M * N, kchunk};
+  int cfg = gemm_config_override();
+  if (cfg == 0) cfg = sizeof(ET) == 2 && o.a_kmajor && o.b_kmajor ? 9 : o.b_kmajor ? 4 : 3;
+  hipError_t r = launch_gemm_with(cfg, A, lda, B, ldb, M, N, K, e, o, s);
+  if (r != hipSuccess) return r;
+  const int64_t work = (int64_t)M * (N / 8);
+  LL_LAUNCH("splitk_reduce", splitk_reduce_kernel<OutT>, dim3((unsigned)std::min<int64_t>(cdiv(work, 256), 8192)),
+            dim3(256), 0, s, scratch, sl, (int64_t)M * N, (int64_t)N, M, N, out, ldo);
+  return hipGetLastError();
 }
 
 template <class ET, class Epi>

@@ -190,7 +190,8 @@ hipError_t rope_table(float2* cs, const Dims& d, hipStream_t s) {
 //          transposed first.
 //   mm_tn: C = X^T Y with X [K, M], Y [K, N] row-major, K = tokens (the weight-gradient GEMMs).
 //          bf16 reads X and Y in place (MN-major, LDS transpose reads); fp32 goes through
-//          transposed copies (token axis padded with zeros to Kp).
+//          transposed copies (token axis padded with zeros to Kp). With a scratch buffer (sk,
+//          sk_bytes) a bf16 GEMM with too few output tiles for the chip is split along the tokens.
 template <class T, class Epi>
 hipError_t mm_nn(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const Epi& e, T* wT,
                  const void* zrow, hipStream_t s) {
@@ -203,9 +204,15 @@ hipError_t mm_nn(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N,
 }
 template <class T, class Epi>
 hipError_t mm_tn(const T* X, int64_t ldx, const T* Y, int64_t ldy, int M, int N, int64_t K, int64_t Kp, const Epi& e,
-                 T* xT, T* yT, const void* zrow, hipStream_t s) {
+                 T* xT, T* yT, const void* zrow, hipStream_t s, float* sk = nullptr, size_t sk_bytes = 0) {
   if constexpr (std::is_same<T, bf16>::value) {
-    return launch_gemm(X, ldx, Y, ldy, M, N, (int)K, e, GemmOps{false, false, zrow}, s);
+    const GemmOps ops{false, false, zrow};
+    if constexpr (std::is_same<Epi, EpiStore<T>>::value) {
+      const int sl = splitk_slices(cdiv(M, 256) * cdiv(N, 256), K, 64, 8);
+      if (sl > 1 && sk && !e.dq.ia && (size_t)sl * M * N * sizeof(float) <= sk_bytes && gemm_config_override() == 0)
+        return launch_gemm_splitk(X, ldx, Y, ldy, M, N, (int)K, sl, e.C, e.ldc, sk, ops, s);
+    }
+    return launch_gemm(X, ldx, Y, ldy, M, N, (int)K, e, ops, s);
   } else {
     hipError_t r = transpose2d(X, K, M, ldx, xT, Kp, Kp, s);
     if (r == hipSuccess) r = transpose2d(Y, K, N, ldy, yT, Kp, Kp, s);
@@ -369,7 +376,9 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   }
   {
     EpiStore<T> e{P<T>(g->w_o), (int64_t)d.QD, Deq{nullptr, nullptr}};
-    LL_HIP(mm_tn(CP<T>(w.dattn), d.D, CP<T>(sv.o), d.QD, d.D, d.QD, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s));
+    // du (dead after the MLP backward) holds the split-K partial sums
+    LL_HIP(mm_tn(CP<T>(w.dattn), d.D, CP<T>(sv.o), d.QD, d.D, d.QD, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s,
+                 P<float>(w.du), (size_t)(d.N * d.F * d.es)));
   }
   // attention core
   T* dqkv = P<T>(w.dqkv);
@@ -427,7 +436,8 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   }
   {
     EpiStore<T> e{P<T>(g->w_qkv), (int64_t)d.D, Deq{nullptr, nullptr}};
-    LL_HIP(mm_tn(CP<T>(dqkv), d.QKVD, CP<T>(sv.xn), d.D, d.QKVD, d.D, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s));
+    LL_HIP(mm_tn(CP<T>(dqkv), d.QKVD, CP<T>(sv.xn), d.D, d.QKVD, d.D, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s,
+                 P<float>(w.du), (size_t)(d.N * d.F * d.es)));
   }
   // input RMSNorm backward + residual
   LL_HIP(launch_rmsnorm_bwd(CP<T>(w.dxn), x, g1, sv.r1, CP<T>(w.dh), dx, w.dgp, N, d.D, (const float*)nullptr,

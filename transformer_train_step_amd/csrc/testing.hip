@@ -53,6 +53,43 @@ extern "C" int llt_gemm(int32_t op_dtype, int32_t a_kmajor, int32_t b_kmajor, co
   return gemm_dispatch<fp8>(A, lda, B, ldb, M, N, K, out_dtype, C, ldc, inv_a, inv_b, o, s);
 }
 
+extern "C" size_t llt_gemm_splitk_workspace_bytes(int32_t M, int32_t N, int32_t slices) {
+  if (M < 0 || N < 0 || slices < 1 || slices > 16) return 0;
+  return 256 + (size_t)slices * M * N * sizeof(float);
+}
+
+extern "C" int llt_gemm_splitk(int32_t a_kmajor, int32_t b_kmajor, const void* A, int64_t lda, const void* B,
+                               int64_t ldb, int32_t M, int32_t N, int32_t K, int32_t slices, int32_t out_dtype,
+                               void* C, int64_t ldc, void* ws, size_t ws_bytes, void* stream) {
+  LL_CHECK(out_dtype == LL_F32 || out_dtype == LL_BF16, LL_ERR_INVALID_ARG, "bad out_dtype");
+  LL_CHECK(M >= 0 && N >= 0 && K >= 0, LL_ERR_INVALID_ARG, "negative size");
+  LL_CHECK(slices >= 1 && slices <= 16, LL_ERR_INVALID_ARG, "slices must be in [1, 16]");
+  const bool ak = a_kmajor != 0, bk = b_kmajor != 0;
+  LL_CHECK(N % 8 == 0 && ldc % 8 == 0 && ldc >= N, LL_ERR_UNSUPPORTED, "N and ldc must be multiples of 8, ldc >= N");
+  const int64_t kp = round_up(K, 64);
+  LL_CHECK(!ak || (lda >= kp && lda % 8 == 0), LL_ERR_INVALID_ARG, "K-major A: lda >= K rounded to 64, lda % 8 == 0");
+  LL_CHECK(!bk || (ldb >= kp && ldb % 8 == 0), LL_ERR_INVALID_ARG, "K-major B: ldb >= K rounded to 64, ldb % 8 == 0");
+  LL_CHECK(ak || (lda >= M && lda % 8 == 0 && M % 8 == 0), LL_ERR_INVALID_ARG, "MN-major A: M % 8 == 0, lda >= M, lda % 8 == 0");
+  LL_CHECK(bk || (ldb >= N && ldb % 8 == 0), LL_ERR_INVALID_ARG, "MN-major B: ldb >= N, ldb % 8 == 0");
+  const size_t need = llt_gemm_splitk_workspace_bytes(M, N, slices);
+  LL_CHECK(ws && aligned16(ws) && ws_bytes >= need, LL_ERR_WORKSPACE,
+           "ws must be 16-byte aligned and hold llt_gemm_splitk_workspace_bytes");
+  if (M == 0 || N == 0) return LL_OK;
+  LL_CHECK(C && ((A && B) || K == 0), LL_ERR_INVALID_ARG, "null pointer");
+  LL_CHECK(aligned16(A) && aligned16(B) && aligned16(C), LL_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LL_HIP(fill_f32(static_cast<float*>(ws), 0.f, 64, s));
+  const GemmOps o{ak, bk, ws};
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + 256);
+  const bf16* a = static_cast<const bf16*>(A);
+  const bf16* b = static_cast<const bf16*>(B);
+  if (out_dtype == LL_BF16)
+    LL_HIP(launch_gemm_splitk(a, lda, b, ldb, M, N, K, slices, static_cast<bf16*>(C), ldc, part, o, s));
+  else
+    LL_HIP(launch_gemm_splitk(a, lda, b, ldb, M, N, K, slices, static_cast<float*>(C), ldc, part, o, s));
+  return LL_OK;
+}
+
 extern "C" int llt_set_gemm_config(int32_t cfg) {
   LL_CHECK(cfg >= 0 && cfg <= 10, LL_ERR_INVALID_ARG, "cfg must be in [0, 10]");
   set_gemm_config_override(cfg);
