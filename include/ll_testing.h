@@ -30,18 +30,18 @@ int llt_gemm(int32_t op_dtype, int32_t a_kmajor, int32_t b_kmajor, const void* A
              int64_t ldb, int32_t M, int32_t N, int32_t K, int32_t out_dtype, void* C, int64_t ldc,
              const float* inv_a, const float* inv_b, void* ws, size_t ws_bytes, void* stream);
 
-/* The same product for bf16 operands, split along K: slice s (of `slices`, 1..16) sums K elements
- * [s c, min(K, (s + 1) c)), c = K / slices rounded up to 64, into fp32 partials in ws; a second
- * kernel adds the slices in order and rounds once to out_dtype. Used for weight gradients whose
- * output has too few 256 x 256 tiles to fill the chip. Layouts and K-major padding as llt_gemm
- * (K-major rows padded to a multiple of 64 elements, zero beyond K).
+/* The same product (bf16, or e4m3 with both operands K-major) split along K: slice s (of `slices`,
+ * 1..16) sums K elements [s c, min(K, (s + 1) c)), c = K / slices rounded up to the K tile (64 bf16,
+ * 128 e4m3), into fp32 partials in ws; a second kernel adds the slices in order, multiplies by
+ * *inv_a * *inv_b (if given) and rounds once to out_dtype. Used for weight gradients whose output
+ * has too few 256 x 256 tiles to fill the chip. Layouts, padding and scales as llt_gemm.
  *   ws: >= llt_gemm_splitk_workspace_bytes(M, N, slices) bytes, 16-byte aligned (256 bytes of zero
  *   row for MN-major K tails, then slices * M * N fp32 partials). K == 0 writes zeros (A and B may
  *   then be NULL). */
 size_t llt_gemm_splitk_workspace_bytes(int32_t M, int32_t N, int32_t slices);
-int llt_gemm_splitk(int32_t a_kmajor, int32_t b_kmajor, const void* A, int64_t lda, const void* B, int64_t ldb,
-                    int32_t M, int32_t N, int32_t K, int32_t slices, int32_t out_dtype, void* C, int64_t ldc,
-                    void* ws, size_t ws_bytes, void* stream);
+int llt_gemm_splitk(int32_t op_dtype, int32_t a_kmajor, int32_t b_kmajor, const void* A, int64_t lda, const void* B,
+                    int64_t ldb, int32_t M, int32_t N, int32_t K, int32_t slices, int32_t out_dtype, void* C,
+                    int64_t ldc, const float* inv_a, const float* inv_b, void* ws, size_t ws_bytes, void* stream);
 
 /* Process-wide override of the GEMM configuration (for measurements). Block tile, waves, bytes of K
  * per LDS tile row, LDS stages: 1 = 128 x 128, 4 waves, 128 B, 2; 2 = 256 x 256, 4 waves, 128 B, 2;

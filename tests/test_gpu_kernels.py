@@ -170,8 +170,8 @@ def test_gemm_splitk(ak, bk, M, N, K, slices, out):
     C = torch.full((M, N), 7.0, dtype=torch.float32 if out == "fp32" else torch.bfloat16, device="cuda")
     nws = ll.llt_gemm_splitk_workspace_bytes(M, N, slices)
     ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
-    ll.llt_gemm_splitk(ak, bk, A, lda, B, ldb, M, N, K, slices, ll.LL_F32 if out == "fp32" else ll.LL_BF16,
-                       C, N, ws, nws)
+    ll.llt_gemm_splitk(ll._lib.LLT_OP_BF16, ak, bk, A, lda, B, ldb, M, N, K, slices,
+                       ll.LL_F32 if out == "fp32" else ll.LL_BF16, C, N, ws, nws)
     torch.cuda.synchronize()
     got = host(C.float())
     if K == 0:
@@ -188,6 +188,39 @@ def test_gemm_splitk(ak, bk, M, N, K, slices, out):
         assert_close(got, ref, 1e-5, "gemm splitk", elem_rtol=1e-4)
     else:
         assert_close(got, ref, 4e-3, "gemm splitk bf16", elem_rtol=8e-3)
+
+
+@pytest.mark.parametrize("M,N,K,slices", [
+    (3072, 12288, 4096, 4),   # the MLP weight-gradient shape (D x F), 576 output tiles
+    (200, 136, 1000, 3),      # ragged M/N, K padded to 1024 with zero codes
+])
+def test_gemm_splitk_e4m3(M, N, K, slices):
+    """e4m3 GEMM split along K, the slices' fp32 partials added and scaled by inv_a * inv_b in the
+    reduction kernel, compared with the exact product of the decoded codes."""
+    need_gpu()
+    print(f"gemm splitk e4m3 {M}x{N}x{K} slices={slices}", flush=True)
+    rng = np.random.default_rng(21)
+    kp = (K + 127) // 128 * 128
+    a_codes = np.zeros((M, kp), np.uint8)
+    b_codes = np.zeros((N, kp), np.uint8)
+    a_codes[:, :K] = rng.integers(0, 0x7F, (M, K)) | (rng.integers(0, 2, (M, K)) << 7)
+    b_codes[:, :K] = rng.integers(0, 0x7F, (N, K)) | (rng.integers(0, 2, (N, K)) << 7)
+    a_codes[a_codes == 0xFF] = 0
+    b_codes[b_codes == 0xFF] = 0
+    ia, ib = 0.03125, 0.75
+    inv = torch.tensor([ia, ib], dtype=torch.float32, device="cuda")
+    C = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    nws = ll.llt_gemm_splitk_workspace_bytes(M, N, slices)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ll.llt_gemm_splitk(ll._lib.LLT_OP_E4M3, True, True, torch.from_numpy(a_codes).cuda(), kp,
+                       torch.from_numpy(b_codes).cuda(), kp, M, N, K, slices, ll.LL_BF16, C, N, ws, nws,
+                       inv[0:1], inv[1:2])
+    torch.cuda.synchronize()
+    got = host(C.float())
+    rows = np.random.default_rng(1).choice(M, min(M, 64), replace=False)
+    ref = (nu.e4m3_decode(a_codes[rows]) @ nu.e4m3_decode(b_codes).T) * ia * ib
+    # bf16 output rounding plus the e4m3 MFMA's reduced-precision 128-deep sums
+    assert_close(got[rows], ref, 4e-3, "gemm splitk e4m3", elem_rtol=1e-2)
 
 
 def test_gemm_e4m3_subnormal_operands():

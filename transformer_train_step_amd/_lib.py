@@ -98,8 +98,9 @@ _SIGS = {
                            c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
                            c_size_t, c_void_p]),
     "llt_gemm_splitk_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
-    "llt_gemm_splitk": (c_int32, [c_int32, c_int32, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_int32,
-                                  c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_size_t, c_void_p]),
+    "llt_gemm_splitk": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_int64, c_int32,
+                                  c_int32, c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_void_p,
+                                  c_void_p, c_size_t, c_void_p]),
     "llt_set_gemm_config": (c_int32, [c_int32]),
     "llt_trace_begin": (c_int32, [c_int32]),
     "llt_trace_end": (c_int32, []),
@@ -277,10 +278,11 @@ def llt_gemm_splitk_workspace_bytes(M, N, slices) -> int:
     return lib().llt_gemm_splitk_workspace_bytes(M, N, slices)
 
 
-def llt_gemm_splitk(a_kmajor, b_kmajor, A, lda, B, ldb, M, N, K, slices, out_dtype, C, ldc, ws, ws_bytes,
-                    stream=None, raise_on_error=True):
-    return _call("llt_gemm_splitk", int(a_kmajor), int(b_kmajor), ptr(A), lda, ptr(B), ldb, M, N, K, slices,
-                 out_dtype, ptr(C), ldc, ptr(ws), ws_bytes, stream_handle(stream), raise_on_error=raise_on_error)
+def llt_gemm_splitk(op_dtype, a_kmajor, b_kmajor, A, lda, B, ldb, M, N, K, slices, out_dtype, C, ldc, ws,
+                    ws_bytes, inv_a=None, inv_b=None, stream=None, raise_on_error=True):
+    return _call("llt_gemm_splitk", op_dtype, int(a_kmajor), int(b_kmajor), ptr(A), lda, ptr(B), ldb, M, N, K,
+                 slices, out_dtype, ptr(C), ldc, ptr(inv_a), ptr(inv_b), ptr(ws), ws_bytes, stream_handle(stream),
+                 raise_on_error=raise_on_error)
 
 
 def llt_set_gemm_config(cfg: int):

@@ -746,10 +746,11 @@ struct EpiSplitK32 {
   }
 };
 
-// out[m, n] = round(sum over the S slices of part[s slice + m ldp + n]), 8 columns per thread
+// out[m, n] = round(deq(sum over the S slices of part[s slice + m ldp + n])), 8 columns per thread
 template <class T>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int S, int64_t slice,
-                                                           int64_t ldp, int M, int N, T* __restrict__ out, int64_t ldo) {
+                                                           int64_t ldp, int M, int N, T* __restrict__ out, int64_t ldo,
+                                                           Deq dq) {
   const int nseg = N / 8;
   const int64_t total = (int64_t)M * nseg;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
@@ -761,6 +762,8 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] += t[k];
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = dq.apply(v[k]);
     Vec8<T>::store(out + (int64_t)m * ldo + n, v);
   }
 }
@@ -904,13 +907,13 @@ inline int splitk_slices(int64_t tiles, int64_t K, int ke, int smax) {
   return best;
 }
 
-// out = round(A B^T) (OutT) in `slices` K slices: the GEMM writes each slice's fp32 partial sums to
-// scratch [slices, M, N] and a second kernel adds them. For GEMMs with a long K and too few output
-// tiles to fill the chip (weight gradients of small projections).
+// out = round(deq(A B^T)) (OutT) in `slices` K slices: the GEMM writes each slice's fp32 partial
+// sums to scratch [slices, M, N] and a second kernel adds them. For GEMMs with a long K and too few
+// output tiles to fill the chip (weight gradients).
 template <class ET, class OutT>
 inline hipError_t launch_gemm_splitk(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
                                      int slices, OutT* out, int64_t ldo, float* scratch, const GemmOps& o,
-                                     hipStream_t s) {
+                                     hipStream_t s, Deq dq = Deq{nullptr, nullptr}) {
   if (M <= 0 || N <= 0) return hipSuccess;
   constexpr int KE = 128 / (int)sizeof(ET);
   const int kchunk = (int)std::max<int64_t>(KE, round_up(cdiv(K, slices), KE));
@@ -922,7 +925,7 @@ inline hipError_t launch_gemm_splitk(const ET* A, int64_t lda, const ET* B, int6
   if (r != hipSuccess) return r;
   const int64_t work = (int64_t)M * (N / 8);
   LL_LAUNCH("splitk_reduce", splitk_reduce_kernel<OutT>, dim3((unsigned)std::min<int64_t>(cdiv(work, 256), 8192)),
-            dim3(256), 0, s, scratch, sl, (int64_t)M * N, (int64_t)N, M, N, out, ldo);
+            dim3(256), 0, s, scratch, sl, (int64_t)M * N, (int64_t)N, M, N, out, ldo, dq);
   return hipGetLastError();
 }
 

@@ -302,6 +302,19 @@ int layer_fwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   return LL_OK;
 }
 
+// FP8 weight gradient C [M, N] = deq(X Y^T) over the token axis (both operands the quantiser's
+// transposed codes, K-major, Np tokens): split along the tokens when the output has too few 256 x 256
+// tiles for the chip and the scratch holds the partial sums.
+template <class T>
+hipError_t wgrad_e4m3(const uint8_t* X, const uint8_t* Y, int64_t Np, int M, int N, T* C, Deq dq, float* sk,
+                      size_t sk_bytes, hipStream_t s) {
+  const int sl = splitk_slices(cdiv(M, 256) * cdiv(N, 256), Np, 128, 8);
+  if (sl > 1 && (size_t)sl * M * N * sizeof(float) <= sk_bytes && gemm_config_override() == 0)
+    return launch_gemm_splitk(X, Np, Y, Np, M, N, (int)Np, sl, C, (int64_t)N, sk, GemmOps{}, s, dq);
+  EpiStore<T> e{C, (int64_t)N, dq};
+  return launch_gemm_nt(X, Np, Y, Np, M, N, (int)Np, e, s);
+}
+
 // ------------------------------------------------------------------------------------------ bwd
 template <class T, int DH>
 int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32_t* ids, const Saved& sv,
@@ -329,16 +342,17 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
         EpiRelu2Bwd<T> e{P<T>(w.du), CP<T>(sv.u), (int64_t)d.F, Deq{&qdm->inv_scale, &q[QS_W2].inv_scale}, &qdu->amax};
         LL_HIP(launch_gemm_nt(w.dm8, d.D, sv.w28t, d.D, (int)N, d.F, d.D, e, s));
       }
-      {   // dW2 = dm^T r   [D, F]
-        EpiStore<T> e{P<T>(g->w_proj), (int64_t)d.F, Deq{&qdm->inv_scale, &q[QS_R].inv_scale}};
-        LL_HIP(launch_gemm_nt(w.dm8t, Np, sv.r8t, Np, d.D, d.F, (int)Np, e, s));
-      }
       LL_HIP(launch_cast_e4m3(CP<T>(w.du), N, d.F, d.F, qdu, w.du8, d.F, w.du8t, Np, Np, (float*)nullptr,
                               (float*)nullptr, s));
-      {   // dW1 = du^T hn  [F, D]
-        EpiStore<T> e{P<T>(g->w_fc), (int64_t)d.D, Deq{&qdu->inv_scale, &q[QS_HN].inv_scale}};
-        LL_HIP(launch_gemm_nt(w.du8t, Np, sv.hn8t, Np, d.F, d.D, (int)Np, e, s));
-      }
+      // the bf16 du is dead from here: it holds the split-K partial sums of the weight gradients
+      float* sk = P<float>(w.du);
+      const size_t sk_bytes = (size_t)(d.N * d.F * d.es);
+      // dW2 = dm^T r   [D, F]
+      LL_HIP(wgrad_e4m3(w.dm8t, sv.r8t, Np, d.D, d.F, P<T>(g->w_proj), Deq{&qdm->inv_scale, &q[QS_R].inv_scale}, sk,
+                        sk_bytes, s));
+      // dW1 = du^T hn  [F, D]
+      LL_HIP(wgrad_e4m3(w.du8t, sv.hn8t, Np, d.F, d.D, P<T>(g->w_fc), Deq{&qdu->inv_scale, &q[QS_HN].inv_scale}, sk,
+                        sk_bytes, s));
       {   // dhn = du W1 (W1^T quantised is [D, F])
         EpiStore<T> e{P<T>(w.dhn), (int64_t)d.D, Deq{&qdu->inv_scale, &q[QS_W1].inv_scale}};
         LL_HIP(launch_gemm_nt(w.du8, d.F, sv.w18t, d.F, (int)N, d.D, d.F, e, s));

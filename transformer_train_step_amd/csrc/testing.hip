@@ -58,19 +58,37 @@ extern "C" size_t llt_gemm_splitk_workspace_bytes(int32_t M, int32_t N, int32_t 
   return 256 + (size_t)slices * M * N * sizeof(float);
 }
 
-extern "C" int llt_gemm_splitk(int32_t a_kmajor, int32_t b_kmajor, const void* A, int64_t lda, const void* B,
-                               int64_t ldb, int32_t M, int32_t N, int32_t K, int32_t slices, int32_t out_dtype,
-                               void* C, int64_t ldc, void* ws, size_t ws_bytes, void* stream) {
+template <class ET>
+static int splitk_dispatch(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K, int slices,
+                           int32_t out_dtype, void* C, int64_t ldc, float* part, Deq dq, const GemmOps& o,
+                           hipStream_t s) {
+  const ET* a = static_cast<const ET*>(A);
+  const ET* b = static_cast<const ET*>(B);
+  if (out_dtype == LL_BF16)
+    LL_HIP(launch_gemm_splitk(a, lda, b, ldb, M, N, K, slices, static_cast<bf16*>(C), ldc, part, o, s, dq));
+  else
+    LL_HIP(launch_gemm_splitk(a, lda, b, ldb, M, N, K, slices, static_cast<float*>(C), ldc, part, o, s, dq));
+  return LL_OK;
+}
+
+extern "C" int llt_gemm_splitk(int32_t op_dtype, int32_t a_kmajor, int32_t b_kmajor, const void* A, int64_t lda,
+                               const void* B, int64_t ldb, int32_t M, int32_t N, int32_t K, int32_t slices,
+                               int32_t out_dtype, void* C, int64_t ldc, const float* inv_a, const float* inv_b,
+                               void* ws, size_t ws_bytes, void* stream) {
+  LL_CHECK(op_dtype == LLT_OP_BF16 || op_dtype == LLT_OP_E4M3, LL_ERR_INVALID_ARG, "op_dtype must be bf16 or e4m3");
   LL_CHECK(out_dtype == LL_F32 || out_dtype == LL_BF16, LL_ERR_INVALID_ARG, "bad out_dtype");
   LL_CHECK(M >= 0 && N >= 0 && K >= 0, LL_ERR_INVALID_ARG, "negative size");
   LL_CHECK(slices >= 1 && slices <= 16, LL_ERR_INVALID_ARG, "slices must be in [1, 16]");
   const bool ak = a_kmajor != 0, bk = b_kmajor != 0;
+  const int esz = op_dtype == LLT_OP_BF16 ? 2 : 1, ke = 128 / esz;
+  LL_CHECK((ak && bk) || op_dtype == LLT_OP_BF16, LL_ERR_UNSUPPORTED, "MN-major operands need bf16");
   LL_CHECK(N % 8 == 0 && ldc % 8 == 0 && ldc >= N, LL_ERR_UNSUPPORTED, "N and ldc must be multiples of 8, ldc >= N");
-  const int64_t kp = round_up(K, 64);
-  LL_CHECK(!ak || (lda >= kp && lda % 8 == 0), LL_ERR_INVALID_ARG, "K-major A: lda >= K rounded to 64, lda % 8 == 0");
-  LL_CHECK(!bk || (ldb >= kp && ldb % 8 == 0), LL_ERR_INVALID_ARG, "K-major B: ldb >= K rounded to 64, ldb % 8 == 0");
+  const int64_t kp = round_up(K, ke);
+  LL_CHECK(!ak || (lda >= kp && (lda * esz) % 16 == 0), LL_ERR_INVALID_ARG, "K-major A: lda >= K rounded to the K tile, 16-byte rows");
+  LL_CHECK(!bk || (ldb >= kp && (ldb * esz) % 16 == 0), LL_ERR_INVALID_ARG, "K-major B: ldb >= K rounded to the K tile, 16-byte rows");
   LL_CHECK(ak || (lda >= M && lda % 8 == 0 && M % 8 == 0), LL_ERR_INVALID_ARG, "MN-major A: M % 8 == 0, lda >= M, lda % 8 == 0");
   LL_CHECK(bk || (ldb >= N && ldb % 8 == 0), LL_ERR_INVALID_ARG, "MN-major B: ldb >= N, ldb % 8 == 0");
+  LL_CHECK((inv_a == nullptr) == (inv_b == nullptr), LL_ERR_INVALID_ARG, "inv_a and inv_b: both or neither");
   const size_t need = llt_gemm_splitk_workspace_bytes(M, N, slices);
   LL_CHECK(ws && aligned16(ws) && ws_bytes >= need, LL_ERR_WORKSPACE,
            "ws must be 16-byte aligned and hold llt_gemm_splitk_workspace_bytes");
@@ -81,13 +99,9 @@ extern "C" int llt_gemm_splitk(int32_t a_kmajor, int32_t b_kmajor, const void* A
   LL_HIP(fill_f32(static_cast<float*>(ws), 0.f, 64, s));
   const GemmOps o{ak, bk, ws};
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + 256);
-  const bf16* a = static_cast<const bf16*>(A);
-  const bf16* b = static_cast<const bf16*>(B);
-  if (out_dtype == LL_BF16)
-    LL_HIP(launch_gemm_splitk(a, lda, b, ldb, M, N, K, slices, static_cast<bf16*>(C), ldc, part, o, s));
-  else
-    LL_HIP(launch_gemm_splitk(a, lda, b, ldb, M, N, K, slices, static_cast<float*>(C), ldc, part, o, s));
-  return LL_OK;
+  if (op_dtype == LLT_OP_BF16)
+    return splitk_dispatch<bf16>(A, lda, B, ldb, M, N, K, slices, out_dtype, C, ldc, part, Deq{inv_a, inv_b}, o, s);
+  return splitk_dispatch<fp8>(A, lda, B, ldb, M, N, K, slices, out_dtype, C, ldc, part, Deq{inv_a, inv_b}, o, s);
 }
 
 extern "C" int llt_set_gemm_config(int32_t cfg) {
