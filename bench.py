@@ -43,11 +43,11 @@ SOURCES = ("transformer_train_step_amd/csrc/gemm.h", "transformer_train_step_amd
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated (valid while the sources
 # hash to sha256_16; otherwise the roofline reports traffic null)
 TRAFFIC = {
-    "gemm_bf16_acc32_kk": {"sources": SOURCES, "sha256_16": "28f4214b897d862e", "read_bytes": 6.2581e+09,
-                           "write_bytes": 6.3285e+08,
+    "gemm_bf16_acc32_kk": {"sources": SOURCES, "sha256_16": "f677a6ee8c48aaff", "read_bytes": 6.2688e+09,
+                           "write_bytes": 5.4592e+08,
                            "profile": "profiles/gemm_bf16_acc32_kk_hbm_bytes_layer_lce_40x1024.md"},
-    "gemm_bf16_lce_logits_kk": {"sources": SOURCES, "sha256_16": "28f4214b897d862e", "read_bytes": 5.9731e+09,
-                                "write_bytes": 1.1063e+09,
+    "gemm_bf16_lce_logits_kk": {"sources": SOURCES, "sha256_16": "f677a6ee8c48aaff", "read_bytes": 5.4683e+09,
+                                "write_bytes": 1.0717e+09,
                                 "profile": "profiles/gemm_bf16_lce_logits_kk_hbm_bytes_layer_lce_40x1024.md"},
 }
 

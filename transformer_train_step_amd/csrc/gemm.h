@@ -688,7 +688,6 @@ template <class T> struct EpiRelu2Bwd {
 template <class T> struct EpiQkv {
   static constexpr const char* kName = "qkv";
   static constexpr int kKind = kEpiPlain;
-  static constexpr bool kSplitPhase = false;   // the split-phase loop spills with this epilogue
   T* C; int64_t ldc; const T* table; int64_t ldt; const int32_t* ids; int vcol0;
   __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
 #pragma unroll
@@ -869,11 +868,6 @@ inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* 
   }
 }
 
-// Whether the automatic choice may take the split-phase K loop with epilogue E (an epilogue opts out
-// with a static constexpr bool kSplitPhase = false).
-template <class E, class = void> struct SplitPhaseOk : std::true_type {};
-template <class E> struct SplitPhaseOk<E, std::void_t<decltype(E::kSplitPhase)>> : std::bool_constant<E::kSplitPhase> {};
-
 // Picks the block tile from the wave quantisation on 256 CUs: 256 x 256 with 8 waves (measured
 // ~25% faster per FLOP than 128 x 128 on the layer's shapes) unless its last wave of blocks
 // leaves so many CUs idle that 128 x 128 finishes first. Requirements (checked by the callers): K a multiple of the K tile for K-major
@@ -890,7 +884,7 @@ inline hipError_t launch_gemm(const ET* A, int64_t lda, const ET* B, int64_t ldb
     const double e128 = 0.75 * (double)t128 / (double)(cdiv(t128, 256) * 256);
     // 4 x 2 waves, except 2 x 4 when B is MN-major (measured ~3% faster there); bf16 with both
     // operands K-major takes the split-phase K loop (measured 2-5% faster than config 4)
-    const bool kk16 = sizeof(ET) == 2 && SplitPhaseOk<Epi>::value && o.a_kmajor && o.b_kmajor;
+    const bool kk16 = sizeof(ET) == 2 && o.a_kmajor && o.b_kmajor;
     cfg = e256 >= e128 ? (kk16 ? 9 : o.b_kmajor ? 4 : 3) : 1;
   }
   return launch_gemm_with(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
