@@ -159,6 +159,8 @@ def main():
     ap.add_argument("--no-trace", action="store_true", help="skip the traced pass (roofline)")
     ap.add_argument("--kernels", action="store_true",
                     help="print every traced kernel (ms per step, launches, TFLOP/s of its algorithmic work)")
+    ap.add_argument("--lce-chunk", type=int, default=10240, metavar="TOKENS",
+                    help="tokens per chunk of the fused linear cross-entropy (logits of one chunk are stored)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, copy a MIB-MiB device buffer once (a plain copy of known size, "
                          "the reference for HBM byte counters)")
@@ -198,9 +200,10 @@ def main():
         del src, dst
     t_in = time.perf_counter()
     if args.workload == "model":
-        step, n_launch_trace = model_step(w, dev, torch, synth, LayerConfig, Model)
+        step, n_launch_trace = model_step(w, dev, torch, synth, LayerConfig, Model, args.lce_chunk)
     else:
-        step, n_launch_trace = layer_lce_step(w, dev, torch, synth, LayerConfig, Layer, FusedLCE, to_dev)
+        step, n_launch_trace = layer_lce_step(w, dev, torch, synth, LayerConfig, Layer, FusedLCE, to_dev,
+                                              args.lce_chunk)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in HBM ({time.perf_counter() - t_in:.1f} s to generate)")
 
@@ -225,7 +228,7 @@ def main():
     report(args, w, ms, step, stream, ev0, ev1, L, n_launch_trace)
 
 
-def layer_lce_step(w, dev, torch, synth, LayerConfig, Layer, FusedLCE, to_dev):
+def layer_lce_step(w, dev, torch, synth, LayerConfig, Layer, FusedLCE, to_dev, lce_chunk):
     """Inputs and the step closure of the layer / loss workloads (inputs drawn by synth)."""
     B, T = w["batch"], w["seq"]
     N = B * T
@@ -252,7 +255,7 @@ def layer_lce_step(w, dev, torch, synth, LayerConfig, Layer, FusedLCE, to_dev):
     if w["lce"]:
         w_head = to_dev(synth.normal((V, D), 0.02, 0, synth.K_WHEAD, "bf16"))
         targets = torch.from_numpy(synth.uniform_ints((N,), V_REAL, 0, synth.K_TARGETS)).to(dev)
-        lce = FusedLCE("bf16", N, D, V, token_chunk=10240, device=dev)
+        lce = FusedLCE("bf16", N, D, V, token_chunk=lce_chunk, device=dev)
         dh_buf = torch.empty_like(x)
         dw_head = torch.empty_like(w_head)
     del inp
@@ -272,7 +275,7 @@ def layer_lce_step(w, dev, torch, synth, LayerConfig, Layer, FusedLCE, to_dev):
     return step, 4096
 
 
-def model_step(w, dev, torch, synth, LayerConfig, Model):
+def model_step(w, dev, torch, synth, LayerConfig, Model, lce_chunk):
     """Inputs and the step closure of the whole model. Its ~3.9B weights are drawn on the GPU with
     torch's seeded generator (N(0, 0.02), bf16; gains and residual scalars 1); token ids and
     targets come from synth."""
@@ -296,7 +299,7 @@ def model_step(w, dev, torch, synth, LayerConfig, Model):
             lp["ve_table"] = rn(V, HKV * DH)
         layers.append(lp)
     params = {"embed": rn(V, D), "layers": layers, "final_norm_w": torch.ones(D, device=dev), "head": rn(V, D)}
-    model = Model(LayerConfig(batch=B, seq=T), n_layers, V, token_chunk=10240, device=dev)
+    model = Model(LayerConfig(batch=B, seq=T), n_layers, V, token_chunk=lce_chunk, device=dev)
     grads = model.new_grads(params)
     ids = torch.from_numpy(synth.uniform_ints((N,), V_REAL, 0, synth.K_IDS)).to(dev)
     targets = torch.from_numpy(synth.uniform_ints((N,), V_REAL, 0, synth.K_TARGETS)).to(dev)
@@ -320,7 +323,8 @@ def report(args, w, ms, step, stream, ev0, ev1, L, n_launch_trace):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16+e4m3",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, uniform token ids)",
-        "config": {"workload": w["desc"], "tokens_per_step": N, "batch": B, "seq_len": T},
+        "config": {"workload": w["desc"], "tokens_per_step": N, "batch": B, "seq_len": T,
+                   "lce_token_chunk": args.lce_chunk},
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
         "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / PEAK_BF16, 2),
         "algorithmic_flops_per_step": flops,
