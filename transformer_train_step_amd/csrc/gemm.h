@@ -663,6 +663,25 @@ template <class T> struct EpiRelu2 {
   }
 };
 
+// u = round(deq(acc)); stores u only; returns max of r = round(relu(u)^2) (the quantiser of r then
+// reads u and forms the same r)
+template <class T> struct EpiRelu2Amax {
+  static constexpr const char* kName = "relu2";
+  static constexpr int kKind = kEpiAmax;
+  T* u; int64_t ld; Deq dq; float* amax;
+  __device__ __forceinline__ float seg(int m, int n, float (&v)[8]) const {
+    float mx = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[k] = Elem<T>::rnd(dq.apply(v[k]));
+      const float p = fmaxf(v[k], 0.f);
+      mx = fmaxf(mx, Elem<T>::rnd(p * p));
+    }
+    Vec8<T>::store(u + (int64_t)m * ld + n, v);
+    return mx;
+  }
+};
+
 // dr = round(deq(acc)); du = round(dr * 2 relu(u)); stores du; returns max |du|
 template <class T> struct EpiRelu2Bwd {
   static constexpr const char* kName = "relu2_bwd";

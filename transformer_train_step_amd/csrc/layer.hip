@@ -95,18 +95,17 @@ size_t carve_saved(void* base, const Dims& d, Saved& s) {
 // ---------------------------------------------------------------- forward workspace
 struct FwdWs {
   float2* cs;
-  void *vt, *hn, *r;
+  void *vt, *hn;
   uint8_t* r8;
 };
 size_t carve_fwd(void* base, const Dims& d, FwdWs& w) {
   Carver c(base);
   w.cs = c.take<float2>(d.T * (d.DH / 2) + 1);
   w.vt = d.bf ? nullptr : c.take<char>(d.B * d.KVD * d.Tp * d.es);   // fp32 kernels read V^T
-  w.hn = w.r = nullptr;
+  w.hn = nullptr;
   w.r8 = nullptr;
   if (d.fp8) {
     w.hn = c.take<char>(d.N * d.D * d.es);
-    w.r = c.take<char>(d.N * d.F * d.es);
     w.r8 = c.take<uint8_t>(d.N * d.F);
   }
   return c.bytes();
@@ -276,12 +275,12 @@ int layer_fwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
       LL_HIP(launch_cast_e4m3(CP<T>(w.hn), N, d.D, d.D, &q[QS_HN], sv.hn8, d.D, sv.hn8t, d.Np, d.Np,
                               (float*)nullptr, (float*)nullptr, s));
       {
-        EpiRelu2<T> e{P<T>(sv.u), P<T>(w.r), (int64_t)d.F, Deq{&q[QS_HN].inv_scale, &q[QS_W1].inv_scale},
-                      &q[QS_R].amax};
+        // u is stored; r = relu(u)^2 only reaches HBM as e4m3 codes (the cast forms r from u)
+        EpiRelu2Amax<T> e{P<T>(sv.u), (int64_t)d.F, Deq{&q[QS_HN].inv_scale, &q[QS_W1].inv_scale}, &q[QS_R].amax};
         LL_HIP(launch_gemm_nt(sv.hn8, d.D, sv.w18, d.D, (int)N, d.F, d.D, e, s));
       }
-      LL_HIP(launch_cast_e4m3(CP<T>(w.r), N, d.F, d.F, &q[QS_R], w.r8, d.F, sv.r8t, d.Np, d.Np,
-                              (float*)nullptr, (float*)nullptr, s));
+      LL_HIP((launch_cast_e4m3<T, true>(CP<T>(sv.u), N, d.F, d.F, &q[QS_R], w.r8, d.F, sv.r8t, d.Np, d.Np,
+                                        (float*)nullptr, (float*)nullptr, s)));
       {
         EpiResidual<T> e{y, CP<T>(sv.h), P<T>(sv.m), (int64_t)d.D, p->resid_mlp,
                          Deq{&q[QS_R].inv_scale, &q[QS_W2].inv_scale}};

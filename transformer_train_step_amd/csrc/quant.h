@@ -88,7 +88,9 @@ __device__ __forceinline__ uint8_t quant_one(float x, float scale) {
 //   q   [rows, ldq] (or null); qt [cols, ldqt] (or null) with ldqt >= rows_pad >= rows;
 //   the grid covers rows_pad rows so qt[:, rows:rows_pad] is zero-filled.
 // cols % 16 == 0, ld % 8 == 0, ldq % 16 == 0 (any ldqt; 16-byte stores when ldqt % 16 == 0). Block (0,0) thread 0 also writes qs->scale / qs->inv_scale.
-template <class T>
+// RELU2: the tensor quantised is r = round(relu(x)^2), formed from x on the fly (x = the MLP's
+// pre-activation u, so r itself is never stored).
+template <class T, bool RELU2 = false>
 __global__ void __launch_bounds__(256)
 cast_e4m3_kernel(const T* __restrict__ x, int64_t rows, int cols, int64_t ld, QScale* qs,
                  uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qt, int64_t ldqt,
@@ -112,6 +114,13 @@ cast_e4m3_kernel(const T* __restrict__ x, int64_t rows, int cols, int64_t ld, QS
     float v[16];
     Vec8<T>::load(x + r * ld + c, *reinterpret_cast<float(*)[8]>(v));
     Vec8<T>::load(x + r * ld + c + 8, *reinterpret_cast<float(*)[8]>(v + 8));
+    if constexpr (RELU2) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float p = fmaxf(v[k], 0.f);
+        v[k] = Elem<T>::rnd(p * p);
+      }
+    }
 #pragma unroll
     for (int k = 0; k < 16; ++k) w[k >> 2] |= (uint32_t)quant_one(v[k], scale) << (8 * (k & 3));
     if (q) *reinterpret_cast<uint4*>(q + r * ldq + c) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -136,15 +145,15 @@ cast_e4m3_kernel(const T* __restrict__ x, int64_t rows, int cols, int64_t ld, QS
   }
 }
 
-template <class T>
+template <class T, bool RELU2 = false>
 inline hipError_t launch_cast_e4m3(const T* x, int64_t rows, int cols, int64_t ld, QScale* qs,
                                    uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, int64_t rows_pad,
                                    float* scale_out, float* inv_out, hipStream_t s) {
   const int64_t rp = qt ? rows_pad : rows;
   const int64_t gy = cdiv(std::max<int64_t>(rp, 1), 64);
   const int gx = (int)cdiv(std::max(cols, 1), 64);
-  LL_LAUNCH("cast_e4m3", (cast_e4m3_kernel<T>), dim3(gx, (unsigned)gy), dim3(256), 0, s, x, rows, cols, ld, qs,
-                     q, ldq, qt, ldqt, rp, scale_out, inv_out);
+  LL_LAUNCH(RELU2 ? "cast_e4m3_relu2" : "cast_e4m3", (cast_e4m3_kernel<T, RELU2>), dim3(gx, (unsigned)gy), dim3(256), 0,
+            s, x, rows, cols, ld, qs, q, ldq, qt, ldqt, rp, scale_out, inv_out);
   return hipGetLastError();
 }
 
