@@ -92,24 +92,15 @@ template <> struct Vec4<float> {
 };
 
 // ------------------------------------------------------------------ e4m3fn
-// Round a finite fp32 with |v| <= 448 to the nearest e4m3fn code, ties to even. Written from the
-// OCP E4M3 definition: bias 7, 3 mantissa bits, subnormal quantum 2^-9, largest finite 448.
-// For |v| >= 2^-6 the code is the fp32 pattern rebiased (exponent -120) with the mantissa
-// rounded from 23 to 3 bits; below 2^-6 it is |v| / 2^-9 rounded to an integer 0..8 (8 being
-// the smallest normal 2^-6, code 0x08).
-__device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= 0x3C800000u) {                      // |v| >= 2^-6: normal
-    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);  // RNE at mantissa bit 20
-    code = ((r >> 20) - (120u << 3)) & 0x7Fu;       // exponent 127 -> 7
-  } else {                                     // subnormal: k = rne(|v| * 2^9), 0 <= k <= 8
-    float s = __uint_as_float(a) * 512.0f;     // exact (power-of-two scaling, |v| < 2^-6)
-    code = (uint32_t)__builtin_rintf(s);       // rintf: ties to even
-  }
-  return (uint8_t)(sign | code);
+// Round finite fp32 values with |v| <= 448 to the nearest e4m3fn codes, ties to even (OCP E4M3:
+// bias 7, 3 mantissa bits, subnormal quantum 2^-9, largest finite 448), four at a time, code k in
+// byte k. gfx950's v_cvt_pk_fp8_f32 converts to OCP e4m3fn with round-to-nearest-even and
+// subnormals; over every fp32 pattern with |v| <= 448 it gives the same code as rebiasing the
+// exponent (-120) and rounding the mantissa from 23 to 3 bits (|v| >= 2^-6), or rounding |v| / 2^-9
+// to an integer (|v| < 2^-6), which is how the rule was checked.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float v0, float v1, float v2, float v3) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, lo, true);
 }
 
 // Decode an e4m3fn code (finite codes only) to fp32.

@@ -77,10 +77,12 @@ __device__ __forceinline__ void scales_from_amax(float amax, float& scale, float
   inv = __fdiv_rn(1.0f, scale);                                   // exact for a power of two
 }
 
-__device__ __forceinline__ uint8_t quant_one(float x, float scale) {
-  float y = __fmul_rn(x, scale);
-  y = fminf(fmaxf(y, -448.0f), 448.0f);
-  return f32_to_e4m3(y);
+// Codes of 4 values: clamp(fl32(x * scale), -448, 448) rounded to e4m3fn
+__device__ __forceinline__ uint32_t quant4(const float* x, float scale) {
+  float y[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) y[k] = fminf(fmaxf(__fmul_rn(x[k], scale), -448.0f), 448.0f);
+  return f32x4_to_e4m3(y[0], y[1], y[2], y[3]);
 }
 
 // Cast of x [rows, cols] with the scale derived from qs->amax. Block = 64 rows x 64 cols tile,
@@ -122,7 +124,7 @@ cast_e4m3_kernel(const T* __restrict__ x, int64_t rows, int cols, int64_t ld, QS
       }
     }
 #pragma unroll
-    for (int k = 0; k < 16; ++k) w[k >> 2] |= (uint32_t)quant_one(v[k], scale) << (8 * (k & 3));
+    for (int k = 0; k < 4; ++k) w[k] = quant4(v + 4 * k, scale);
     if (q) *reinterpret_cast<uint4*>(q + r * ldq + c) = make_uint4(w[0], w[1], w[2], w[3]);
   }
   if (!qt) return;
