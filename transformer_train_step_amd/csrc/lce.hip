@@ -76,7 +76,8 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
   for (int64_t r0 = 0; r0 < n; r0 += p.chunk) {
     const int rows = (int)std::min<int64_t>(p.chunk, n - r0);
     const T* Hc = H + r0 * d;
-    EpiLceLogits<T> epi{z, p.vpad, p.part, p.nparts, softcap, 1.f / softcap};
+    constexpr float kLog2e = 1.4426950408889634f;
+    EpiLceLogits<T> epi{z, p.vpad, p.part, p.nparts, 2.f * kLog2e / softcap, softcap * kLog2e};
     {
       // the row-LSE partials assume 256 vocabulary columns per block tile
       const int oc = gemm_config_override();
