@@ -274,11 +274,12 @@ def test_gemm_e4m3_products_and_accumulation_precision():
     assert abs(got - 65663.0) <= 65663.0 * 2.0 ** -10
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11])
 @pytest.mark.parametrize("op,ak,bk,K", [
     ("bf16", True, True, 64), ("bf16", True, True, 192), ("bf16", True, True, 320),
     ("bf16", False, False, 200), ("bf16", True, False, 1000), ("bf16", False, True, 96),
-    ("fp32", True, True, 96), ("e4m3", True, True, 384),
+    ("fp32", True, True, 96), ("e4m3", True, True, 128), ("e4m3", True, True, 384), ("e4m3", True, True, 640),
+    ("e4m3", True, True, 2048),
 ])
 def test_gemm_block_configs(cfg, op, ak, bk, K):
     """Every block-tile / K-tile / LDS-stage configuration on ragged M and N and on K-tile counts

@@ -27,6 +27,7 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -102,6 +103,10 @@ __device__ __forceinline__ int kmaj_swz(int row) {
   if constexpr (KB == 128) return (((row >> 1) & 1) << 2) | ((row >> 2) & 1);
   else return ((row >> 2) & 1) << 1;
 }
+// 128-byte rows read as 32-row fragments (the 32x32 MFMA: lanes l and l + 32 read the same row at
+// chunks two apart, rows r and r + 16 in the same instruction): the 16-row map above with chunk bit 1
+// from row bit 4. Measured with the LDS bank-conflict counter to take no conflict cycle.
+__device__ __forceinline__ int kmaj_swz32(int row) { return kmaj_swz<128>(row) ^ (((row >> 4) & 1) << 1); }
 __device__ __forceinline__ int mn_swz(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 4) & 1)); }
 
 // Issue the direct global->LDS loads of one operand tile for K tile kt (this wave's share).
@@ -109,7 +114,7 @@ __device__ __forceinline__ int mn_swz(int k) { return (2 * (k & 3)) ^ (8 * ((k >
 //   MN-major: element (r, k) at g[k * ld + r]; tile = KB/es k-rows x ROWS elements; k-rows at or
 //   beyond kvalid read the zero row instead (the K tail of a token-contracted GEMM).
 // Rows/columns past rmax are clamped to valid memory; they only feed outputs that are not stored.
-template <class ET, bool KMAJ, int ROWS, int KB, int NW>
+template <class ET, bool KMAJ, int ROWS, int KB, int NW, bool S32 = false>
 __device__ __forceinline__ void issue_tile(const char* g, int64_t ldb, int r0, int rmax, int kt, int kvalid,
                                            const char* zrow, unsigned char* lds_op, int wave, int lane) {
   constexpr int TILE = ROWS * KB;
@@ -123,7 +128,7 @@ __device__ __forceinline__ void issue_tile(const char* g, int64_t ldb, int r0, i
     if constexpr (KMAJ) {
       constexpr int CPR = KB / 16;
       const int row = base / KB + lane / CPR;
-      const int logical = (lane % CPR) ^ kmaj_swz<KB>(row);
+      const int logical = (lane % CPR) ^ (S32 ? kmaj_swz32(row) : kmaj_swz<KB>(row));
       const int gr = min(r0 + row, rmax - 1);
       src = g + gr * ldb + (int64_t)kt * KB + logical * 16;
     } else {
@@ -202,6 +207,17 @@ __device__ __forceinline__ u32x4 read_chunk(const unsigned char* t, int off, int
   }
 }
 
+// 32-row K-major fragment of 128-byte rows for the 32x32x64 e4m3 MFMA: lane l takes row
+// f0 + (l & 31) and K bytes [64 C + 32 h, 64 C + 32 h + 32), h = l >> 5, as two 16-byte chunks (the
+// MFMA pairs the same lanes of both operands, so only the correspondence of K positions matters).
+template <int C>
+__device__ __forceinline__ void read_frag32(const unsigned char* t, int off, int f0, int lane, u32x4 (&f)[2]) {
+  const int row = f0 + (lane & 31), sw = kmaj_swz32(row), h = lane >> 5;
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+    f[cc] = *reinterpret_cast<const u32x4*>(t + (off + row * 128 + (((4 * C + 2 * h + cc) ^ sw) * 16)));
+}
+
 // s_waitcnt vmcnt(N) only (expcnt and lgkmcnt fields at their no-wait maxima). Issued through the
 // builtin so that the compiler's own wait insertion knows which loads have completed.
 template <int N>
@@ -273,6 +289,26 @@ __device__ __forceinline__ void sched_interleave() {
 template <class E, class = void> struct IsSplitK : std::false_type {};
 template <class E> struct IsSplitK<E, std::void_t<decltype(E::kSplitK)>> : std::bool_constant<E::kSplitK> {};
 
+// The same for fewer MFMAs than reads: NV0 loads first, then NMF groups each of a share of the
+// NRD reads and NVM loads followed by one MFMA.
+template <int NMF, int NRD, int NVM, int NV0 = 0>
+__device__ __forceinline__ void sched_interleave_per_mfma() {
+  static_assert(NRD <= 3 * NMF && NVM <= 3 * NMF, "at most three reads and three loads per MFMA");
+  if constexpr (NV0 > 0) __builtin_amdgcn_sched_group_barrier(0x010, NV0, 0);
+#pragma unroll
+  for (int g = 0; g < NMF; ++g) {
+    const int nv = (g + 1) * NVM / NMF - g * NVM / NMF;
+    const int nr = (g + 1) * NRD / NMF - g * NRD / NMF;
+    if (nv == 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    else if (nv == 2) __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
+    else if (nv == 3) __builtin_amdgcn_sched_group_barrier(0x010, 3, 0);
+    if (nr == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    else if (nr == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    else if (nr == 3) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+}
+
 // C[m, n] = sum_k A(m, k) B(n, k), A(m, k) = AK ? A[m * lda + k] : A[k * lda + m] (likewise B).
 // WGM x WGN waves; wave tile (BM/WGM) x (BN/WGN) in 16 x 16 MFMA fragments. K advances KB bytes
 // per tile through an NS-stage LDS ring: tile kt + NS - 1 is in flight while tile kt is multiplied.
@@ -292,9 +328,12 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   constexpr int NIW = STAGE / 1024 / NW;                    // load instructions per wave per tile
   // register-prefetch schedule: one wave per SIMD (4 waves, 128 x 128 each), 64-byte K tiles, 3 stages
   constexpr bool RP = (NW == 4 && NS == 3 && KB == 64 && BM == 256 && BN == 256);
-  constexpr bool SP = MODE >= 1;   // split-phase K loop
+  constexpr bool SP = MODE == 1 || MODE == 2;  // split-phase K loop (bf16)
   constexpr bool IL = MODE == 2;   // ... with the reads and half the loads interleaved into the MFMAs
-  constexpr int NV0 = NIW / 2;     // loads issued together right after the barrier (IL)
+  constexpr int NV0 = NIW / 2;     // loads issued together right after the barrier (IL, SP32)
+  constexpr bool SP32 = MODE == 3; // split-phase K loop on the 32x32x64 e4m3 MFMA, interleaved
+  static_assert(!SP32 || (sizeof(ET) == 1 && NS == 2 && KB == 128 && AK && BK && FM % 2 == 0 && FN % 2 == 0),
+                "32x32 split-phase loop: e4m3, 2 stages, 128-byte K tiles, K-major operands");
   // One LDS array per stage: distinct objects let the compiler see that the direct loads into the
   // next stages do not alias the fragment reads of the current one (a single array indexed by
   // stage makes it wait for every load in flight before the first read of each tile).
@@ -334,8 +373,8 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
     else return st3;
   };
   auto issue = [&](int kt, unsigned char* sa) {
-    issue_tile<ET, AK, BM, KB, NW>(Ab, ldab, m0, M, kt, Kl, zb, sa, wave, lane);
-    issue_tile<ET, BK, BN, KB, NW>(Bb, ldbb, n0, N, kt, Kl, zb, sa + BM * KB, wave, lane);
+    issue_tile<ET, AK, BM, KB, NW, SP32>(Ab, ldab, m0, M, kt, Kl, zb, sa, wave, lane);
+    issue_tile<ET, BK, BN, KB, NW, SP32>(Bb, ldbb, n0, N, kt, Kl, zb, sa + BM * KB, wave, lane);
   };
 
   floatx4 acc[FN][FM];
@@ -343,6 +382,18 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   for (int i = 0; i < FN; ++i)
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // SP32: 32 x 32 fragments (lane l: m = l & 31 of fragment j, n = 8 q + 4 (l >> 5) + r of fragment
+  // i in element 4 q + r)
+  constexpr int FM2 = SP32 ? FM / 2 : 1, FN2 = SP32 ? FN / 2 : 1;
+  floatx16 acc32[FN2][FM2];
+  if constexpr (SP32) {
+#pragma unroll
+    for (int i = 0; i < FN2; ++i)
+#pragma unroll
+      for (int j = 0; j < FM2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc32[i][j][e] = 0.f;
+  }
 
   const int nk = (int)cdiv(Kl, KE);
   // K tile kt lives in stage kt % NS; step<S> handles the tiles with kt % NS == S. Every step
@@ -460,6 +511,66 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
       half_step(I1{}, kt + 1);
     }
     if (kt < nk) half_step(I0{}, kt);
+  } else if constexpr (SP32) {
+    // The bf16 split-phase structure with e4m3 fragments: half C of a 128-byte K tile is one 32x32x64
+    // MFMA step (64 bytes of K), so each half holds FM/2 + FN/2 fragments of 2 x 16 bytes per lane
+    // (the 16x16x128 MFMA's fragments are twice as large and do not fit double-buffered).
+    u32x4 fa[2][FM2][2], fb[2][FN2][2];
+    auto rd = [&](const unsigned char* sa, auto ci, auto hi) __attribute__((always_inline)) {
+      constexpr int C = decltype(ci)::value, H = decltype(hi)::value;
+#pragma unroll
+      for (int i = 0; i < FN2; ++i) read_frag32<C>(sa, BM * KB, wn * TN + i * 32, lane, fb[H][i]);
+#pragma unroll
+      for (int j = 0; j < FM2; ++j) read_frag32<C>(sa, 0, wm * TM + j * 32, lane, fa[H][j]);
+    };
+    auto mm = [&](auto hi) __attribute__((always_inline)) {
+      constexpr int H = decltype(hi)::value;
+#pragma unroll
+      for (int j = 0; j < FM2; ++j)
+#pragma unroll
+        for (int i = 0; i < FN2; ++i) {
+          const intx8 vb = __builtin_bit_cast(intx8, __builtin_shufflevector(fb[H][i][0], fb[H][i][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          const intx8 va = __builtin_bit_cast(intx8, __builtin_shufflevector(fa[H][j][0], fa[H][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          // format 0 = e4m3 for both operands; E8M0 block scales 127 = 2^0
+          acc32[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, va, acc32[i][j], 0, 0, 0, 0x7f7f7f7f, 0,
+                                                                         0x7f7f7f7f);
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    constexpr int NR = 2 * (FM2 + FN2);   // LDS reads per half
+    auto half_step = [&](auto si, int kt) __attribute__((always_inline)) {
+      constexpr int S = decltype(si)::value;
+      unsigned char* sa = stage(std::integral_constant<int, S>{});
+      unsigned char* sn = stage(std::integral_constant<int, S ^ 1>{});
+      wait_lgkm0();
+      __builtin_amdgcn_sched_barrier(0);
+      rd(sa, I1{}, I1{});
+      mm(I0{});
+      sched_interleave_per_mfma<FM2 * FN2, NR, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt_lgkm0<0>();              // tile kt + 1 has landed (this wave's part), tile kt is read
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      issue(min(kt + 2, nk - 1), sa);
+      rd(sn, I0{}, I0{});
+      mm(I1{});
+      sched_interleave_per_mfma<FM2 * FN2, NR, NIW - NV0, NV0>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (nk > 0) {
+      issue(0, st0);
+      issue(min(1, nk - 1), st1);
+      wait_vmcnt<NIW>();
+      asm volatile("s_barrier" ::: "memory");
+      rd(st0, I0{}, I0{});
+    }
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+      half_step(I0{}, kt);
+      half_step(I1{}, kt + 1);
+    }
+    if (kt < nk) half_step(I0{}, kt);
   } else if constexpr (!RP) {
     if (nk > 0) {
       issue(0, st0);
@@ -549,16 +660,35 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   float red_amax = 0.f;
 #pragma unroll 1
   for (int s0 = 0; s0 < BM; s0 += PR) {
+    if constexpr (SP32) {
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int rloc = wm * TM + j * 16 + r16 - s0;
-      if (rloc >= 0 && rloc < PR) {                         // uniform over each 16-row fragment
-        float* row = slab_row(rloc);
-        const int x = swz(rloc);
+      for (int j = 0; j < FM2; ++j) {
+        const int rloc = wm * TM + j * 32 + (lane & 31) - s0;
+        if (rloc >= 0 && rloc < PR) {                       // uniform over each 32-row fragment
+          float* row = slab_row(rloc);
+          const int x = swz(rloc);
 #pragma unroll
-        for (int i = 0; i < FN; ++i) {
-          const int c = ((wn * TN + i * 16) >> 2) + g;
-          *reinterpret_cast<floatx4*>(row + ((c ^ x) << 2)) = acc[i][j];
+          for (int i = 0; i < FN2; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c = ((wn * TN + i * 32 + 8 * q) >> 2) + (lane >> 5);
+              *reinterpret_cast<floatx4*>(row + ((c ^ x) << 2)) =
+                  floatx4{acc32[i][j][4 * q], acc32[i][j][4 * q + 1], acc32[i][j][4 * q + 2], acc32[i][j][4 * q + 3]};
+            }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int rloc = wm * TM + j * 16 + r16 - s0;
+        if (rloc >= 0 && rloc < PR) {                       // uniform over each 16-row fragment
+          float* row = slab_row(rloc);
+          const int x = swz(rloc);
+#pragma unroll
+          for (int i = 0; i < FN; ++i) {
+            const int c = ((wn * TN + i * 16) >> 2) + g;
+            *reinterpret_cast<floatx4*>(row + ((c ^ x) << 2)) = acc[i][j];
+          }
         }
       }
     }
@@ -852,6 +982,8 @@ inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t
 //   9 = 256 x 256, 8 waves (4 x 2), 128 B, 2, split-phase K loop with the LDS reads and half the
 //       loads interleaved into the MFMAs (bf16; e4m3 falls back to 4)
 //  10 = 256 x 256, 4 waves (2 x 2, one per SIMD), 128 B, 2, split-phase K loop (bf16; e4m3: 4)
+//  11 = 256 x 256, 8 waves (4 x 2), 128 B, 2, split-phase K loop on the 32x32x64 MFMA with reads and
+//       half the loads interleaved (e4m3; bf16 runs it as 9, fp32 as 4)
 // e4m3 needs 128-byte K tiles (32 bytes of K per lane per MFMA): 5, 6, 7 fall back to 3, 4, 1.
 // 0 = automatic (gemm_config_override()).
 template <class ET, class Epi>
@@ -862,6 +994,11 @@ inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* 
     if (cfg == 6) cfg = 4;
     if (cfg == 7) cfg = 1;
     if (cfg == 8 || cfg == 9 || cfg == 10) cfg = 4;
+    if (cfg == 11) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
+  } else if constexpr (sizeof(ET) == 2) {
+    if (cfg == 11) cfg = 9;
+  } else {
+    if (cfg == 9 || cfg == 10 || cfg == 11) cfg = 4;
   }
   switch (cfg) {
     case 1: return launch_gemm_cfg<ET, 128, 128, 2, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
@@ -902,9 +1039,10 @@ inline hipError_t launch_gemm(const ET* A, int64_t lda, const ET* B, int64_t ldb
     const double e256 = (double)t256 / (double)(cdiv(t256, 256) * 256);
     const double e128 = 0.75 * (double)t128 / (double)(cdiv(t128, 256) * 256);
     // 4 x 2 waves, except 2 x 4 when B is MN-major (measured ~3% faster there); bf16 with both
-    // operands K-major takes the split-phase K loop (measured 2-5% faster than config 4)
+    // operands K-major takes the split-phase K loop (measured 2-5% faster than config 4), e4m3 the
+    // split-phase loop on the 32x32x64 MFMA (6-9% faster than config 4 on the MLP shapes)
     const bool kk16 = sizeof(ET) == 2 && o.a_kmajor && o.b_kmajor;
-    cfg = e256 >= e128 ? (kk16 ? 9 : o.b_kmajor ? 4 : 3) : 1;
+    cfg = e256 >= e128 ? (sizeof(ET) == 1 ? 11 : kk16 ? 9 : o.b_kmajor ? 4 : 3) : 1;
   }
   return launch_gemm_with(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
 }
@@ -933,7 +1071,7 @@ inline hipError_t launch_gemm_splitk(const ET* A, int64_t lda, const ET* B, int6
   const int sl = (int)std::max<int64_t>(1, cdiv(K, kchunk));
   EpiSplitK32 e{scratch, (int64_t)N, (int64_t)M * N, kchunk};
   int cfg = gemm_config_override();
-  if (cfg == 0) cfg = sizeof(ET) == 2 && o.a_kmajor && o.b_kmajor ? 9 : o.b_kmajor ? 4 : 3;
+  if (cfg == 0) cfg = sizeof(ET) == 1 ? 11 : sizeof(ET) == 2 && o.a_kmajor && o.b_kmajor ? 9 : o.b_kmajor ? 4 : 3;
   hipError_t r = launch_gemm_with(cfg, A, lda, B, ldb, M, N, K, e, o, s);
   if (r != hipSuccess) return r;
   const int64_t work = (int64_t)M * (N / 8);
