@@ -52,7 +52,7 @@ int llt_gemm_splitk(int32_t op_dtype, int32_t a_kmajor, int32_t b_kmajor, const 
  * fragments of one half of a K tile are read while the MFMAs of the other half run, the reads and
  * half the next tile's loads interleaved with those MFMAs); 10 = split-phase with 4 waves (2 x 2),
  * reads and MFMAs in separate groups; 11 = 256 x 256, 8 waves (4 x 2), 128 B, 2, split-phase K loop
- * on the 32x32x64 e4m3 MFMA (e4m3 only; bf16 runs it as 9). e4m3 GEMMs need 128-byte K tiles and run
+ * on the 32x32 MFMAs (32x32x64 e4m3, 32x32x16 bf16; bf16 with an MN-major operand runs it as 9). e4m3 GEMMs need 128-byte K tiles and run
  * 5, 6, 7 as 3, 4, 1 and 8, 9, 10 as 4; fp32 runs 9, 10 and 11 as 4. 0 = automatic choice per GEMM shape. The LCE logits GEMM
  * always uses a 256-wide vocabulary tile (configurations 1, 7 and 8 select 9 there). */
 int llt_set_gemm_config(int32_t cfg);

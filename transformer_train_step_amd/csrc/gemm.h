@@ -331,9 +331,9 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   constexpr bool SP = MODE == 1 || MODE == 2;  // split-phase K loop (bf16)
   constexpr bool IL = MODE == 2;   // ... with the reads and half the loads interleaved into the MFMAs
   constexpr int NV0 = NIW / 2;     // loads issued together right after the barrier (IL, SP32)
-  constexpr bool SP32 = MODE == 3; // split-phase K loop on the 32x32x64 e4m3 MFMA, interleaved
-  static_assert(!SP32 || (sizeof(ET) == 1 && NS == 2 && KB == 128 && AK && BK && FM % 2 == 0 && FN % 2 == 0),
-                "32x32 split-phase loop: e4m3, 2 stages, 128-byte K tiles, K-major operands");
+  constexpr bool SP32 = MODE == 3; // split-phase K loop on the 32x32 MFMAs (x64 e4m3, x16 bf16), interleaved
+  static_assert(!SP32 || (sizeof(ET) <= 2 && NS == 2 && KB == 128 && AK && BK && FM % 2 == 0 && FN % 2 == 0),
+                "32x32 split-phase loop: e4m3 or bf16, 2 stages, 128-byte K tiles, K-major operands");
   // One LDS array per stage: distinct objects let the compiler see that the direct loads into the
   // next stages do not alias the fragment reads of the current one (a single array indexed by
   // stage makes it wait for every load in flight before the first read of each tile).
@@ -529,11 +529,19 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
       for (int j = 0; j < FM2; ++j)
 #pragma unroll
         for (int i = 0; i < FN2; ++i) {
-          const intx8 vb = __builtin_bit_cast(intx8, __builtin_shufflevector(fb[H][i][0], fb[H][i][1], 0, 1, 2, 3, 4, 5, 6, 7));
-          const intx8 va = __builtin_bit_cast(intx8, __builtin_shufflevector(fa[H][j][0], fa[H][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
-          // format 0 = e4m3 for both operands; E8M0 block scales 127 = 2^0
-          acc32[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, va, acc32[i][j], 0, 0, 0, 0x7f7f7f7f, 0,
-                                                                         0x7f7f7f7f);
+          if constexpr (sizeof(ET) == 1) {
+            const intx8 vb = __builtin_bit_cast(intx8, __builtin_shufflevector(fb[H][i][0], fb[H][i][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            const intx8 va = __builtin_bit_cast(intx8, __builtin_shufflevector(fa[H][j][0], fa[H][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            // format 0 = e4m3 for both operands; E8M0 block scales 127 = 2^0
+            acc32[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, va, acc32[i][j], 0, 0, 0, 0x7f7f7f7f, 0,
+                                                                           0x7f7f7f7f);
+          } else {
+            // two 32x32x16 steps, each on one 16-byte chunk (8 bf16 of K) per lane
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              acc32[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fb[H][i][c]),
+                                                                    __builtin_bit_cast(bf16x8_t, fa[H][j][c]), acc32[i][j], 0, 0, 0);
+          }
         }
     };
     using I0 = std::integral_constant<int, 0>;
@@ -547,7 +555,7 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
       __builtin_amdgcn_sched_barrier(0);
       rd(sa, I1{}, I1{});
       mm(I0{});
-      sched_interleave_per_mfma<FM2 * FN2, NR, 0>();
+      sched_interleave_per_mfma<FM2 * FN2 * (sizeof(ET) == 1 ? 1 : 2), NR, 0>();
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt_lgkm0<0>();              // tile kt + 1 has landed (this wave's part), tile kt is read
       asm volatile("s_barrier" ::: "memory");
@@ -555,7 +563,7 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
       issue(min(kt + 2, nk - 1), sa);
       rd(sn, I0{}, I0{});
       mm(I1{});
-      sched_interleave_per_mfma<FM2 * FN2, NR, NIW - NV0, NV0>();
+      sched_interleave_per_mfma<FM2 * FN2 * (sizeof(ET) == 1 ? 1 : 2), NR, NIW - NV0, NV0>();
       __builtin_amdgcn_sched_barrier(0);
     };
     if (nk > 0) {
@@ -946,7 +954,7 @@ inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t
   const dim3 nb((unsigned)nbt, slices);
   const ET* z = static_cast<const ET*>(o.zrow);
   constexpr int NT = 64 * WGM * WGN;
-  if constexpr (sizeof(ET) == 2) {
+  if constexpr (sizeof(ET) == 2 && MODE != 3) {   // MODE 3: K-major operands only (the callers check)
     if (!o.a_kmajor && !o.b_kmajor) {
       const char* tag = gemm_tag<ET, Epi, false, false>();
       LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, false, Epi, MODE>), nb, dim3(NT),
@@ -982,8 +990,10 @@ inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t
 //   9 = 256 x 256, 8 waves (4 x 2), 128 B, 2, split-phase K loop with the LDS reads and half the
 //       loads interleaved into the MFMAs (bf16; e4m3 falls back to 4)
 //  10 = 256 x 256, 4 waves (2 x 2, one per SIMD), 128 B, 2, split-phase K loop (bf16; e4m3: 4)
-//  11 = 256 x 256, 8 waves (4 x 2), 128 B, 2, split-phase K loop on the 32x32x64 MFMA with reads and
-//       half the loads interleaved (e4m3; bf16 runs it as 9, fp32 as 4)
+//  11 = 256 x 256, 8 waves (4 x 2), 128 B, 2, split-phase K loop on the 32x32 MFMAs (32x32x64 e4m3,
+//       32x32x16 bf16) with reads and half the loads interleaved (fp32 runs it as 4; bf16 with an
+//       MN-major operand as 9). bf16 measured ~7% slower than 9 on the loss's shapes, so only e4m3
+//       takes it automatically.
 // e4m3 needs 128-byte K tiles (32 bytes of K per lane per MFMA): 5, 6, 7 fall back to 3, 4, 1.
 // 0 = automatic (gemm_config_override()).
 template <class ET, class Epi>
@@ -996,7 +1006,10 @@ inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* 
     if (cfg == 8 || cfg == 9 || cfg == 10) cfg = 4;
     if (cfg == 11) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
   } else if constexpr (sizeof(ET) == 2) {
-    if (cfg == 11) cfg = 9;
+    if (cfg == 11) {
+      if (o.a_kmajor && o.b_kmajor) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
+      cfg = 9;
+    }
   } else {
     if (cfg == 9 || cfg == 10 || cfg == 11) cfg = 4;
   }
