@@ -345,10 +345,20 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   const int nbm = (int)cdiv(M, BM), nbn = (int)cdiv(N, BN);
   const int nb = nbm * nbn;
   int b = xcd_remap(blockIdx.x, nb);
-  // G = tile rows per L2 group: each XCD walks its share of the tiles G rows at a time
-  const int grp = b / (G * nbn), first = grp * G;
-  const int gs = min(nbm - first, G);
-  const int bm = first + (b % (G * nbn)) % gs, bn = (b % (G * nbn)) / gs;
+  // Each XCD walks its share of the tiles G tile rows at a time (G > 0), or -G tile columns at a
+  // time (G < 0)
+  int bm, bn;
+  if (G > 0) {
+    const int grp = b / (G * nbn), first = grp * G;
+    const int gs = min(nbm - first, G);
+    bm = first + (b % (G * nbn)) % gs;
+    bn = (b % (G * nbn)) / gs;
+  } else {
+    const int gc = -G, grp = b / (gc * nbm), first = grp * gc;
+    const int gs = min(nbn - first, gc);
+    bn = first + (b % (gc * nbm)) % gs;
+    bm = (b % (gc * nbm)) / gs;
+  }
   const int m0 = bm * BM, n0 = bn * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -949,10 +959,10 @@ template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, int MODE =
 inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
                                   const Epi& epi, const GemmOps& o, hipStream_t s) {
   const int64_t nbt = cdiv(M, BM) * cdiv(N, BN);
-  // Tile rows per group of the block order: 2 when the output has at least as many tile rows as tile
-  // columns, else 8 (measured on the step's shapes: 3-9% faster for the e4m3 GEMMs and the loss's
-  // dW GEMM than 8, while the logits GEMM, 5x wider than tall, prefers 8)
-  const int G = cdiv(M, BM) >= cdiv(N, BN) ? 2 : 8;
+  // Block order: along the longer side of the output, 2 tile rows (or columns) at a time (measured
+  // on the step's shapes over groups of 2, 3, 4, 8, 16 rows or columns: 3-9% faster than 8 rows for
+  // the e4m3 GEMMs and the loss's dW GEMM, 4% for the logits GEMM, 5x wider than tall)
+  const int G = cdiv(M, BM) >= cdiv(N, BN) ? 2 : -2;
   unsigned slices = 1;
   if constexpr (IsSplitK<Epi>::value) slices = (unsigned)std::max<int64_t>(1, cdiv(K, epi.kchunk));
   const dim3 nb((unsigned)nbt, slices);
