@@ -85,19 +85,21 @@ __device__ __forceinline__ uint32_t quant4(const float* x, float scale) {
   return f32x4_to_e4m3(y[0], y[1], y[2], y[3]);
 }
 
-// Cast of x [rows, cols] with the scale derived from qs->amax. Block = 64 rows x 64 cols tile,
-// 256 threads; each thread converts 16 consecutive elements of one row.
+// Cast of x [rows, cols] with the scale derived from qs->amax. Block = 128 x 128 tile, 256 threads;
+// each thread converts 16 consecutive elements of one row in each of four 32-row quarters, so that
+// both the codes and the transposed codes leave the block as whole 128-byte rows.
 //   q   [rows, ldq] (or null); qt [cols, ldqt] (or null) with ldqt >= rows_pad >= rows;
 //   the grid covers rows_pad rows so qt[:, rows:rows_pad] is zero-filled.
 // cols % 16 == 0, ld % 8 == 0, ldq % 16 == 0 (any ldqt; 16-byte stores when ldqt % 16 == 0). Block (0,0) thread 0 also writes qs->scale / qs->inv_scale.
 // RELU2: the tensor quantised is r = round(relu(x)^2), formed from x on the fly (x = the MLP's
 // pre-activation u, so r itself is never stored).
+constexpr int kCastTile = 128;
 template <class T, bool RELU2 = false>
 __global__ void __launch_bounds__(256)
 cast_e4m3_kernel(const T* __restrict__ x, int64_t rows, int cols, int64_t ld, QScale* qs,
                  uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qt, int64_t ldqt,
                  int64_t rows_pad, float* scale_out, float* inv_out) {
-  __shared__ uint32_t tile[64][17];                  // 64 rows x 64 bytes (+4 B pad per row)
+  __shared__ uint32_t tile[kCastTile][kCastTile / 4 + 1];   // 128 rows x 128 bytes (+4 B pad per row)
   float scale, inv;
   scales_from_amax(qs->amax, scale, inv);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
@@ -106,43 +108,54 @@ cast_e4m3_kernel(const T* __restrict__ x, int64_t rows, int cols, int64_t ld, QS
     if (scale_out) *scale_out = scale;
     if (inv_out) *inv_out = inv;
   }
-  const int64_t r0 = (int64_t)blockIdx.y * 64;
-  const int c0 = blockIdx.x * 64;
-  const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
-  const int64_t r = r0 + tr;
+  const int64_t r0 = (int64_t)blockIdx.y * kCastTile;
+  const int c0 = blockIdx.x * kCastTile;
+  const int tc = (threadIdx.x & 7) * 16;
   const int c = c0 + tc;
-  uint32_t w[4] = {0, 0, 0, 0};
-  if (r < rows && c < cols) {
-    float v[16];
-    Vec8<T>::load(x + r * ld + c, *reinterpret_cast<float(*)[8]>(v));
-    Vec8<T>::load(x + r * ld + c + 8, *reinterpret_cast<float(*)[8]>(v + 8));
-    if constexpr (RELU2) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float p = fmaxf(v[k], 0.f);
-        v[k] = Elem<T>::rnd(p * p);
+  for (int h = 0; h < 4; ++h) {
+    const int tr = (threadIdx.x >> 3) + 32 * h;
+    const int64_t r = r0 + tr;
+    uint32_t w[4] = {0, 0, 0, 0};
+    if (r < rows && c < cols) {
+      float v[16];
+      Vec8<T>::load(x + r * ld + c, *reinterpret_cast<float(*)[8]>(v));
+      Vec8<T>::load(x + r * ld + c + 8, *reinterpret_cast<float(*)[8]>(v + 8));
+      if constexpr (RELU2) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float p = fmaxf(v[k], 0.f);
+          v[k] = Elem<T>::rnd(p * p);
+        }
       }
-    }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = quant4(v + 4 * k, scale);
-    if (q) *reinterpret_cast<uint4*>(q + r * ldq + c) = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int k = 0; k < 4; ++k) w[k] = quant4(v + 4 * k, scale);
+      if (q) *reinterpret_cast<uint4*>(q + r * ldq + c) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    if (qt) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) tile[tr][(tc >> 2) + k] = w[k];
+    }
   }
   if (!qt) return;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) tile[tr][(tc >> 2) + k] = w[k];
   __syncthreads();
-  // transposed: thread -> output row (source column) cc = tid / 4, 16 source rows
-  const int cc = threadIdx.x >> 2, rr = (threadIdx.x & 3) * 16;
-  if (c0 + cc < cols && r0 + rr < rows_pad) {
-    const unsigned char* tb = reinterpret_cast<const unsigned char*>(&tile[0][0]);
-    uint8_t* dst = qt + (int64_t)(c0 + cc) * ldqt + r0 + rr;
-    if ((ldqt & 15) == 0 && r0 + rr + 16 <= rows_pad) {
-      uint32_t o[4] = {0, 0, 0, 0};
+  // transposed: thread -> output row (source column) cc, 16 source rows rr .. rr + 15; 8 threads
+  // write one output row's 128 bytes
+  const unsigned char* tb = reinterpret_cast<const unsigned char*>(&tile[0][0]);
+  constexpr int RB = (kCastTile / 4 + 1) * 4;               // bytes per LDS tile row
 #pragma unroll
-      for (int k = 0; k < 16; ++k) o[k >> 2] |= (uint32_t)tb[(rr + k) * 68 + cc] << (8 * (k & 3));
-      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-    } else {
-      for (int k = 0; k < 16 && r0 + rr + k < rows_pad; ++k) dst[k] = tb[(rr + k) * 68 + cc];
+  for (int h = 0; h < 4; ++h) {
+    const int cc = (threadIdx.x >> 3) + 32 * h, rr = (threadIdx.x & 7) * 16;
+    if (c0 + cc < cols && r0 + rr < rows_pad) {
+      uint8_t* dst = qt + (int64_t)(c0 + cc) * ldqt + r0 + rr;
+      if ((ldqt & 15) == 0 && r0 + rr + 16 <= rows_pad) {
+        uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < 16; ++k) o[k >> 2] |= (uint32_t)tb[(rr + k) * RB + cc] << (8 * (k & 3));
+        *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+      } else {
+        for (int k = 0; k < 16 && r0 + rr + k < rows_pad; ++k) dst[k] = tb[(rr + k) * RB + cc];
+      }
     }
   }
 }
@@ -152,8 +165,8 @@ inline hipError_t launch_cast_e4m3(const T* x, int64_t rows, int cols, int64_t l
                                    uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, int64_t rows_pad,
                                    float* scale_out, float* inv_out, hipStream_t s) {
   const int64_t rp = qt ? rows_pad : rows;
-  const int64_t gy = cdiv(std::max<int64_t>(rp, 1), 64);
-  const int gx = (int)cdiv(std::max(cols, 1), 64);
+  const int64_t gy = cdiv(std::max<int64_t>(rp, 1), kCastTile);
+  const int gx = (int)cdiv(std::max(cols, 1), kCastTile);
   LL_LAUNCH(RELU2 ? "cast_e4m3_relu2" : "cast_e4m3", (cast_e4m3_kernel<T, RELU2>), dim3(gx, (unsigned)gy), dim3(256), 0,
             s, x, rows, cols, ld, qs, q, ldq, qt, ldqt, rp, scale_out, inv_out);
   return hipGetLastError();
