@@ -8,7 +8,7 @@
 //   inv_scale = 1 / scale                         (exact)
 //   q         = e4m3fn_rne(clamp(fl32(x * scale), -448, 448))
 // The cast kernel writes the row-major codes and, optionally, the transposed codes (the K-major
-// operand of the weight-gradient GEMMs) through a 64 x 64 byte tile in LDS. The transposed
+// operand of the weight-gradient GEMMs) through a 128 x 128 byte tile in LDS. The transposed
 // buffer may have more columns than `rows` (a padded leading dimension); those are zero-filled
 // so a GEMM may run its K loop over whole 128-byte tiles.
 #pragma once
