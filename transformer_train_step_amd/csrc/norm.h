@@ -93,48 +93,60 @@ template <> struct Seg8<float> {
 // RMSNorm backward fused with the residual add (and optionally the next branch scaling):
 //   out  = round(resid + r (g d) - x r^3 mean(x g d))       (d = dL/d(normed), x = norm input;
 //                                                             resid NULL reads as 0)
-//   dg   : per-wave partial sums of d * x * r  -> dg_part[wave_global][D]
+//   dg   : per-row-group partial sums of d * x * r  -> dg_part[group][D]
 //   if bout: bout = round(a * out) and *dot += sum(out * aux)   (next residual branch)
-// Waves own whole rows, kNormBwdRowsPerWave each; a row's d, x and resid are loaded once, all
-// loads of the row issued together, and kept in their storage format.
-constexpr int kNormBwdRowsPerWave = 4;
+// A pair of waves owns a row group of kNormBwdRows consecutive rows and splits each row's columns
+// (chunk j of thread t covers columns 8 t + 1024 j .. + 7), so a thread holds NC = D / 1024 chunks
+// (3 at D = 3072: three waves per SIMD fit, where one wave per row held 6 and only one fitted).
+// The two halves of mean(x g d) meet in LDS, in a fixed order, with one barrier per row (two
+// alternating slots). A row's d, x, resid and aux are loaded once, all loads of the row issued
+// together, and kept in their storage format; g is staged in LDS once per block.
+constexpr int kNormBwdRows = 8;
+constexpr int kNormBwdCols = 1024;   // columns per pass of a wave pair (128 threads x 8)
 
-template <class T>
+template <class T, int NC>
 __global__ void __launch_bounds__(256)
 rmsnorm_bwd_kernel(const T* __restrict__ d, const T* __restrict__ x, const float* __restrict__ g,
                    const float* __restrict__ rstd, const T* __restrict__ resid, T* __restrict__ out,
                    float* __restrict__ dg_part, int64_t N, int D, const float* a, T* bout,
                    const T* aux, float* dot) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  float dga[kMaxDChunks][8];
+  __shared__ float gs[NC * kNormBwdCols];
+  __shared__ float red[2][2][2];   // [slot][pair][wave of the pair]
+  for (int c = threadIdx.x * 4; c < D; c += 256 * 4)
+    *reinterpret_cast<float4*>(gs + c) = *reinterpret_cast<const float4*>(g + c);
+  __syncthreads();
+  const int pair = threadIdx.x >> 7, half = (threadIdx.x >> 6) & 1, t = threadIdx.x & 127;
+  const int64_t grp = (int64_t)blockIdx.x * 2 + pair;
+  float dga[NC][8];
 #pragma unroll
-  for (int j = 0; j < kMaxDChunks; ++j)
+  for (int j = 0; j < NC; ++j)
 #pragma unroll
     for (int k = 0; k < 8; ++k) dga[j][k] = 0.f;
   const float av = bout ? *a : 0.f;
   float dsum = 0.f;
-  for (int i = 0; i < kNormBwdRowsPerWave; ++i) {
-    const int64_t row = wg * kNormBwdRowsPerWave + i;
-    if (row >= N) break;
-    const float r = rstd[row];
-    Seg8<T> ds[kMaxDChunks], xs[kMaxDChunks], rs[kMaxDChunks];
+  // every wave runs all kNormBwdRows iterations (the barrier inside must be reached by all)
+  for (int i = 0; i < kNormBwdRows; ++i) {
+    const int64_t row = grp * kNormBwdRows + i;
+    const bool live = row < N;
+    const float r = live ? rstd[row] : 0.f;
+    Seg8<T> ds[NC], xs[NC], rs[NC], as[NC];
 #pragma unroll
-    for (int j = 0; j < kMaxDChunks; ++j) {
-      const int c = lane * 8 + j * 512;
-      if (c < D) {
+    for (int j = 0; j < NC; ++j) {
+      const int c = t * 8 + j * kNormBwdCols;
+      if (live && c < D) {
         ds[j].load(d + row * D + c);
         xs[j].load(x + row * D + c);
         if (resid) rs[j].load(resid + row * D + c);
+        if (bout) as[j].load(aux + row * D + c);
       }
     }
     float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxDChunks; ++j) {
-      const int c = lane * 8 + j * 512;
-      if (c < D) {
+    for (int j = 0; j < NC; ++j) {
+      const int c = t * 8 + j * kNormBwdCols;
+      if (live && c < D) {
         float gv[8];
-        Vec8<float>::load(g + c, gv);
+        Vec8<float>::load(gs + c, gv);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           s += xs[j][k] * gv[k] * ds[j][k];
@@ -142,24 +154,26 @@ rmsnorm_bwd_kernel(const T* __restrict__ d, const T* __restrict__ x, const float
         }
       }
     }
-    s = group_sum<64>(s) / (float)D;
+    s = group_sum<64>(s);
+    if ((threadIdx.x & 63) == 0) red[i & 1][pair][half] = s;
+    __syncthreads();
+    s = (red[i & 1][pair][0] + red[i & 1][pair][1]) / (float)D;
     const float r3s = r * r * r * s;
 #pragma unroll
-    for (int j = 0; j < kMaxDChunks; ++j) {
-      const int c = lane * 8 + j * 512;
-      if (c < D) {
+    for (int j = 0; j < NC; ++j) {
+      const int c = t * 8 + j * kNormBwdCols;
+      if (live && c < D) {
         float gv[8], rv[8];
-        Vec8<float>::load(g + c, gv);
+        Vec8<float>::load(gs + c, gv);
 #pragma unroll
         for (int k = 0; k < 8; ++k)
           rv[k] = Elem<T>::rnd((resid ? rs[j][k] : 0.f) + (r * (gv[k] * ds[j][k]) - xs[j][k] * r3s));
         Vec8<T>::store(out + row * D + c, rv);
         if (bout) {
-          float ax[8], bv[8];
-          Vec8<T>::load(aux + row * D + c, ax);
+          float bv[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            dsum += rv[k] * ax[k];
+            dsum += rv[k] * as[j][k];
             bv[k] = av * rv[k];
           }
           Vec8<T>::store(bout + row * D + c, bv);
@@ -167,24 +181,38 @@ rmsnorm_bwd_kernel(const T* __restrict__ d, const T* __restrict__ x, const float
       }
     }
   }
+  if (grp * kNormBwdRows < N) {
 #pragma unroll
-  for (int j = 0; j < kMaxDChunks; ++j) {
-    const int c = lane * 8 + j * 512;
-    if (c < D) Vec8<float>::store(dg_part + wg * D + c, dga[j]);
+    for (int j = 0; j < NC; ++j) {
+      const int c = t * 8 + j * kNormBwdCols;
+      if (c < D) Vec8<float>::store(dg_part + grp * D + c, dga[j]);
+    }
   }
   if (bout) block_atomic_add(dot, dsum);
 }
 
-inline int64_t rmsnorm_bwd_partials(int64_t N) { return cdiv(cdiv(N, kNormBwdRowsPerWave), 4) * 4; }
+// row groups (dg_part rows) for N rows: whole blocks of two groups; groups past the last row leave
+// their dg_part row unwritten, so the count used by the column sum covers written rows only
+inline int64_t rmsnorm_bwd_partials(int64_t N) { return cdiv(N, kNormBwdRows); }
 
 template <class T>
 inline hipError_t launch_rmsnorm_bwd(const T* d, const T* x, const float* g, const float* rstd,
                                      const T* resid, T* out, float* dg_part, int64_t N, int D,
                                      const float* a, T* bout, const T* aux, float* dot, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  const int64_t blocks = cdiv(cdiv(N, kNormBwdRowsPerWave), 4);
-  LL_LAUNCH("rmsnorm_bwd", (rmsnorm_bwd_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, s, d, x, g, rstd, resid,
-                     out, dg_part, N, D, a, bout, aux, dot);
+  const int64_t blocks = cdiv(cdiv(N, kNormBwdRows), 2);
+  // instantiated per count of 1024-column chunks so that the register arrays hold only the
+  // chunks D has
+  switch (cdiv(D, kNormBwdCols)) {
+#define LL_NORM_BWD_NC(nc)                                                                              \
+  case nc:                                                                                              \
+    LL_LAUNCH("rmsnorm_bwd", (rmsnorm_bwd_kernel<T, nc>), dim3((unsigned)blocks), dim3(256), 0, s, d, x, g, rstd, \
+              resid, out, dg_part, N, D, a, bout, aux, dot);                                            \
+    break;
+    LL_NORM_BWD_NC(1) LL_NORM_BWD_NC(2) LL_NORM_BWD_NC(3) LL_NORM_BWD_NC(4)
+#undef LL_NORM_BWD_NC
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
