@@ -13,27 +13,32 @@ constexpr int kMaxDChunks = 8;   // D <= 8 * 512 = 4096 (one wave covers 512 col
 
 // y = round(x * r * g), r = 1 / sqrt(mean(x^2) + eps); one wave per row, kNormFwdRows rows per
 // block; optional amax of y. The row is loaded once into registers (every 16-byte load of the row
-// issued before the first use).
+// issued before the first use); g is staged in LDS once per block. Instantiated per count NC of
+// 512-column chunks, so the row registers hold only the chunks D has.
 constexpr int kNormFwdRows = 16;
-template <class T>
+template <class T, int NC>
 __global__ void __launch_bounds__(256)
 rmsnorm_fwd_kernel(const T* __restrict__ x, const float* __restrict__ g, T* __restrict__ y,
                    float* __restrict__ rstd, int64_t N, int D, float eps, float* amax) {
+  __shared__ float gs[NC * 512];
+  for (int c = threadIdx.x * 4; c < D; c += 256 * 4)
+    *reinterpret_cast<float4*>(gs + c) = *reinterpret_cast<const float4*>(g + c);
+  __syncthreads();
   const int lane = threadIdx.x & 63;
   float mx = 0.f;
   for (int i = threadIdx.x >> 6; i < kNormFwdRows; i += 4) {
     const int64_t row = (int64_t)blockIdx.x * kNormFwdRows + i;
     if (row >= N) break;
     const T* xr = x + row * D;
-    float v[kMaxDChunks][8];
+    float v[NC][8];
 #pragma unroll
-    for (int j = 0; j < kMaxDChunks; ++j) {
+    for (int j = 0; j < NC; ++j) {
       const int c = lane * 8 + j * 512;
       if (c < D) Vec8<T>::load(xr + c, v[j]);
     }
     float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxDChunks; ++j)
+    for (int j = 0; j < NC; ++j)
       if (lane * 8 + j * 512 < D)
 #pragma unroll
         for (int k = 0; k < 8; ++k) ss += v[j][k] * v[j][k];
@@ -41,11 +46,11 @@ rmsnorm_fwd_kernel(const T* __restrict__ x, const float* __restrict__ g, T* __re
     const float r = 1.0f / sqrtf(ss / (float)D + eps);
     if (lane == 0) rstd[row] = r;
 #pragma unroll
-    for (int j = 0; j < kMaxDChunks; ++j) {
+    for (int j = 0; j < NC; ++j) {
       const int c = lane * 8 + j * 512;
       if (c < D) {
         float gv[8];
-        Vec8<float>::load(g + c, gv);
+        Vec8<float>::load(gs + c, gv);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           v[j][k] = Elem<T>::rnd(v[j][k] * r * gv[k]);
@@ -62,8 +67,17 @@ template <class T>
 inline hipError_t launch_rmsnorm_fwd(const T* x, const float* g, T* y, float* rstd, int64_t N, int D,
                                      float eps, float* amax, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  LL_LAUNCH("rmsnorm_fwd", (rmsnorm_fwd_kernel<T>), dim3((unsigned)cdiv(N, kNormFwdRows)), dim3(256), 0, s, x, g, y,
-            rstd, N, D, eps, amax);
+  const dim3 grid((unsigned)cdiv(N, kNormFwdRows));
+  switch (cdiv(D, 512)) {
+#define LL_NORM_FWD_NC(nc)                                                                              \
+  case nc:                                                                                              \
+    LL_LAUNCH("rmsnorm_fwd", (rmsnorm_fwd_kernel<T, nc>), grid, dim3(256), 0, s, x, g, y, rstd, N, D, eps, amax); \
+    break;
+    LL_NORM_FWD_NC(1) LL_NORM_FWD_NC(2) LL_NORM_FWD_NC(3) LL_NORM_FWD_NC(4)
+    LL_NORM_FWD_NC(5) LL_NORM_FWD_NC(6) LL_NORM_FWD_NC(7) LL_NORM_FWD_NC(8)
+#undef LL_NORM_FWD_NC
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
