@@ -57,7 +57,8 @@ def test_embedding_scatter_add(dtype):
     assert_close(host(dE), ref, 1e-6, "scatter", elem_rtol=1e-5)
 
 
-@pytest.mark.parametrize("dtype,n,d", [("fp32", 37, 256), ("bf16", 301, 3072), ("bf16", 1, 8), ("fp32", 130, 4096)])
+@pytest.mark.parametrize("dtype,n,d", [("fp32", 37, 256), ("bf16", 301, 3072), ("bf16", 1, 8), ("fp32", 130, 4096),
+                                         ("bf16", 77, 1536), ("fp32", 20, 2056)])
 def test_rmsnorm_fwd_bwd(dtype, n, d):
     need_gpu()
     print(f"rmsnorm {dtype} {n}x{d}", flush=True)
