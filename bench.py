@@ -43,10 +43,10 @@ SOURCES = ("transformer_train_step_amd/csrc/gemm.h", "transformer_train_step_amd
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated (valid while the sources
 # hash to sha256_16; otherwise the roofline reports traffic null)
 TRAFFIC = {
-    "gemm_bf16_acc32_kk": {"sources": SOURCES, "sha256_16": "88750ccf4a91e1c3", "read_bytes": 6.8566e+09,
-                           "write_bytes": 5.4593e+08,
+    "gemm_bf16_acc32_kk": {"sources": SOURCES, "sha256_16": "43150f6ace8d2cb7", "read_bytes": 6.8564e+09,
+                           "write_bytes": 5.4590e+08,
                            "profile": "profiles/gemm_bf16_acc32_kk_hbm_bytes_layer_lce_40x1024.md"},
-    "gemm_bf16_lce_logits_kk": {"sources": SOURCES, "sha256_16": "88750ccf4a91e1c3", "read_bytes": 8.0783e+09,
+    "gemm_bf16_lce_logits_kk": {"sources": SOURCES, "sha256_16": "43150f6ace8d2cb7", "read_bytes": 8.0510e+09,
                                 "write_bytes": 1.0837e+09,
                                 "profile": "profiles/gemm_bf16_lce_logits_kk_hbm_bytes_layer_lce_40x1024.md"},
 }

@@ -82,20 +82,34 @@ lce_lse_kernel(const float* __restrict__ part, int nparts, const T* __restrict__
                float* __restrict__ lse_chunk, float* __restrict__ loss_acc) {
   __shared__ float red[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  static_assert(kLseRows % 4 == 0 && kLseRows / 4 <= 64, "rows per wave");
+  // lane k < kLseRows / 4 fetches the target and its capped logit of the wave's k-th row up front
+  // (one round trip for all of them instead of two per row)
+  int32_t tk = ignore;
+  float ck = 0.f;
+  if (lane < kLseRows / 4) {
+    const int row = blockIdx.x * kLseRows + wave + 4 * lane;
+    if (row < rows) {
+      tk = y[row];
+      if (tk != ignore) ck = softcap_tanh(Elem<T>::ld(z, (int64_t)row * ldz + tk), softcap, 1.f / softcap);
+    }
+  }
   float acc = 0.f;
-  for (int i = wave; i < kLseRows; i += 4) {
-    const int row = blockIdx.x * kLseRows + i;
+#pragma unroll
+  for (int k = 0; k < kLseRows / 4; ++k) {
+    const int row = blockIdx.x * kLseRows + wave + 4 * k;
     if (row >= rows) break;
     const float* pr = part + (int64_t)row * nparts;
     float S = 0.f;
     for (int t = lane; t < nparts; t += 64) S += pr[t];
     S = group_sum<64>(S);
     const float l = __logf(S);
+    const int32_t t = __shfl(tk, k, 64);
+    const float c = __shfl(ck, k, 64);
     if (lane == 0) {
       lse_chunk[row] = l;
       if (lse_out) lse_out[row] = l;
-      const int32_t t = y[row];
-      if (t != ignore) acc += l - softcap_tanh(Elem<T>::ld(z, (int64_t)row * ldz + t), softcap, 1.f / softcap);
+      if (t != ignore) acc += l - c;
     }
   }
   if (lane == 0) red[wave] = acc;
