@@ -8,6 +8,7 @@ import pytest
 import torch
 
 from oracle import numerics as nu
+from tests import torch_fp8
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -103,13 +104,8 @@ def test_quantizer_golden_example():
 
 
 def _torch_quant(x32: np.ndarray):
-    t = torch.from_numpy(x32)
-    amax = t.abs().max()
-    ratio = torch.tensor(448.0, dtype=torch.float32) / torch.clamp(amax, min=torch.tensor(1e-12, dtype=torch.float32))
-    _, e = torch.frexp(ratio)
-    scale = torch.ldexp(torch.tensor(1.0), e - 1)
-    q = (t * scale).clamp(-448, 448).to(torch.float8_e4m3fn)
-    return q, scale.item(), (1.0 / scale).item()
+    q, inv = torch_fp8.quant(torch.from_numpy(x32))
+    return q, 1.0 / inv, inv
 
 
 @pytest.mark.parametrize("std", [1.0, 0.02, 1e-4, 30.0])
@@ -150,3 +146,18 @@ def test_fp8_gemm_matches_torch_scaled_mm():
     ref = torch._scaled_mm(qa, qb.t(), scale_a=torch.tensor(tia), scale_b=torch.tensor(tib),
                            out_dtype=torch.float32).double().numpy()
     np.testing.assert_allclose(ours, ref, rtol=1e-5, atol=1e-6 * np.abs(ref).max())
+
+
+def test_scale_matches_search_over_amax_sweep():
+    """The oracle's scale against the largest power of two below 448 / amax found by search, over
+    amax values at, just below and just above binade edges, the 1e-12 floor and beyond."""
+    am = [0.0, 1e-30, 1e-12, 1.5e-12, 448.0, 448.0 * 2 ** -20, 3.0e38]
+    for k in range(-40, 41):
+        edge = 448.0 * 2.0 ** k                   # 448 / amax is a power of two exactly here
+        am += [edge, float(np.nextafter(np.float32(edge), np.float32(0))),
+               float(np.nextafter(np.float32(edge), np.float32(np.inf))), 0.7 * edge]
+    for a in am:
+        a32 = float(np.float32(a))
+        _, _, scale, inv = nu.quantize_tensorwise(np.array([a32, -a32 / 2]))
+        assert scale == torch_fp8.search_scale(a32), a32
+        assert inv * scale == 1.0
