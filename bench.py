@@ -8,7 +8,8 @@ layer backward from that gradient. Every kernel is libll's (HIP, gfx950); inputs
 HBM before the timed region. Prints one JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload layer_lce|layer|layer_ve_2k|lce|model] [--no-cpu-baseline]
+                    [--workload layer_lce|layer|layer_ve_2k|lce|model|train|muon] [--no-cpu-baseline]
+                    [--lce-chunk TOKENS] [--lce-vocab-tile 128|256] [--sweep-lce]
 
 FLOP accounting (algorithmic, not executed work): per token of one layer, fwd + bwd,
 6 * P_mm + 6 * Hq * Dh * (T + 1) with P_mm = 100,663,296 matrix weights (causal attention counted
@@ -95,17 +96,36 @@ WORKLOADS = {
                   desc="full 3.848B model fwd+bwd (token embedding 50304x3072, 28 decoder layers with value "
                        "embeddings on the 14 even layers, FP8 e4m3 MLPs, final RMSNorm, untied head + fused "
                        "linear cross-entropy softcap 15; 40x1024 tokens)"),
+    "train": dict(batch=40, seq=1024, ve=True, layer=True, lce=True, layers=28, accum=7,
+                  desc="one optimizer step of the full 3.848B model on one GPU: 7 accumulated micro-batches of "
+                       "40x1024 tokens through the whole model (as 'model'), then Muon (5 Newton-Schulz steps) on "
+                       "the 112 layer matrices and AdamW on the embedding, head, 14 value-embedding tables, gains "
+                       "and residual scalars; bf16 master weights and optimizer state"),
+    "muon": dict(batch=0, seq=0, ve=False, layer=False, lce=False, muon=True,
+                 desc="Muon step (momentum, 5 Newton-Schulz steps on bf16 MFMA, update) of one decoder layer's "
+                      "four matrices: W_qkv 5120x3072, W_o 3072x3072, W_fc 12288x3072, W_proj 3072x12288"),
 }
+MUON_SHAPES = ((HQ + 2 * HKV) * DH, D), (D, HQ * DH), (F, D), (D, F)
+
+
+def muon_flops(rows: int, cols: int, steps: int = 5) -> int:
+    """Newton-Schulz GEMM work on the wide orientation [m, n]: X X^T, A A, B X per step."""
+    m, n = min(rows, cols), max(rows, cols)
+    return steps * (2 * m * m * n + 2 * m * m * m + 2 * m * m * n)
 
 
 def step_flops(w: dict) -> int:
+    """Algorithmic FLOPs of one step: layers and loss (the optimizer is not counted, as on the pages;
+    the Muon workload counts its Newton-Schulz GEMMs)."""
+    if w.get("muon"):
+        return sum(muon_flops(r, c) for r, c in MUON_SHAPES)
     n = w["batch"] * w["seq"]
     f = 0
     if w["layer"]:
         f += w.get("layers", 1) * layer_flops_per_token(w["seq"]) * n
     if w["lce"]:
         f += lce_flops(n)
-    return f
+    return f * w.get("accum", 1)
 
 
 def cpu_baseline(seq: int, ve: bool, with_layer: bool, with_lce: bool, layers: int = 1) -> dict:
@@ -161,6 +181,10 @@ def main():
                     help="print every traced kernel (ms per step, launches, TFLOP/s of its algorithmic work)")
     ap.add_argument("--lce-chunk", type=int, default=10240, metavar="TOKENS",
                     help="tokens per chunk of the fused linear cross-entropy (logits of one chunk are stored)")
+    ap.add_argument("--lce-vocab-tile", type=int, default=256, choices=(128, 256),
+                    help="vocabulary columns per partial row sum (the logits GEMM's N tile)")
+    ap.add_argument("--sweep-lce", action="store_true",
+                    help="also time the loss alone over token_chunk x vocab_tile (reported as lce_sweep)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, copy a MIB-MiB device buffer once (a plain copy of known size, "
                          "the reference for HBM byte counters)")
@@ -199,11 +223,13 @@ def main():
         log(f"[bench] calibration copy of {n} bytes done")
         del src, dst
     t_in = time.perf_counter()
-    if args.workload == "model":
+    if args.workload in ("model", "train"):
         step, n_launch_trace = model_step(w, dev, torch, synth, LayerConfig, Model, args.lce_chunk)
+    elif args.workload == "muon":
+        step, n_launch_trace = muon_step(dev, torch, L)
     else:
         step, n_launch_trace = layer_lce_step(w, dev, torch, synth, LayerConfig, Layer, FusedLCE, to_dev,
-                                              args.lce_chunk)
+                                              args.lce_chunk, args.lce_vocab_tile)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in HBM ({time.perf_counter() - t_in:.1f} s to generate)")
 
@@ -228,7 +254,7 @@ def main():
     report(args, w, ms, step, stream, ev0, ev1, L, n_launch_trace)
 
 
-def layer_lce_step(w, dev, torch, synth, LayerConfig, Layer, FusedLCE, to_dev, lce_chunk):
+def layer_lce_step(w, dev, torch, synth, LayerConfig, Layer, FusedLCE, to_dev, lce_chunk, vocab_tile=256):
     """Inputs and the step closure of the layer / loss workloads (inputs drawn by synth)."""
     B, T = w["batch"], w["seq"]
     N = B * T
@@ -255,7 +281,7 @@ def layer_lce_step(w, dev, torch, synth, LayerConfig, Layer, FusedLCE, to_dev, l
     if w["lce"]:
         w_head = to_dev(synth.normal((V, D), 0.02, 0, synth.K_WHEAD, "bf16"))
         targets = torch.from_numpy(synth.uniform_ints((N,), V_REAL, 0, synth.K_TARGETS)).to(dev)
-        lce = FusedLCE("bf16", N, D, V, token_chunk=lce_chunk, device=dev)
+        lce = FusedLCE("bf16", N, D, V, token_chunk=lce_chunk, vocab_tile=vocab_tile, device=dev)
         dh_buf = torch.empty_like(x)
         dw_head = torch.empty_like(w_head)
     del inp
@@ -300,11 +326,24 @@ def model_step(w, dev, torch, synth, LayerConfig, Model, lce_chunk):
         layers.append(lp)
     params = {"embed": rn(V, D), "layers": layers, "final_norm_w": torch.ones(D, device=dev), "head": rn(V, D)}
     model = Model(LayerConfig(batch=B, seq=T), n_layers, V, token_chunk=lce_chunk, device=dev)
-    grads = model.new_grads(params)
-    ids = torch.from_numpy(synth.uniform_ints((N,), V_REAL, 0, synth.K_IDS)).to(dev)
-    targets = torch.from_numpy(synth.uniform_ints((N,), V_REAL, 0, synth.K_TARGETS)).to(dev)
+    accum = w.get("accum", 0)
+    if accum:
+        from transformer_train_step_amd.ops import TrainStep
+        ts = TrainStep(model, params, accum=accum)
+        batches = [(torch.from_numpy(synth.uniform_ints((N,), V_REAL, k, synth.K_IDS)).to(dev),
+                    torch.from_numpy(synth.uniform_ints((N,), V_REAL, k, synth.K_TARGETS)).to(dev))
+                   for k in range(accum)]
+    else:
+        grads = model.new_grads(params)
+        ids = torch.from_numpy(synth.uniform_ints((N,), V_REAL, 0, synth.K_IDS)).to(dev)
+        targets = torch.from_numpy(synth.uniform_ints((N,), V_REAL, 0, synth.K_TARGETS)).to(dev)
     log(f"[bench] model buffers: saved {model.saved_bytes / 2**30:.1f} GiB, workspace "
         f"{model.ws_bytes / 2**30:.1f} GiB, device memory in use {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+
+    if accum:
+        def step():
+            ts(batches)
+        return step, 32768
 
     def step():
         model(params, ids, targets, grads)
@@ -312,19 +351,41 @@ def model_step(w, dev, torch, synth, LayerConfig, Model, lce_chunk):
     return step, 16384
 
 
+def muon_step(dev, torch, L):
+    """Muon on one layer's four matrices (weights N(0, 0.02), gradients N(0, 1e-3), bf16)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    mats = []
+    for r, c in MUON_SHAPES:
+        w = torch.empty((r, c), device=dev).normal_(0, 0.02, generator=gen).to(torch.bfloat16)
+        g = torch.empty((r, c), device=dev).normal_(0, 1e-3, generator=gen).to(torch.bfloat16)
+        mats.append((w, g, torch.zeros_like(w)))
+    wsb = max(L.ll_muon_workspace_bytes(r, c) for r, c in MUON_SHAPES)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def step():
+        for w, g, b in mats:
+            L.ll_muon_step(L.LL_BF16, w, g, b, w.shape[0], w.shape[1], 0.02, 0.95, 1, 0.0, 5, ws, wsb)
+
+    return step, 4096
+
+
 def report(args, w, ms, step, stream, ev0, ev1, L, n_launch_trace):
     import torch
     B, T = w["batch"], w["seq"]
-    N = B * T
+    N = B * T * w.get("accum", 1)
     flops = step_flops(w)
     tok_s = N / (ms * 1e-3)
+    value, unit = round(tok_s, 1), "tokens/s"
+    if w.get("muon"):
+        value, unit = round(1e3 / ms, 3), "Muon steps/s (one layer's four matrices)"
     out = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16+e4m3",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, uniform token ids)",
         "config": {"workload": w["desc"], "tokens_per_step": N, "batch": B, "seq_len": T,
-                   "lce_token_chunk": args.lce_chunk},
+                   "lce_token_chunk": args.lce_chunk, "lce_vocab_tile": args.lce_vocab_tile},
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
         "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / PEAK_BF16, 2),
         "algorithmic_flops_per_step": flops,
@@ -373,12 +434,45 @@ def report(args, w, ms, step, stream, ev0, ev1, L, n_launch_trace):
                 tf = f"{v['flops'] / (v['ms'] * 1e-3) / 1e12:8.1f} TFLOP/s" if v["flops"] and v["ms"] > 0 else ""
                 log(f"[bench]   {k:40s} {v['ms'] / tsteps:8.3f} ms/step {v['launches'] / tsteps:6.1f} launches {tf}")
 
-    if not args.no_cpu_baseline:
+    if args.sweep_lce:
+        out["lce_sweep"] = lce_sweep(args, torch)
+    if not args.no_cpu_baseline and not w.get("muon") and not w.get("accum"):
         log("[bench] timing the oracle on the host (bounded sample)...")
         seq = T if w["layer"] else 1024
         out["cpu_baseline"] = cpu_baseline(seq, w["ve"], w["layer"], w["lce"], w.get("layers", 1))
         log(f"[bench] oracle: {out['cpu_baseline']['value']} tokens/s on {out['cpu_baseline']['cores']} threads")
     print(json.dumps(out), flush=True)
+
+
+def lce_sweep(args, torch):
+    """The loss alone (40960 x 3072 @ 50304 x 3072, bf16) timed per token_chunk x vocab_tile."""
+    import synth
+    from transformer_train_step_amd.ops import FusedLCE
+    n = 40960
+    h = torch.empty((n, D), device="cuda").normal_(0, 1, generator=torch.Generator(device="cuda").manual_seed(1))
+    h = h.to(torch.bfloat16)
+    wt = torch.empty((V, D), device="cuda").normal_(0, 0.02, generator=torch.Generator(device="cuda").manual_seed(2))
+    wt = wt.to(torch.bfloat16)
+    y = torch.from_numpy(synth.uniform_ints((n,), V_REAL, 0, synth.K_TARGETS)).cuda()
+    dh, dw = torch.empty_like(h), torch.empty_like(wt)
+    res = []
+    for chunk in (4096, 8192, 10240, 20480):
+        for tile in (128, 256):
+            lce = FusedLCE("bf16", n, D, V, token_chunk=chunk, vocab_tile=tile)
+            lce(h, wt, y, d_hidden=dh, d_weight=dw)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                lce(h, wt, y, d_hidden=dh, d_weight=dw)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 3
+            res.append({"token_chunk": chunk, "vocab_tile": tile, "ms": round(ms, 3),
+                        "pct_bf16_peak": round(100 * lce_flops(n) / (ms * 1e-3) / PEAK_BF16, 2)})
+            log(f"[bench] lce sweep chunk {chunk} tile {tile}: {ms:.3f} ms")
+            del lce
+    return res
 
 
 if __name__ == "__main__":

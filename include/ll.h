@@ -20,8 +20,11 @@
  *   - Every call validates its arguments before enqueuing anything and returns an ll_status.
  *     A failed validation enqueues nothing. A launch failure returns LL_ERR_HIP; the HIP error
  *     text is then in ll_last_error().
- *   - Values that are not finite in the inputs, or token ids / targets out of range, give
- *     unspecified results (they are not checked on the device).
+ *   - Values that are not finite in the inputs give non-finite or unspecified results (the e4m3
+ *     quantiser turns a NaN into the NaN code 0x7F so that it reaches the FP8 GEMMs). Token ids
+ *     outside [0, rows of their table) select nothing: the embedding and value-embedding gathers
+ *     add zero rows and their gradient scatters skip them. Targets outside [0, v) other than
+ *     ignore_index give unspecified results (they are not checked on the device).
  *   - Calls that share a workspace, `saved` buffer or output on one stream run in order; the
  *     caller must not run two calls that share such memory on different streams at once.
  */
@@ -74,8 +77,15 @@ typedef struct {
   const float* resid_mlp;    /* device fp32 scalar a_mlp:   y = h + a_mlp * MLP branch */
 } ll_layer_params;
 
-/* Gradients of one layer. Matrices are written (overwritten) in cfg.dtype; gains and scalars are
- * written in fp32; ve_table is ACCUMULATED into (fp32, the caller zeroes it once per step). */
+/* Gradients of one layer. Matrices are written in cfg.dtype; gains, scalars and the
+ * value-embedding table in fp32 (the table's gradient is a scatter-add of the rows the token ids
+ * pick).
+ * accumulate = 0: every gradient is overwritten (the table is zeroed, then scattered into);
+ * accumulate = 1: every gradient is added to what the buffers hold (gradient accumulation over the
+ * micro-batches of one optimizer step [youdonthavefriends cost analysis, "config appendix": 7
+ * accumulation steps of 20 x 2048 tokens per GPU]): each matrix element is rounded once,
+ * round(old + new), in cfg.dtype (bf16 master weights carry bf16 gradients [linlog.top article,
+ * 吞吐量优化: bf16 主权重]). */
 typedef struct {
   void* attn_norm_w;   /* fp32 [D] */
   void* w_qkv;
@@ -86,6 +96,7 @@ typedef struct {
   float* ve_table;     /* fp32 [ve_rows, Hkv * Dh] or NULL */
   float* resid_attn;   /* fp32 scalar */
   float* resid_mlp;    /* fp32 scalar */
+  int32_t accumulate;  /* 0: overwrite, 1: add into the existing gradients */
 } ll_layer_grads;
 
 /* Bytes of the opaque `saved` buffer that ll_layer_fwd fills and ll_layer_bwd reads, and of the
@@ -117,19 +128,24 @@ int ll_layer_bwd(const ll_layer_cfg* cfg, const ll_layer_params* p, const void* 
                  void* dx, const ll_layer_grads* g, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes of ll_fused_lce_fwd_bwd for these sizes (0 if invalid). */
-size_t ll_fused_lce_workspace_bytes(int32_t dtype, int64_t n, int32_t d, int64_t v, int64_t token_chunk);
+size_t ll_fused_lce_workspace_bytes(int32_t dtype, int64_t n, int32_t d, int64_t v, int64_t token_chunk,
+                                    int32_t vocab_tile);
 
 /* Fused linear cross-entropy with tanh logit softcap [youdonthavefriends cost analysis,
  * "Increasing throughput" and "config appendix"; hn.213312.xyz translation, 提升吞吐量: the LM
  * head matmul is chunked inside the loss and the (n, v) logits are never materialised]:
  *   z = hidden weight^T, c = softcap tanh(z / softcap), lse_i = log sum_j exp(c_ij),
+ *   softcap in (0, 60] (the row sums of exp(c) keep no running maximum: |c| <= softcap bounds them),
  *   loss = mean over rows with targets_i != ignore_index of (lse_i - c_{i, targets_i}),
  *   dz = grad_scale / n_valid (softmax(c) - onehot) (1 - (c / softcap)^2),
  *   d_hidden = dz weight, d_weight = dz^T hidden.
  *   dtype: LL_F32 or LL_BF16 for hidden, weight, d_hidden, d_weight.
  *   hidden [n, d], weight [v, d] (all v rows take part in the softmax, padded rows included),
  *   targets int32 [n] in [0, v) or == ignore_index.  token_chunk: rows per chunk (memory of the
- *   per-chunk logits is token_chunk * v * 2 bytes (bf16) of ws); 0 picks 10240. With several
+ *   per-chunk logits is token_chunk * v * 2 bytes (bf16) of ws); 0 picks 10240.
+ *   vocab_tile: vocabulary columns per partial row sum of exp(c), the N tile of the logits GEMM:
+ *   128 or 256 (0 picks 256).  accumulate_dw: 0 overwrites d_weight, 1 adds into it (one rounding
+ *   of old + new; gradient accumulation over micro-batches). With several
  *   chunks d_weight is accumulated in an fp32 buffer of ws and rounded once at the end; when one
  *   chunk holds all n rows the whole contraction is rounded straight into d_weight. With
  *   gradients, ws also holds one transposed copy of weight ([d, v rounded up to 64]).
@@ -138,9 +154,9 @@ size_t ll_fused_lce_workspace_bytes(int32_t dtype, int64_t n, int32_t d, int64_t
  *   Requires d % 64 == 0 (bf16) / d % 32 == 0 (fp32), v % 8 == 0. */
 int ll_fused_lce_fwd_bwd(int32_t dtype, const void* hidden, const void* weight,
                          const int32_t* targets, int64_t n, int32_t d, int64_t v, float softcap,
-                         int32_t ignore_index, float grad_scale, int64_t token_chunk, float* loss,
-                         float* lse, void* d_hidden, void* d_weight, void* ws, size_t ws_bytes,
-                         void* stream);
+                         int32_t ignore_index, float grad_scale, int64_t token_chunk, int32_t vocab_tile,
+                         int32_t accumulate_dw, float* loss, float* lse, void* d_hidden, void* d_weight,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /* Parameters of the whole model (read only). */
 typedef struct {
@@ -153,11 +169,14 @@ typedef struct {
 
 /* Gradients of the whole model. */
 typedef struct {
-  float* embed;                    /* fp32 [vocab, D], ACCUMULATED into (the caller zeroes it) */
+  float* embed;                    /* fp32 [vocab, D] (zeroed, then scattered into; added into with
+                                      accumulate) */
   const ll_layer_grads* layers;    /* host array [n_layers], as for ll_layer_bwd (ve_table non-NULL exactly
                                       on the value-embedding layers) */
-  float* final_norm_w;             /* fp32 [D], written */
-  void* head;                      /* [vocab, D] in cfg.dtype, written */
+  float* final_norm_w;             /* fp32 [D], written (added into with accumulate) */
+  void* head;                      /* [vocab, D] in cfg.dtype, written (added into with accumulate) */
+  int32_t accumulate;              /* 0: overwrite, 1: add into every gradient (the layers' own
+                                      accumulate fields are ignored) */
 } ll_model_grads;
 
 /* Bytes of the `saved` buffer (activations of every layer) and of the workspace of
@@ -177,14 +196,50 @@ size_t ll_model_workspace_bytes(const ll_layer_cfg* cfg, int32_t n_layers, int64
  *   loss, dhn, d_head = ll_fused_lce_fwd_bwd(hn, head, targets, softcap, ignore_index,
  *   grad_scale, token_chunk);
  * then the backward chain: final-norm backward, ll_layer_bwd from the last layer to the first,
- * and d_embed[token_ids[n]] += dL/dx_0[n] in fp32. token_ids must lie in [0, vocab) (the
- * value-embedding layers index their tables with them unchecked); targets follow
- * ll_fused_lce_fwd_bwd. token_ids, targets: int32 [cfg.batch * cfg.seq] device arrays; loss:
+ * and d_embed[token_ids[n]] += dL/dx_0[n] in fp32. token ids outside [0, vocab) select zero rows
+ * (embedding and value embeddings) and receive no gradient; targets follow ll_fused_lce_fwd_bwd. token_ids, targets: int32 [cfg.batch * cfg.seq] device arrays; loss:
  * device fp32 scalar. */
 int ll_model_fwd_bwd(const ll_layer_cfg* cfg, int32_t n_layers, int64_t vocab, const ll_model_params* p,
                      const int32_t* token_ids, const int32_t* targets, float softcap, int32_t ignore_index,
                      float grad_scale, int64_t token_chunk, float* loss, const ll_model_grads* g, void* saved,
                      size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- optimizer step
+ * The training run's optimizer [youdonthavefriends cost analysis, "config appendix": matrix
+ * parameters take Muon (lr 0.02, momentum 0.95, weight decay 0), the embeddings, LM head,
+ * value-embedding tables and scalars take AdamW with per-group lr, betas (0.8, 0.995 | 0.96 |
+ * 0.95), eps 1e-10 and weight decay; linlog.top article, 吞吐量优化: bf16 master weights, so the
+ * parameters and the optimizer state beside them are bf16]. Both calls update in place. */
+
+/* Workspace bytes of ll_muon_step for a [rows, cols] matrix (0 if invalid): rows * cols bf16 for
+ * the momentum output, 2 min(rows, cols) max(rows, cols) bf16 for the iterates and
+ * 2 min(rows, cols)^2 bf16 for the Gram matrices. */
+size_t ll_muon_workspace_bytes(int64_t rows, int64_t cols);
+
+/* One Muon step of a matrix parameter w [rows, cols] (bf16, row-major) with gradient grad and
+ * momentum buffer momentum_buf (both bf16 [rows, cols]):
+ *   buf = round(momentum buf + grad);  u = round(grad + momentum buf) if nesterov, else buf;
+ *   X_0 = round(u / (||u||_F + 1e-7)), transposed when rows > cols (X is [min, max]);
+ *   ns_steps times: A = round(X X^T);  B = round(b A + c A A);  X = round(a X + B X),
+ *   (a, b, c) = (3.4445, -4.7750, 2.0315): the quintic Newton-Schulz orthogonalisation published
+ *   with Muon (K. Jordan, "Muon: An optimizer for hidden layers in neural networks", 2024; the
+ *   pages name Muon but not its constants), 5 steps in the published recipe;
+ *   w = round(w (1 - lr weight_decay) - lr sqrt(max(1, rows / cols)) X), X back in w's orientation.
+ * dtype must be LL_BF16; rows and cols multiples of 64 (<= 65536). The GEMMs run on bf16 MFMA with
+ * fp32 accumulation; every stored iterate is rounded to bf16 once. */
+int ll_muon_step(int32_t dtype, void* w, const void* grad, void* momentum_buf, int64_t rows, int64_t cols,
+                 float lr, float momentum, int32_t nesterov, float weight_decay, int32_t ns_steps, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/* One AdamW step of n parameters (decoupled weight decay, bias-corrected moments, as torch.optim.AdamW):
+ *   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
+ *   p = p (1 - lr weight_decay) - lr (m / (1 - b1^step)) / (sqrt(v / (1 - b2^step)) + eps),
+ * step = 1 for the first update. param, exp_avg and exp_avg_sq are in param_dtype (LL_BF16 for bf16
+ * master weights, each rounded once where stored, or LL_F32), grad in grad_dtype. No alignment
+ * beyond 16 bytes and any n >= 0. */
+int ll_adamw_step(int32_t param_dtype, int32_t grad_dtype, void* param, const void* grad, void* exp_avg,
+                  void* exp_avg_sq, int64_t n, float lr, float beta1, float beta2, float eps, float weight_decay,
+                  int64_t step, void* stream);
 
 /* Workspace bytes of ll_fp8_quant_tensorwise (a few bytes for the amax). */
 size_t ll_fp8_quant_workspace_bytes(void);

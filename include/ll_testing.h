@@ -10,6 +10,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ll.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -92,6 +94,24 @@ int llt_trace_begin(int32_t capacity);
 int llt_trace_end(void);
 int32_t llt_trace_count(void);
 int llt_trace_get(int32_t i, const char** tag, float* ms, int64_t* mnk);
+/* For a GEMM launch i of the trace: the block configuration that ran (the numbers of
+ * llt_set_gemm_config, after the per-type fallbacks) and the number of K slices of its grid (1 for
+ * an unsplit GEMM); both 0 for launches that are not GEMMs. */
+int llt_trace_get_gemm(int32_t i, int32_t* gemm_cfg, int32_t* slices);
+
+/* Where the layer keeps one of its intermediate tensors, so that a test can read it back: the
+ * byte offset and size of sub-buffer `name` inside the `saved` buffer (region 0), the forward
+ * workspace (region 1) or the backward workspace (region 2) of ll_layer_fwd / ll_layer_bwd for
+ * this cfg. Host-side layout arithmetic only (no device access).
+ *   saved:    "qs" (4 x {amax, scale, inv_scale, pad} fp32: hn, w_fc, r, w_proj), "xn", "qkv", "qh",
+ *             "kh", "o", "lse", "attn_out", "h", "u", "m", "r1", "r2", "hn8", "hn8t", "r8t", "w18",
+ *             "w18t", "w28", "w28t" (e4m3 codes, *t = transposed with the token axis padded to
+ *             a multiple of 128 and zero-filled);
+ *   fwd ws:   "hn" (bf16 input of the hn quantiser), "r8" (codes of r);
+ *   bwd ws:   "qs" (2 x {amax, scale, inv_scale, pad}: dm, du), "dm", "du" (bf16 inputs of their
+ *             quantisers), "dm8", "dm8t", "du8", "du8t", "dhn", "dh", "dattn", "dout", "dqkv", "dxn".
+ * Returns LL_ERR_INVALID_ARG for an invalid cfg or a name the configuration does not hold. */
+int llt_layer_buffer(const ll_layer_cfg* cfg, int32_t region, const char* name, size_t* offset, size_t* bytes);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from .lce import lce_fwd_bwd
-from .model import LayerDims, LayerParams, layer_bwd, layer_fwd, rmsnorm, rmsnorm_bwd, rounder
+from .model import (LayerDims, LayerParams, gather_rows, layer_bwd, layer_fwd, rmsnorm, rmsnorm_bwd, rounder,
+                    scatter_rows)
 
 
 @dataclass
@@ -38,15 +39,13 @@ class ModelParams:
 
 
 def embedding(table, ids):
-    """x[n] = table[ids[n]]."""
-    return np.asarray(table, np.float64)[np.asarray(ids, np.int64)]
+    """x[n] = table[ids[n]] (a zero row for an id outside the table)."""
+    return gather_rows(table, ids)
 
 
 def embedding_bwd(dx, ids, rows):
-    """dE[v] = sum over n with ids[n] = v of dx[n]."""
-    dE = np.zeros((rows, np.shape(dx)[1]), np.float64)
-    np.add.at(dE, np.asarray(ids, np.int64), np.asarray(dx, np.float64))
-    return dE
+    """dE[v] = sum over n with ids[n] = v of dx[n] (ids outside the table add nothing)."""
+    return scatter_rows(dx, ids, rows)
 
 
 def model_fwd_bwd(p: ModelParams, ids, targets, d: LayerDims, softcap=15.0, ignore_index=-100,

@@ -200,6 +200,28 @@ def mlp_bwd(dm, c, w_fc, w_proj, fp8: bool, R):
 
 
 # ----------------------------------------------------------------------------------------------
+# table rows picked by token ids (value embeddings; the model's token embedding)
+# ----------------------------------------------------------------------------------------------
+def gather_rows(table, ids):
+    """out[n] = table[ids[n]]; an id outside [0, rows) picks a zero row (the library's contract for
+    ids it cannot look up; the pages only ever index in range)."""
+    table = np.asarray(table, np.float64)
+    ids = np.asarray(ids, np.int64)
+    ok = (ids >= 0) & (ids < table.shape[0])
+    return np.where(ok[:, None], table[np.where(ok, ids, 0)], 0.0)
+
+
+def scatter_rows(d, ids, rows):
+    """dT[v] = sum of d[n] over the n with ids[n] = v (ids outside [0, rows) add nothing)."""
+    d = np.asarray(d, np.float64)
+    ids = np.asarray(ids, np.int64)
+    ok = (ids >= 0) & (ids < rows)
+    out = np.zeros((rows, d.shape[1]), np.float64)
+    np.add.at(out, ids[ok], d[ok])
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
 # the layer
 # ----------------------------------------------------------------------------------------------
 @dataclass
@@ -254,7 +276,7 @@ def layer_fwd(p: LayerParams, x, ids, d: LayerDims):
     k = qkv[:, Hq * Dh:(Hq + Hkv) * Dh].reshape(B, T, Hkv, Dh)
     v = qkv[:, (Hq + Hkv) * Dh:]
     if p.ve_table is not None:
-        v = R(v + p.ve_table[np.asarray(ids)])
+        v = R(v + gather_rows(p.ve_table, ids))
     v = v.reshape(B, T, Hkv, Dh)
     cos, sin = rope_angles(T, Dh, d.rope_theta)
     qt, rq = qk_norm(q, d.rms_eps)
@@ -299,9 +321,7 @@ def layer_bwd(p: LayerParams, c: dict, dy, d: LayerDims):
     dq = R(qk_norm_bwd(rope_transpose(dqh, c["cos"], c["sin"]), c["q"], c["rq"]))
     dk = R(qk_norm_bwd(rope_transpose(dkh, c["cos"], c["sin"]), c["k"], c["rk"]))
     if p.ve_table is not None:
-        dve = np.zeros(p.ve_table.shape, np.float64)
-        np.add.at(dve, np.asarray(c["ids"]), dv)
-        g["ve_table"] = dve
+        g["ve_table"] = scatter_rows(dv, c["ids"], p.ve_table.shape[0])
     else:
         g["ve_table"] = None
     dqkv = np.concatenate([dq.reshape(N, -1), dk.reshape(N, -1), dv], axis=1)

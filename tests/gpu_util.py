@@ -38,8 +38,30 @@ def rel_err(a, b) -> float:
     return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
 
 
-def assert_close(got, ref, rtol, name="", elem_rtol=None):
-    """Norm-wise relative error <= rtol, and elementwise |got - ref| <= k*rtol*(|ref| + rms(ref))."""
+def error_stats(got, ref) -> dict:
+    """Norm-wise relative error; the largest elementwise |got - ref| / (|ref| + rms(ref)) and its
+    99.99th percentile; and (2-D arrays) the largest row-wise relative error, each row's norm
+    floored at a quarter of the median row norm."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref)) if ref.size else 0.0
+    ratio = np.abs(got - ref) / (np.abs(ref) + rms) if ref.size else np.zeros(1)
+    out = {"norm": rel_err(got, ref), "elem_max": float(np.max(ratio)),
+           "elem_p9999": float(np.quantile(ratio, 0.9999))}
+    if ref.ndim == 2 and ref.shape[0] > 1:
+        rn = np.linalg.norm(ref, axis=1)
+        den = np.maximum(rn, 0.25 * np.median(rn))
+        den[den == 0] = 1.0
+        row = np.linalg.norm(got - ref, axis=1) / den
+        out["row_max"] = float(np.max(row))
+        out["row_argmax"] = int(np.argmax(row))
+    return out
+
+
+def assert_close(got, ref, rtol, name="", elem_rtol=None, row_rtol=None):
+    """Norm-wise relative error <= rtol; elementwise |got - ref| <= elem_rtol * (|ref| + rms(ref))
+    (default 10 rtol); for 2-D arrays with row_rtol, every row's relative error <= row_rtol (the row
+    norm floored at a quarter of the median row norm), so that one wrong row or tile fails."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -52,3 +74,7 @@ def assert_close(got, ref, rtol, name="", elem_rtol=None):
     assert not np.any(bad), (f"{name}: {int(bad.sum())} elements beyond {k:.1e} x (|ref| + rms); "
                              f"first at {np.argwhere(bad)[0]}: got {got[tuple(np.argwhere(bad)[0])]}, "
                              f"ref {ref[tuple(np.argwhere(bad)[0])]}")
+    if row_rtol is not None and ref.ndim == 2 and ref.shape[0] > 1:
+        st = error_stats(got, ref)
+        assert st["row_max"] <= row_rtol, (f"{name}: row {st['row_argmax']} relative error "
+                                           f"{st['row_max']:.3e} > {row_rtol:.1e}")

@@ -94,18 +94,26 @@ def test_lce_validation():
     keep, p = _fake()
     f = lambda **kw: ll.ll_fused_lce_fwd_bwd(**{**dict(dtype=1, hidden=p, weight=p, targets=p, n=16, d=3072,
                                                          v=50304, softcap=15.0, ignore_index=-100, grad_scale=1.0,
-                                                         token_chunk=0, loss=p, lse=None, d_hidden=p, d_weight=p,
+                                                         token_chunk=0, vocab_tile=0, accumulate_dw=0, loss=p,
+                                                         lse=None, d_hidden=p, d_weight=p,
                                                          ws=p, ws_bytes=1 << 20, stream=0,
                                                          raise_on_error=False), **kw})
     assert f(d=100) == L.LL_ERR_UNSUPPORTED
     assert f(v=50301) == L.LL_ERR_UNSUPPORTED
     assert f(softcap=0.0) == L.LL_ERR_INVALID_ARG
+    assert f(softcap=61.0) == L.LL_ERR_INVALID_ARG and "softcap" in ll.ll_last_error()
+    assert f(vocab_tile=64) == L.LL_ERR_UNSUPPORTED
+    assert f(accumulate_dw=2) == L.LL_ERR_INVALID_ARG
     assert f(d_weight=None) == L.LL_ERR_INVALID_ARG
     assert f(loss=None) == L.LL_ERR_INVALID_ARG
     assert f() == L.LL_ERR_WORKSPACE
     need = ll.ll_fused_lce_workspace_bytes(1, 40960, 3072, 50304, 8192)
     assert 1e9 < need < 5e9
+    # 128-wide vocabulary tiles: twice the partial row sums
+    n128 = ll.ll_fused_lce_workspace_bytes(1, 40960, 3072, 50304, 8192, 128)
+    assert n128 - need == (8192 * 393 - 8192 * 197) * 4
     assert ll.ll_fused_lce_workspace_bytes(9, 1, 64, 8, 0) == 0
+    assert ll.ll_fused_lce_workspace_bytes(1, 1, 64, 8, 0, 192) == 0
 
 
 def test_flop_accounting_reproduces_pages_b200_rate():

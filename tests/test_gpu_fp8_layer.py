@@ -1,0 +1,202 @@
+"""The FP8 decoder layer against the oracle at sizes that take the production launch paths, and the
+layer's own e4m3 quantisation state checked bit for bit.
+
+At 4 x 1024 tokens (and 2 x 2048 on a value-embedding layer) every e4m3 GEMM of the MLP runs the
+block configuration the 40 x 1024 benchmark runs (configuration 11: 256 x 256 tiles, split-phase K
+loop on the 32x32x64 MFMA) with its fused epilogues (relu^2 + amax, residual, relu^2 backward),
+the two FP8 weight gradients split along the tokens in 4 slices, and the bf16 O-projection weight
+gradient split in 7 slices; the tests assert this from the launch trace. y, dx, every weight
+gradient and the value-embedding gradient are compared with the float64 oracle on the same inputs.
+
+Bit-exact: the scale, inverse scale and amax of all six quantised tensors (hn, W1, r, W2, dm, du)
+and all of their codes (row-major and transposed, the transposed token axis padded with zero
+codes), each against oracle.numerics.quantize_tensorwise applied to that quantiser's own input as
+the GPU formed it (hn, dm and du read back from the layer's buffers; r formed from the stored u).
+The FP8 weights are quantised from the same bf16 inputs on both sides.
+
+Tolerances are derived in the module's comments below from the measured error distribution."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import transformer_train_step_amd as ll
+from oracle import model as om
+from oracle import numerics as nu
+from tests.gpu_util import assert_close, error_stats, need_gpu
+from tests.layer_cases import GPU_NAME, config_of, device_params
+from transformer_train_step_amd.ops import Layer
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+CASES = {"4x1024": (4, 1024, False, 41), "2x2048_ve": (2, 2048, True, 42)}
+RTOL = 2e-2
+# Elementwise and row bounds (|got - ref| <= ELEM x (|ref| + rms), row error <= ROW), from the
+# measured distribution with a margin of ~2x: one e4m3 code step moves an operand by 1/16 to 1/8,
+# and the codes that flip between the two sides (their inputs differ at fp32-vs-float64 rounding)
+# move single outputs by up to ~10% of (|ref| + rms) (y at 4 x 1024: largest 0.103, 99.99th
+# percentile 0.053; rows: largest 0.030).
+# The value-embedding rows hold single tokens' dv, whose elements carry the FP8 noise of dh
+# unaveraged (largest 0.29 at 2 x 2048; its rows within 0.013).
+ELEM = {"y": 0.2, "dx": 0.2, "ve_table": 0.6}
+ELEM_GRAD = 0.25
+ROW = 0.08
+
+
+def _bytes(t: torch.Tensor, region_off_bytes) -> np.ndarray:
+    off, nb = region_off_bytes
+    return t[off:off + nb].cpu().numpy()
+
+
+def _view(t: torch.Tensor, ob, dtype, shape):
+    a = _bytes(t, ob)
+    if dtype == "bf16":
+        return (a.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(shape)
+    return a.view(dtype).reshape(shape)
+
+
+@functools.lru_cache(maxsize=None)
+def run_case(key):
+    B, T, ve, seed = CASES[key]
+    s = synth.LayerShape(batch=B, seq=T, fp8_mlp=True, value_embed=ve)
+    inp = synth.layer_inputs(s, seed=seed, perturb=True)
+    cfg = config_of(s)
+    c = cfg.c_struct()
+    layer = Layer(cfg)
+    p = device_params(inp)
+    x = torch.from_numpy(inp.x).to(torch.bfloat16).cuda()
+    ids = torch.from_numpy(inp.ids).cuda()
+    dy = torch.from_numpy(inp.dy).to(torch.bfloat16).cuda()
+    N, D, F = s.tokens, s.d_model, s.d_ff
+    Np = -(-N // 128) * 128
+    print(f"fp8 layer {key}: GPU forward", flush=True)
+    ll._lib.llt_trace_begin(4096)
+    y = layer.forward(p, x, ids)
+    torch.cuda.synchronize()
+    st = {}
+    # forward-workspace intermediates, before the backward reuses the workspace
+    st["hn"] = _view(layer.ws, ll._lib.llt_layer_buffer(c, 1, "hn"), "bf16", (N, D))
+    st["r8"] = _view(layer.ws, ll._lib.llt_layer_buffer(c, 1, "r8"), np.uint8, (N, F))
+    print(f"fp8 layer {key}: GPU backward", flush=True)
+    dx, g = layer.backward(p, x, ids, dy)
+    torch.cuda.synchronize()
+    ll._lib.llt_trace_end()
+    launches = []
+    for i in range(ll._lib.llt_trace_count()):
+        tag, _, mnk = ll._lib.llt_trace_get(i)
+        launches.append((tag, mnk) + ll._lib.llt_trace_get_gemm(i))
+    sv = lambda name, dt, shape: _view(layer.saved, ll._lib.llt_layer_buffer(c, 0, name), dt, shape)
+    bw = lambda name, dt, shape: _view(layer.ws, ll._lib.llt_layer_buffer(c, 2, name), dt, shape)
+    st["qs_fwd"] = sv("qs", np.float32, (4, 4))
+    st["qs_bwd"] = bw("qs", np.float32, (2, 4))
+    for k, shape in (("hn8", (N, D)), ("hn8t", (D, Np)), ("r8t", (F, Np)), ("w18", (F, D)), ("w18t", (D, F)),
+                     ("w28", (D, F)), ("w28t", (F, D))):
+        st[k] = sv(k, np.uint8, shape)
+    st["u"] = sv("u", "bf16", (N, F))
+    for k, shape in (("dm8", (N, D)), ("dm8t", (D, Np)), ("du8", (N, F)), ("du8t", (F, Np))):
+        st[k] = bw(k, np.uint8, shape)
+    st["dm"] = bw("dm", "bf16", (N, D))
+    st["du"] = bw("du", "bf16", (N, F))
+    host = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+    gpu = {"y": host(y), "dx": host(dx)}
+    for k in ("w_qkv", "w_o", "w_fc", "w_proj", "g_attn", "g_mlp", "a_attn", "a_mlp", "ve_table"):
+        name = GPU_NAME.get(k, k)
+        if name in g:
+            gpu[k] = float(g[name].item()) if k in ("a_attn", "a_mlp") else host(g[name])
+    print(f"fp8 layer {key}: oracle", flush=True)
+    prm, dims = om.params_from_inputs(inp), om.dims_from_shape(s)
+    yo, cache = om.layer_fwd(prm, inp.x, inp.ids, dims)
+    go = om.layer_bwd(prm, cache, inp.dy, dims)
+    ref = {"y": yo, "dx": go["dx"], "hn": cache["hn"],
+           "scale_a_mlp": float(np.linalg.norm(inp.dy) * np.linalg.norm(cache["m"])),
+           "scale_a_attn": float(np.linalg.norm(go["dh"]) * np.linalg.norm(cache["attn_out"]))}
+    for k in ("w_qkv", "w_o", "w_fc", "w_proj", "g_attn", "g_mlp", "a_attn", "a_mlp", "ve_table"):
+        if go.get(k) is not None:
+            ref[k] = go[k]
+    return s, inp, gpu, ref, st, launches
+
+
+@pytest.mark.parametrize("key", sorted(CASES))
+def test_fp8_layer_takes_the_production_paths(key):
+    need_gpu()
+    s, _, _, _, _, launches = run_case(key)
+    D, F, QD = s.d_model, s.d_ff, s.n_q_heads * s.head_dim
+    e4 = [l for l in launches if l[0].startswith("gemm_e4m3")]
+    assert len(e4) == 6, [l[0] for l in e4]
+    # every e4m3 GEMM on the 32x32x64 split-phase loop (configuration 11)
+    assert all(l[2] == 11 for l in e4), [(l[0], l[2]) for l in e4]
+    tags = {l[0] for l in e4}
+    assert {"gemm_e4m3_relu2_kk", "gemm_e4m3_residual_kk", "gemm_e4m3_relu2_bwd_kk", "gemm_e4m3_store_kk",
+            "gemm_e4m3_splitk_kk"} == tags, tags
+    split8 = sorted((l[1][0], l[1][1], l[3]) for l in e4 if l[0] == "gemm_e4m3_splitk_kk")
+    assert split8 == sorted([(D, F, 4), (F, D, 4)]), split8
+    wo = [l for l in launches if l[0].startswith("gemm_bf16_splitk") and l[1][:2] == (D, QD)]
+    assert len(wo) == 1 and wo[0][3] == 7, wo
+    assert sum(l[0] == "splitk_reduce" for l in launches) == 3
+
+
+@pytest.mark.parametrize("key", sorted(CASES))
+def test_fp8_layer_vs_oracle(key):
+    need_gpu()
+    _, inp, gpu, ref, _, _ = run_case(key)
+    pairs = {}
+    for k in ("y", "dx", "w_qkv", "w_o", "w_fc", "w_proj", "g_attn", "g_mlp", "ve_table", "a_attn", "a_mlp"):
+        if k not in ref:
+            continue
+        if isinstance(ref[k], float):
+            scale = ref["scale_" + k]
+            print(k, gpu[k], ref[k], "bound", 2 * RTOL * scale, flush=True)
+            assert abs(gpu[k] - ref[k]) <= 2 * RTOL * scale, (k, gpu[k], ref[k], scale)
+            continue
+        got, want = gpu[k], ref[k]
+        if k == "ve_table":
+            rows = np.unique(inp.ids)
+            untouched = np.ones(want.shape[0], bool)
+            untouched[rows] = False
+            assert not np.any(got[untouched]), "value-embedding rows without a token were written"
+            got, want = got[rows], want[rows]
+        pairs[k] = (got, want)
+        print(k, {a: (round(b, 5) if isinstance(b, float) else b) for a, b in error_stats(got, want).items()},
+              flush=True)
+    for k, (got, want) in pairs.items():
+        assert_close(got, want, RTOL, k, elem_rtol=ELEM.get(k, ELEM_GRAD), row_rtol=ROW)
+
+
+def _check_quant(x, codes, codes_t, qs_row, name, n_pad=None):
+    """codes (and codes_t, the transpose with a zero-padded token axis) and qs_row
+    (amax, scale, inv_scale) against the oracle quantiser of x."""
+    oc, _, scale, inv = nu.quantize_tensorwise(x)
+    assert np.float32(qs_row[0]) == np.float32(np.max(np.abs(x))), (name, "amax", qs_row[0])
+    assert np.float32(qs_row[1]) == np.float32(scale), (name, "scale", qs_row[1], scale)
+    assert np.float32(qs_row[2]) == np.float32(inv), (name, "inv_scale", qs_row[2], inv)
+    if codes is not None:
+        bad = int(np.sum(codes != oc))
+        assert bad == 0, f"{name}: {bad} codes differ"
+    if codes_t is not None:
+        n = oc.shape[0]
+        assert np.array_equal(codes_t[:, :n], oc.T), f"{name}: transposed codes differ"
+        assert not np.any(codes_t[:, n:]), f"{name}: transposed padding not zero"
+
+
+@pytest.mark.parametrize("key", sorted(CASES))
+def test_fp8_layer_quantisation_state_bitexact(key):
+    need_gpu()
+    s, inp, _, ref, st, _ = run_case(key)
+    qf, qb = st["qs_fwd"], st["qs_bwd"]
+    # weights: identical bf16 inputs on both sides
+    _check_quant(inp.w_fc.astype(np.float64), st["w18"], None, qf[1], "W1")
+    oc, _, _, _ = nu.quantize_tensorwise(inp.w_fc.astype(np.float64))
+    assert np.array_equal(st["w18t"], oc.T)
+    _check_quant(inp.w_proj.astype(np.float64), st["w28"], None, qf[3], "W2")
+    oc, _, _, _ = nu.quantize_tensorwise(inp.w_proj.astype(np.float64))
+    assert np.array_equal(st["w28t"], oc.T)
+    # activations and gradients: each quantiser's own input as the GPU formed it
+    _check_quant(st["hn"], st["hn8"], st["hn8t"], qf[0], "hn")
+    r = nu.bf16_round(np.maximum(st["u"], 0.0) ** 2)
+    _check_quant(r, st["r8"], st["r8t"], qf[2], "r")
+    _check_quant(st["dm"], st["dm8"], st["dm8t"], qb[0], "dm")
+    _check_quant(st["du"], st["du8"], st["du8t"], qb[1], "du")
+    # and those inputs themselves agree with the oracle's at the bf16 parity bar
+    assert_close(st["hn"], ref["hn"], RTOL, "hn", elem_rtol=ELEM_GRAD, row_rtol=ROW)

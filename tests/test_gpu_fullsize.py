@@ -9,10 +9,12 @@ oracle can compute piece by piece:
   tensorwise FP8 scales depend on every token). The FP8 layer at the same size is compared with
   the bf16 layer (property: FP8 noise only);
 * the value-embedding layer at 20 x 2048 tokens on a sampled sequence;
-* the fused linear cross-entropy at 40960 x 3072 @ 50304 x 3072, chunk 10240: lse and dH of
-  sampled rows from the oracle's row-wise definition, the loss from the GPU lse and the oracle's
-  target logits, sampled rows of dW from their definition.
-Weight gradients of the layer sum over all 40 sequences and are checked at the smaller sizes."""
+* the fused linear cross-entropy at 40960 x 3072 @ 50304 x 3072, chunk 10240: lse of every row and
+  the loss from the oracle run over all rows in chunks, dH of sampled rows, sampled rows of dW
+  from the oracle's dz of every token on those vocabulary columns.
+Weight gradients of the layer sum over all 40 sequences; the FP8 layer, with every weight gradient,
+is compared with the oracle at 4 x 1024 and 2 x 2048 tokens (tests/test_gpu_fp8_layer.py), sizes
+that run the same launch configurations as this one."""
 import numpy as np
 import pytest
 import torch
@@ -104,8 +106,9 @@ def test_layer_full_size_sampled_sequences(shape, seqs):
     T = shape.seq
     for b, (yr, dxr) in ref.items():
         r = slice(b * T, (b + 1) * T)
-        assert_close(host(y[r]), yr, 2e-2, f"y[seq {b}]", elem_rtol=0.5)
-        assert_close(host(dx[r]), dxr, 2e-2, f"dx[seq {b}]", elem_rtol=0.5)
+        # bf16 MLP: measured elementwise <= 0.027 of (|ref| + rms), rows <= 0.006, norm-wise 3.4e-3
+        assert_close(host(y[r]), yr, 2e-2, f"y[seq {b}]", elem_rtol=0.06, row_rtol=0.015)
+        assert_close(host(dx[r]), dxr, 2e-2, f"dx[seq {b}]", elem_rtol=0.06, row_rtol=0.015)
 
 
 def test_layer_full_size_fp8_vs_bf16():
@@ -126,6 +129,8 @@ def test_layer_full_size_fp8_vs_bf16():
 
 
 def test_lce_full_size_sampled():
+    """The loss at its full size: lse of every row, the loss and sampled rows of dW from the oracle
+    run chunk by chunk over all 40960 rows (float64), dH on sampled rows."""
     need_gpu()
     print("lce full size 40960x3072 @ 50304x3072 chunk 10240", flush=True)
     n, d, v = synth.LCE_TOKENS, synth.LCE_DIM, synth.LCE_VOCAB
@@ -134,23 +139,33 @@ def test_lce_full_size_sampled():
     lse = torch.empty(n, dtype=torch.float32, device="cuda")
     loss, dh, dw = FusedLCE("bf16", n, d, v, token_chunk=10240)(H, W, y, lse=lse)
     torch.cuda.synchronize()
-    lse_g, dh_g = host(lse), host(dh)
+    lse_g, dh_g, dw_g = host(lse), host(dh), host(dw)
+    del dh, dw, H, W
+    torch.cuda.empty_cache()
     h64, w64 = li.hidden.astype(np.float64), li.weight.astype(np.float64)
-    rows = np.sort(synth.rng(35, 9).choice(n, 48, replace=False))
-    # sampled rows from the row-wise definition (the oracle on those rows; mean over all n rows)
-    o = olce.lce_fwd_bwd(h64[rows], w64, li.targets[rows], softcap=15.0, mode="bf16", grad_scale=len(rows) / n)
-    assert_close(lse_g[rows], o["lse"], 1e-6, "lse rows")
-    assert_close(dh_g[rows], o["dh"], 2e-2, "dH rows", elem_rtol=0.5)
-    # loss = mean(lse - c_target): GPU lse (checked above on samples) and the oracle's target logits
-    zt = nu.bf16_round(np.einsum("nd,nd->n", h64, w64[li.targets]))
-    ref_loss = float(np.mean(lse_g - 15.0 * np.tanh(zt / 15.0)))
-    assert abs(loss.item() - ref_loss) <= 1e-5 * abs(ref_loss), (loss.item(), ref_loss)
-    # sampled rows of dW = dz^T H from their definition, dz from the GPU lse
     vs = np.sort(synth.rng(35, 10).choice(v, 6, replace=False))
-    z = nu.bf16_round(h64 @ w64[vs].T)                              # [n, 6]
-    c = 15.0 * np.tanh(z / 15.0)
-    p = np.exp(c - lse_g[:, None])
-    p[li.targets[:, None] == vs[None, :]] -= 1.0
-    dz = nu.bf16_round(p * (1.0 - (c / 15.0) ** 2) / n)
-    dw_ref = nu.bf16_round(dz.T @ h64)
-    assert_close(host(dw)[vs], dw_ref, 2e-2, "dW rows", elem_rtol=0.5)
+    # the oracle over every row, 2048 rows at a time: lse, the loss terms, and dz on the sampled
+    # vocabulary columns (for dW = dz^T H on those rows)
+    lse_o = np.empty(n)
+    loss_terms = 0.0
+    dz_vs = np.empty((n, len(vs)))
+    for r0 in range(0, n, 2048):
+        r = slice(r0, min(n, r0 + 2048))
+        o = olce.lce_fwd_bwd(h64[r], w64, li.targets[r], softcap=15.0, mode="bf16", need_grads=False)
+        lse_o[r] = o["lse"]
+        loss_terms += o["loss"] * o["n_valid"]
+        z = nu.bf16_round(h64[r] @ w64[vs].T)
+        c = 15.0 * np.tanh(z / 15.0)
+        p = np.exp(c - o["lse"][:, None])
+        p[li.targets[r][:, None] == vs[None, :]] -= 1.0
+        dz_vs[r] = nu.bf16_round(p * (1.0 - (c / 15.0) ** 2) / n)
+        print(f"  oracle rows {r0}..{r.stop}", flush=True)
+    assert_close(lse_g, lse_o, 1e-6, "lse (every row)", elem_rtol=1e-5)
+    ref_loss = loss_terms / n
+    assert abs(loss.item() - ref_loss) <= 1e-5 * abs(ref_loss), (loss.item(), ref_loss)
+    dw_ref = nu.bf16_round(dz_vs.T @ h64)
+    # measured at 300 rows: elementwise <= 0.007 of (|ref| + rms), rows <= 0.007
+    assert_close(dw_g[vs], dw_ref, 2e-2, "dW rows", elem_rtol=0.03, row_rtol=0.02)
+    rows = np.sort(synth.rng(35, 9).choice(n, 48, replace=False))
+    o = olce.lce_fwd_bwd(h64[rows], w64, li.targets[rows], softcap=15.0, mode="bf16", grad_scale=len(rows) / n)
+    assert_close(dh_g[rows], o["dh"], 2e-2, "dH rows", elem_rtol=0.03, row_rtol=0.02)

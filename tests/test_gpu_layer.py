@@ -12,6 +12,7 @@ import torch
 
 import synth
 from oracle import lce as olce
+from oracle import numerics as nu
 from tests.gpu_util import assert_close, need_gpu
 from tests.layer_cases import GRAD_KEYS, run_gpu, run_oracle
 from transformer_train_step_amd.ops import FusedLCE
@@ -19,24 +20,37 @@ from transformer_train_step_amd.ops import FusedLCE
 pytestmark = pytest.mark.gpu
 
 
-def _compare(gpu, ref, rtol, elem_rtol):
+# Elementwise and row bounds of the bf16 / FP8 layer cases (|got - ref| <= elem (|ref| + rms), each
+# row's relative error <= row), about twice the largest values measured on MI355X over these cases:
+#   bf16 MLP: every output within 0.047 elementwise, rows within 0.009 (norm-wise <= 5e-3);
+#   FP8 MLP: y, dx and the attention-side gradients within 0.10, rows 0.03; the MLP weight
+#   gradients, sums over only 192-400 tokens of products of e4m3 codes of which a few flip between
+#   the two sides, within 0.26, rows 0.073; the value-embedding rows (single tokens' dv) within 0.15.
+BARS_BF16 = {"*": (0.1, 0.03)}
+BARS_FP8 = {"*": (0.2, 0.08), "w_fc": (0.5, 0.15), "w_proj": (0.5, 0.15), "ve_table": (0.6, 0.05)}
+
+
+def _compare(gpu, ref, rtol, elem_rtol, bars=None):
     for k in ("y", "dx") + GRAD_KEYS + ("d_head",):
         if k not in ref:
             continue
+        row_rtol = None
+        if bars is not None:
+            elem_rtol, row_rtol = bars.get(k, bars["*"])
         if k == "ve_table":
             # sparse: only rows named by the token ids receive gradient; the rest stay exactly 0
             rows = np.unique(gpu["ids"])
             untouched = np.ones(ref[k].shape[0], bool)
             untouched[rows] = False
             assert not np.any(gpu[k][untouched]), "value-embedding rows without a token were written"
-            assert_close(gpu[k][rows], ref[k][rows], rtol, k, elem_rtol=elem_rtol)
+            assert_close(gpu[k][rows], ref[k][rows], rtol, k, elem_rtol=elem_rtol, row_rtol=row_rtol)
         elif isinstance(ref[k], float):
             # a_attn = sum(dh * attn_out), a_mlp = sum(dy * m) cancel heavily; their error is bounded
             # by |d(a)| <= |da|.|b| + |a|.|db| <= 2 rtol |a||b| when a, b agree to rtol norm-wise
             scale = ref["scale_" + k]
             assert abs(gpu[k] - ref[k]) <= 2 * rtol * scale, (k, gpu[k], ref[k], scale)
         else:
-            assert_close(gpu[k], ref[k], rtol, k, elem_rtol=elem_rtol)
+            assert_close(gpu[k], ref[k], rtol, k, elem_rtol=elem_rtol, row_rtol=row_rtol)
     if "loss" in ref:
         assert abs(gpu["loss"] - ref["loss"]) <= rtol * abs(ref["loss"]), (gpu["loss"], ref["loss"])
 
@@ -68,7 +82,7 @@ def test_layer_bf16_real_dims(batch, seq, fp8, ve, seed):
     print(f"layer bf16 B={batch} T={seq} fp8={fp8} ve={ve}", flush=True)
     gpu = run_gpu(inp)
     ref = run_oracle(inp)
-    _compare(gpu, ref, 2e-2, 0.5)
+    _compare(gpu, ref, 2e-2, None, BARS_FP8 if fp8 else BARS_BF16)
 
 
 def test_tiny_fp32_layer_ragged_and_single_token():
@@ -120,3 +134,68 @@ def test_fused_lce_forward_only_and_empty():
     loss, dh, dw = lce(torch.from_numpy(inp.hidden).cuda(), torch.from_numpy(inp.weight).cuda(), y)
     torch.cuda.synchronize()
     assert loss.item() == 0.0 and not dh.any().item() and not dw.any().item()
+
+
+def test_tiny_fp32_layer_gradient_accumulation():
+    """Two backward passes with different dy, the second with accumulate: every matrix, gain and
+    scalar gradient equals the oracle's sum of the two (fp32, 1e-5); the value-embedding table
+    accumulates in both calls (its contract)."""
+    need_gpu()
+    s = synth.TINY_FP32
+    inp = synth.layer_inputs(s, seed=11, perturb=True)
+    dy2 = synth.normal((s.tokens, s.d_model), 1.0, 11, 99, "fp32")
+    from oracle import model as om
+    from tests.layer_cases import config_of, device_params, GPU_NAME
+    from transformer_train_step_amd.ops import Layer
+    print("tiny fp32 layer: accumulate over two backward calls", flush=True)
+    layer = Layer(config_of(s))
+    p = device_params(inp)
+    x = torch.from_numpy(inp.x).cuda()
+    ids = torch.from_numpy(inp.ids).cuda()
+    layer.forward(p, x, ids)
+    dx1, g = layer.backward(p, x, ids, torch.from_numpy(inp.dy).cuda())
+    dx2, g = layer.backward(p, x, ids, torch.from_numpy(dy2).cuda(), grads=g, accumulate=True)
+    torch.cuda.synchronize()
+    prm, dims = om.params_from_inputs(inp), om.dims_from_shape(s)
+    _, cache = om.layer_fwd(prm, inp.x, inp.ids, dims)
+    r1 = om.layer_bwd(prm, cache, inp.dy, dims)
+    r2 = om.layer_bwd(prm, cache, dy2, dims)
+    assert_close(dx2.cpu().numpy(), r2["dx"], 1e-5, "dx (second call)")
+    for k in ("w_qkv", "w_o", "w_fc", "w_proj", "g_attn", "g_mlp", "ve_table"):
+        assert_close(g[GPU_NAME.get(k, k)].cpu().numpy(), r1[k] + r2[k], 1e-5, k, elem_rtol=1e-3)
+    for k in ("a_attn", "a_mlp"):
+        got = float(g[GPU_NAME[k]].item())
+        assert abs(got - (r1[k] + r2[k])) <= 1e-5 * (abs(r1[k]) + abs(r2[k])), (k, got, r1[k] + r2[k])
+
+
+@pytest.mark.parametrize("n,d,v,chunk,vtile,dtype", [
+    (300, 3072, 50304, 128, 128, "bf16"),   # 128-wide vocabulary tiles (128 x 128 logits GEMM), 3 chunks
+    (97, 256, 520, 40, 128, "fp32"),
+    (200, 256, 512, 0, 256, "fp32"),        # one chunk: dW straight from the GEMM
+])
+def test_fused_lce_vocab_tile_and_accumulate(n, d, v, chunk, vtile, dtype):
+    """The loss with 128- and 256-wide vocabulary tiles against the oracle, then a second call with
+    accumulate_dw: d_weight = round(first + second)."""
+    need_gpu()
+    inp = synth.lce_inputs(n, d, v, min(v, 50257), dtype=dtype, seed=n + 1, n_ignored=3)
+    print(f"lce n={n} v={v} chunk={chunk} vocab_tile={vtile} {dtype} + accumulate", flush=True)
+    lce = FusedLCE(dtype, n, d, v, chunk, vocab_tile=vtile)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    H = torch.from_numpy(inp.hidden).to(tdt).cuda()
+    W = torch.from_numpy(inp.weight).to(tdt).cuda()
+    y = torch.from_numpy(inp.targets).cuda()
+    lse = torch.empty(n, dtype=torch.float32, device="cuda")
+    loss, dh, dw = lce(H, W, y, lse=lse)
+    torch.cuda.synchronize()
+    ref = olce.lce_fwd_bwd(inp.hidden, inp.weight, inp.targets, mode=dtype)
+    rtol = 1e-5 if dtype == "fp32" else 2e-2
+    assert abs(loss.item() - ref["loss"]) <= (1e-5 if dtype == "fp32" else 1e-4) * abs(ref["loss"])
+    assert_close(lse.cpu().numpy(), ref["lse"], 1e-6 if dtype == "fp32" else 1e-5, "lse", elem_rtol=1e-4)
+    assert_close(dh.float().cpu().numpy(), ref["dh"], rtol, "d_hidden", elem_rtol=max(10 * rtol, 1e-3))
+    dw1 = dw.float().cpu().numpy().astype(np.float64)
+    assert_close(dw1, ref["dw"], rtol, "d_weight", elem_rtol=max(10 * rtol, 1e-3))
+    _, _, dw2 = lce(H, W, y, d_weight=dw, accumulate_dw=True)
+    torch.cuda.synchronize()
+    want = dw1 + ref["dw"]
+    assert_close(dw2.float().cpu().numpy(), nu.bf16_round(want) if dtype == "bf16" else want, rtol,
+                 "d_weight accumulated", elem_rtol=max(10 * rtol, 1e-3))

@@ -307,3 +307,17 @@ def test_fp8_mlp_close_to_bf16_mlp():
     g16 = om.mlp_bwd(dm, c16, w1, w2, False, R)
     for a, b in zip(g8, g16):
         assert rel(a, b) < 0.08
+
+
+def test_gather_and_scatter_rows_out_of_range_ids():
+    """ids outside the table pick zero rows and receive nothing; in-range ids are the one-hot
+    products (gather = onehot @ table, scatter = onehot^T @ d)."""
+    rng = np.random.default_rng(19)
+    table = rng.standard_normal((6, 3))
+    ids = np.array([2, -1, 5, 6, 2, 10**6, 0])
+    ok = (ids >= 0) & (ids < 6)
+    onehot = np.zeros((len(ids), 6))
+    onehot[np.arange(len(ids))[ok], ids[ok]] = 1.0
+    np.testing.assert_array_equal(om.gather_rows(table, ids), onehot @ table)
+    d = rng.standard_normal((len(ids), 3))
+    np.testing.assert_allclose(om.scatter_rows(d, ids, 6), onehot.T @ d, rtol=1e-14)

@@ -44,7 +44,8 @@ class LayerParams(ctypes.Structure):
 class LayerGrads(ctypes.Structure):
     _fields_ = [("attn_norm_w", c_void_p), ("w_qkv", c_void_p), ("w_o", c_void_p),
                 ("mlp_norm_w", c_void_p), ("w_fc", c_void_p), ("w_proj", c_void_p),
-                ("ve_table", c_void_p), ("resid_attn", c_void_p), ("resid_mlp", c_void_p)]
+                ("ve_table", c_void_p), ("resid_attn", c_void_p), ("resid_mlp", c_void_p),
+                ("accumulate", c_int32)]
 
 
 class ModelParams(ctypes.Structure):
@@ -54,7 +55,7 @@ class ModelParams(ctypes.Structure):
 
 class ModelGrads(ctypes.Structure):
     _fields_ = [("embed", c_void_p), ("layers", ctypes.POINTER(LayerGrads)), ("final_norm_w", c_void_p),
-                ("head", c_void_p)]
+                ("head", c_void_p), ("accumulate", c_int32)]
 
 
 _lib = None
@@ -75,10 +76,10 @@ _SIGS = {
     "ll_layer_bwd": (c_int32, [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerParams), c_void_p,
                                c_void_p, c_void_p, c_size_t, c_void_p, c_void_p,
                                ctypes.POINTER(LayerGrads), c_void_p, c_size_t, c_void_p]),
-    "ll_fused_lce_workspace_bytes": (c_size_t, [c_int32, c_int64, c_int32, c_int64, c_int64]),
+    "ll_fused_lce_workspace_bytes": (c_size_t, [c_int32, c_int64, c_int32, c_int64, c_int64, c_int32]),
     "ll_fused_lce_fwd_bwd": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, c_int64, c_int32,
-                                       c_int64, c_float, c_int32, c_float, c_int64, c_void_p,
-                                       c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+                                       c_int64, c_float, c_int32, c_float, c_int64, c_int32, c_int32,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "ll_model_saved_bytes": (c_size_t, [ctypes.POINTER(LayerCfg), c_int32, c_int64]),
     "ll_model_workspace_bytes": (c_size_t, [ctypes.POINTER(LayerCfg), c_int32, c_int64, c_int64]),
     "ll_model_fwd_bwd": (c_int32, [ctypes.POINTER(LayerCfg), c_int32, c_int64, ctypes.POINTER(ModelParams),
@@ -107,6 +108,14 @@ _SIGS = {
     "llt_trace_count": (c_int32, []),
     "llt_trace_get": (c_int32, [c_int32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(c_float),
                                 ctypes.POINTER(c_int64)]),
+    "llt_trace_get_gemm": (c_int32, [c_int32, ctypes.POINTER(c_int32), ctypes.POINTER(c_int32)]),
+    "ll_muon_workspace_bytes": (c_size_t, [c_int64, c_int64]),
+    "ll_muon_step": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_float, c_float, c_int32,
+                               c_float, c_int32, c_void_p, c_size_t, c_void_p]),
+    "ll_adamw_step": (c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_float, c_float,
+                                c_float, c_float, c_float, c_int64, c_void_p]),
+    "llt_layer_buffer": (c_int32, [ctypes.POINTER(LayerCfg), c_int32, ctypes.c_char_p, ctypes.POINTER(c_size_t),
+                                   ctypes.POINTER(c_size_t)]),
 }
 
 ENTRY_POINTS = tuple(_SIGS)
@@ -208,16 +217,17 @@ def ll_layer_bwd(cfg, params, x, token_ids, saved, saved_bytes, dy, dx, grads, w
                  stream_handle(stream), raise_on_error=raise_on_error)
 
 
-def ll_fused_lce_workspace_bytes(dtype, n, d, v, token_chunk) -> int:
-    return lib().ll_fused_lce_workspace_bytes(dtype, n, d, v, token_chunk)
+def ll_fused_lce_workspace_bytes(dtype, n, d, v, token_chunk, vocab_tile=0) -> int:
+    return lib().ll_fused_lce_workspace_bytes(dtype, n, d, v, token_chunk, vocab_tile)
 
 
 def ll_fused_lce_fwd_bwd(dtype, hidden, weight, targets, n, d, v, softcap, ignore_index, grad_scale,
-                         token_chunk, loss, lse, d_hidden, d_weight, ws, ws_bytes, stream=None,
-                         raise_on_error=True):
+                         token_chunk, vocab_tile, accumulate_dw, loss, lse, d_hidden, d_weight, ws, ws_bytes,
+                         stream=None, raise_on_error=True):
     return _call("ll_fused_lce_fwd_bwd", dtype, ptr(hidden), ptr(weight), ptr(targets), n, d, v,
-                 softcap, ignore_index, grad_scale, token_chunk, ptr(loss), ptr(lse), ptr(d_hidden),
-                 ptr(d_weight), ptr(ws), ws_bytes, stream_handle(stream), raise_on_error=raise_on_error)
+                 softcap, ignore_index, grad_scale, token_chunk, vocab_tile, int(accumulate_dw), ptr(loss),
+                 ptr(lse), ptr(d_hidden), ptr(d_weight), ptr(ws), ws_bytes, stream_handle(stream),
+                 raise_on_error=raise_on_error)
 
 
 def ll_model_saved_bytes(cfg: LayerCfg, n_layers: int, vocab: int) -> int:
@@ -312,3 +322,18 @@ def llt_trace_get(i: int):
 def llt_trace_read() -> list:
     """[(tag, ms, (M, N, K))] of every launch recorded since llt_trace_begin."""
     return [llt_trace_get(i) for i in range(llt_trace_count())]
+
+
+def llt_trace_get_gemm(i: int):
+    """(block configuration, K slices) of GEMM launch i of the trace; (0, 0) for other launches."""
+    cfg, sl = c_int32(), c_int32()
+    _call("llt_trace_get_gemm", i, ctypes.byref(cfg), ctypes.byref(sl))
+    return cfg.value, sl.value
+
+
+def llt_layer_buffer(cfg: LayerCfg, region: int, name: str):
+    """(byte offset, bytes) of a named intermediate inside saved (0), fwd ws (1) or bwd ws (2)."""
+    off, nb = c_size_t(), c_size_t()
+    _call("llt_layer_buffer", ctypes.byref(cfg), region, name.encode(), ctypes.byref(off), ctypes.byref(nb))
+    return off.value, nb.value
+

@@ -20,6 +20,7 @@ namespace {
 struct TraceRec {
   const char* tag;
   int64_t m, n, k;
+  int cfg, slices;
   hipEvent_t a, b;
 };
 std::mutex g_trace_mu;
@@ -34,7 +35,7 @@ static int g_gemm_cfg = 0;
 int gemm_config_override() { return g_gemm_cfg; }
 void set_gemm_config_override(int c) { g_gemm_cfg = c; }
 
-int trace_open(const char* tag, hipStream_t s, int64_t m, int64_t n, int64_t k) {
+int trace_open(const char* tag, hipStream_t s, int64_t m, int64_t n, int64_t k, int gemm_cfg, int slices) {
   std::lock_guard<std::mutex> lk(g_trace_mu);
   if (!g_trace_on || g_trace_used >= (int)g_trace.size()) return -1;
   const int slot = g_trace_used++;
@@ -42,6 +43,8 @@ int trace_open(const char* tag, hipStream_t s, int64_t m, int64_t n, int64_t k) 
   g_trace[slot].m = m;
   g_trace[slot].n = n;
   g_trace[slot].k = k;
+  g_trace[slot].cfg = gemm_cfg;
+  g_trace[slot].slices = slices;
   if (hipEventRecord(g_trace[slot].a, s) != hipSuccess) return -1;
   return slot;
 }
@@ -60,7 +63,7 @@ int llt_trace_begin(int32_t capacity) {
       (void)hipEventDestroy(r.a);
       (void)hipEventDestroy(r.b);
     }
-    ll::g_trace.assign(capacity, ll::TraceRec{nullptr, 0, 0, 0, nullptr, nullptr});
+    ll::g_trace.assign(capacity, ll::TraceRec{nullptr, 0, 0, 0, 0, 0, nullptr, nullptr});
     for (auto& r : ll::g_trace) {
       LL_HIP(hipEventCreate(&r.a));
       LL_HIP(hipEventCreate(&r.b));
@@ -97,6 +100,14 @@ int llt_trace_get(int32_t i, const char** tag, float* ms, int64_t* mnk) {
   return LL_OK;
 }
 
+int llt_trace_get_gemm(int32_t i, int32_t* gemm_cfg, int32_t* slices) {
+  std::lock_guard<std::mutex> lk(ll::g_trace_mu);
+  LL_CHECK(i >= 0 && i < ll::g_trace_used, LL_ERR_INVALID_ARG, "trace index out of range");
+  LL_CHECK(gemm_cfg && slices, LL_ERR_INVALID_ARG, "gemm_cfg and slices must not be null");
+  *gemm_cfg = ll::g_trace[i].cfg;
+  *slices = ll::g_trace[i].slices;
+  return LL_OK;
+}
 
 const char* ll_status_string(int status) {
   switch (status) {

@@ -183,12 +183,14 @@ attn_delta_kernel(const T* __restrict__ dO, const T* __restrict__ O, float* __re
 // dE[ids[n], c] += dv[n, c]   (fp32 atomics; duplicate ids accumulate)
 template <class T>
 __global__ void ve_scatter_kernel(const T* __restrict__ dv, int64_t lddv, const int32_t* __restrict__ ids,
-                                  float* __restrict__ dE, int64_t ldE, int64_t N, int C) {
+                                  float* __restrict__ dE, int64_t ldE, int64_t rows, int64_t N, int C) {
   const int64_t total = N * C;
   for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < total; k += (int64_t)gridDim.x * blockDim.x) {
     const int64_t n = k / C;
     const int c = (int)(k - n * C);
-    atomicAdd(dE + (int64_t)ids[n] * ldE + c, Elem<T>::ld(dv, n * lddv + c));
+    const int32_t id = ids[n];
+    if (id >= 0 && id < rows)   // ids outside the table add nothing (as in the forward's gather)
+      atomicAdd(dE + (int64_t)id * ldE + c, Elem<T>::ld(dv, n * lddv + c));
   }
 }
 

@@ -103,6 +103,9 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(float v0, float v1, float v2, 
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, lo, true);
 }
 
+// relu that passes NaN through (fmaxf(NaN, 0) would return 0); equal to max(v, 0) otherwise
+__device__ __forceinline__ float relu_keep_nan(float v) { return v < 0.f ? 0.f : v; }
+
 // Decode an e4m3fn code (finite codes only) to fp32.
 __device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
   uint32_t e = (c >> 3) & 0xF, m = c & 7;
@@ -188,12 +191,21 @@ int gemm_config_override();
 
 // GEMM launches also record their (M, N, K).
 bool trace_on();
-int trace_open(const char* tag, hipStream_t s, int64_t m = 0, int64_t n = 0, int64_t k = 0);
+int trace_open(const char* tag, hipStream_t s, int64_t m = 0, int64_t n = 0, int64_t k = 0, int gemm_cfg = 0,
+               int slices = 0);
 void trace_close(int slot, hipStream_t s);
 
 #define LL_LAUNCH_MNK(tag, m, n, k, kern, grid, block, shm, stream, ...)                          \
   do {                                                                                          \
     const int ll_slot_ = ::ll::trace_on() ? ::ll::trace_open((tag), (stream), (m), (n), (k)) : -1; \
+    hipLaunchKernelGGL(kern, grid, block, shm, stream, __VA_ARGS__);                            \
+    if (ll_slot_ >= 0) ::ll::trace_close(ll_slot_, (stream));                                   \
+  } while (0)
+// GEMM launches also record the block configuration that ran and the number of K slices
+#define LL_LAUNCH_GEMM(tag, m, n, k, cfg, slices, kern, grid, block, shm, stream, ...)             \
+  do {                                                                                          \
+    const int ll_slot_ =                                                                        \
+        ::ll::trace_on() ? ::ll::trace_open((tag), (stream), (m), (n), (k), (cfg), (slices)) : -1; \
     hipLaunchKernelGGL(kern, grid, block, shm, stream, __VA_ARGS__);                            \
     if (ll_slot_ >= 0) ::ll::trace_close(ll_slot_, (stream));                                   \
   } while (0)

@@ -759,15 +759,39 @@ struct Deq {
   __device__ __forceinline__ float apply(float acc) const { return ia ? (acc * *ia) * *ib : acc; }
 };
 
-// C = round(deq(acc))
+// C = round(deq(acc)), or with accumulate C = round(C + deq(acc)) (gradient accumulation over
+// micro-batches: one rounding of the sum)
 template <class OutT> struct EpiStore {
   static constexpr const char* kName = "store";
   static constexpr int kKind = kEpiPlain;
-  OutT* C; int64_t ldc; Deq dq;
+  OutT* C; int64_t ldc; Deq dq; int accumulate = 0;
   __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
+    OutT* p = C + (int64_t)m * ldc + n;
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = dq.apply(v[k]);
-    Vec8<OutT>::store(C + (int64_t)m * ldc + n, v);
+    if (accumulate) {
+      float o[8];
+      Vec8<OutT>::load(p, o);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] += o[k];
+    }
+    Vec8<OutT>::store(p, v);
+  }
+};
+
+// out = round(alpha other + beta acc) (other [m, n] read at the output's position; out must not
+// alias an operand of the GEMM)
+template <class T> struct EpiLin {
+  static constexpr const char* kName = "lin";
+  static constexpr int kKind = kEpiPlain;
+  T* out; const T* other; int64_t ld; float alpha; float beta;
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
+    const int64_t o = (int64_t)m * ld + n;
+    float x[8];
+    Vec8<T>::load(other + o, x);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = alpha * x[k] + beta * v[k];
+    Vec8<T>::store(out + o, v);
   }
 };
 
@@ -801,7 +825,7 @@ template <class T> struct EpiRelu2 {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       v[k] = Elem<T>::rnd(dq.apply(v[k]));
-      const float p = fmaxf(v[k], 0.f);
+      const float p = relu_keep_nan(v[k]);
       rr[k] = Elem<T>::rnd(p * p);
       mx = fmaxf(mx, rr[k]);
     }
@@ -822,7 +846,7 @@ template <class T> struct EpiRelu2Amax {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       v[k] = Elem<T>::rnd(dq.apply(v[k]));
-      const float p = fmaxf(v[k], 0.f);
+      const float p = relu_keep_nan(v[k]);
       mx = fmaxf(mx, Elem<T>::rnd(p * p));
     }
     Vec8<T>::store(u + (int64_t)m * ld + n, v);
@@ -842,7 +866,7 @@ template <class T> struct EpiRelu2Bwd {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float dr = Elem<T>::rnd(dq.apply(v[k]));
-      v[k] = Elem<T>::rnd(dr * (2.f * fmaxf(uv[k], 0.f)));
+      v[k] = Elem<T>::rnd(dr * (2.f * relu_keep_nan(uv[k])));
       mx = fmaxf(mx, fabsf(v[k]));
     }
     Vec8<T>::store(du + o, v);
@@ -851,19 +875,22 @@ template <class T> struct EpiRelu2Bwd {
 };
 
 // qkv = round(acc); on the v columns (n >= vcol0) of value-embedding layers:
-// v = round(v + table[ids[m], n - vcol0])
+// v = round(v + table[ids[m], n - vcol0]), nothing added for ids outside [0, rows)
 template <class T> struct EpiQkv {
   static constexpr const char* kName = "qkv";
   static constexpr int kKind = kEpiPlain;
-  T* C; int64_t ldc; const T* table; int64_t ldt; const int32_t* ids; int vcol0;
+  T* C; int64_t ldc; const T* table; int64_t ldt; const int32_t* ids; int vcol0; int64_t rows;
   __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = Elem<T>::rnd(v[k]);
     if (table && n >= vcol0) {
-      float e[8];
-      Vec8<T>::load(table + (int64_t)ids[m] * ldt + (n - vcol0), e);
+      const int32_t id = ids[m];
+      if (id >= 0 && id < rows) {
+        float e[8];
+        Vec8<T>::load(table + (int64_t)id * ldt + (n - vcol0), e);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] += e[k];
+        for (int k = 0; k < 8; ++k) v[k] += e[k];
+      }
     }
     Vec8<T>::store(C + (int64_t)m * ldc + n, v);
   }
@@ -886,17 +913,24 @@ struct EpiAcc32 {
   }
 };
 
-// the last call of an fp32 accumulation: out = round(C32 + acc) (C32 is only read)
+// the last call of an fp32 accumulation: out = round(C32 + acc), or with accumulate
+// out = round(out + C32 + acc) (C32 is only read)
 template <class OutT> struct EpiAcc32Out {
   static constexpr const char* kName = "acc32";
   static constexpr int kKind = kEpiPlain;
-  const float* C; OutT* out; int64_t ldc;
+  const float* C; OutT* out; int64_t ldc; int accumulate = 0;
   __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
     const int64_t o = (int64_t)m * ldc + n;
     float c[8];
     Vec8<float>::load(C + o, c);
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] += c[k];
+    if (accumulate) {
+      float p[8];
+      Vec8<OutT>::load(out + o, p);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] += p[k];
+    }
     Vec8<OutT>::store(out + o, v);
   }
 };
@@ -912,11 +946,12 @@ struct EpiSplitK32 {
   }
 };
 
-// out[m, n] = round(deq(sum over the S slices of part[s slice + m ldp + n])), 8 columns per thread
+// out[m, n] = round(deq(sum over the S slices of part[s slice + m ldp + n])) (+ out[m, n] before the
+// rounding with accumulate), 8 columns per thread
 template <class T>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int S, int64_t slice,
                                                            int64_t ldp, int M, int N, T* __restrict__ out, int64_t ldo,
-                                                           Deq dq) {
+                                                           Deq dq, int accumulate) {
   const int nseg = N / 8;
   const int64_t total = (int64_t)M * nseg;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
@@ -930,6 +965,11 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = dq.apply(v[k]);
+    if (accumulate) {
+      Vec8<T>::load(out + (int64_t)m * ldo + n, t);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] += t[k];
+    }
     Vec8<T>::store(out + (int64_t)m * ldo + n, v);
   }
 }
@@ -956,7 +996,7 @@ struct GemmOps {
 };
 
 template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, int MODE = 0, class Epi>
-inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
+inline hipError_t launch_gemm_cfg(int cfg_id, const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
                                   const Epi& epi, const GemmOps& o, hipStream_t s) {
   const int64_t nbt = cdiv(M, BM) * cdiv(N, BN);
   // Block order: along the longer side of the output, 2 tile rows (or columns) at a time (measured
@@ -971,25 +1011,25 @@ inline hipError_t launch_gemm_cfg(const ET* A, int64_t lda, const ET* B, int64_t
   if constexpr (sizeof(ET) == 2 && MODE != 3) {   // MODE 3: K-major operands only (the callers check)
     if (!o.a_kmajor && !o.b_kmajor) {
       const char* tag = gemm_tag<ET, Epi, false, false>();
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, false, Epi, MODE>), nb, dim3(NT),
+      LL_LAUNCH_GEMM(tag, M, N, K, cfg_id, (int)slices, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, false, Epi, MODE>), nb, dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi, G);
       return hipGetLastError();
     }
     if (!o.a_kmajor) {
       const char* tag = gemm_tag<ET, Epi, false, true>();
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, true, Epi, MODE>), nb, dim3(NT),
+      LL_LAUNCH_GEMM(tag, M, N, K, cfg_id, (int)slices, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, true, Epi, MODE>), nb, dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi, G);
       return hipGetLastError();
     }
     if (!o.b_kmajor) {
       const char* tag = gemm_tag<ET, Epi, true, false>();
-      LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, false, Epi, MODE>), nb, dim3(NT),
+      LL_LAUNCH_GEMM(tag, M, N, K, cfg_id, (int)slices, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, false, Epi, MODE>), nb, dim3(NT),
                     0, s, A, lda, B, ldb, M, N, K, z, epi, G);
       return hipGetLastError();
     }
   }
   const char* tag = gemm_tag<ET, Epi, true, true>();
-  LL_LAUNCH_MNK(tag, M, N, K, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, true, Epi, MODE>), nb, dim3(NT), 0, s,
+  LL_LAUNCH_GEMM(tag, M, N, K, cfg_id, (int)slices, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, true, true, Epi, MODE>), nb, dim3(NT), 0, s,
                 A, lda, B, ldb, M, N, K, z, epi, G);
   return hipGetLastError();
 }
@@ -1018,36 +1058,47 @@ inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* 
     if (cfg == 6) cfg = 4;
     if (cfg == 7) cfg = 1;
     if (cfg == 8 || cfg == 9 || cfg == 10) cfg = 4;
-    if (cfg == 11) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
+    if (cfg == 11) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 3>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
   } else if constexpr (sizeof(ET) == 2) {
     if (cfg == 11) {
-      if (o.a_kmajor && o.b_kmajor) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
+      if (o.a_kmajor && o.b_kmajor) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 3>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
       cfg = 9;
     }
   } else {
     if (cfg == 9 || cfg == 10 || cfg == 11) cfg = 4;
   }
+  if constexpr (sizeof(ET) <= 2) {
+    // 12: 256 x 256, 4 waves (2 x 2, one per SIMD, 128 x 128 each), split-phase on the 32x32 MFMAs;
+    // 13: the same on the 16x16 MFMAs with interleaved reads (bf16). K-major operands only.
+    if ((cfg == 12 || cfg == 13) && o.a_kmajor && o.b_kmajor) {
+      if (cfg == 12 || sizeof(ET) == 1) return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2, 3>(12, A, lda, B, ldb, M, N, K, epi, o, s);
+      if constexpr (sizeof(ET) == 2) return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2, 2>(13, A, lda, B, ldb, M, N, K, epi, o, s);
+    }
+    if (cfg == 12 || cfg == 13) cfg = 9;
+  } else {
+    if (cfg == 12 || cfg == 13) cfg = 4;
+  }
   switch (cfg) {
-    case 1: return launch_gemm_cfg<ET, 128, 128, 2, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
-    case 2: return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
-    case 3: return launch_gemm_cfg<ET, 256, 256, 2, 4, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
-    case 4: return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+    case 1: return launch_gemm_cfg<ET, 128, 128, 2, 2, 128, 2>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
+    case 2: return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
+    case 3: return launch_gemm_cfg<ET, 256, 256, 2, 4, 128, 2>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
+    case 4: return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
     default:
       if constexpr (sizeof(ET) != 1) {
-        if (cfg == 5) return launch_gemm_cfg<ET, 256, 256, 2, 4, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
-        if (cfg == 6) return launch_gemm_cfg<ET, 256, 256, 4, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
-        if (cfg == 7) return launch_gemm_cfg<ET, 128, 128, 2, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
-        if (cfg == 8) return launch_gemm_cfg<ET, 256, 256, 2, 2, 64, 3>(A, lda, B, ldb, M, N, K, epi, o, s);
+        if (cfg == 5) return launch_gemm_cfg<ET, 256, 256, 2, 4, 64, 3>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
+        if (cfg == 6) return launch_gemm_cfg<ET, 256, 256, 4, 2, 64, 3>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
+        if (cfg == 7) return launch_gemm_cfg<ET, 128, 128, 2, 2, 64, 3>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
+        if (cfg == 8) return launch_gemm_cfg<ET, 256, 256, 2, 2, 64, 3>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
         if (cfg == 9) {
-          if constexpr (sizeof(ET) == 2) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
-          else return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+          if constexpr (sizeof(ET) == 2) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 2>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
+          else return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
         }
         if (cfg == 10) {
-          if constexpr (sizeof(ET) == 2) return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2, 1>(A, lda, B, ldb, M, N, K, epi, o, s);
-          else return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+          if constexpr (sizeof(ET) == 2) return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2, 1>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
+          else return launch_gemm_cfg<ET, 256, 256, 2, 2, 128, 2>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
         }
       }
-      return launch_gemm_cfg<ET, 256, 256, 2, 4, 128, 2>(A, lda, B, ldb, M, N, K, epi, o, s);
+      return launch_gemm_cfg<ET, 256, 256, 2, 4, 128, 2>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
   }
 }
 
@@ -1091,7 +1142,7 @@ inline int splitk_slices(int64_t tiles, int64_t K, int ke, int smax) {
 template <class ET, class OutT>
 inline hipError_t launch_gemm_splitk(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
                                      int slices, OutT* out, int64_t ldo, float* scratch, const GemmOps& o,
-                                     hipStream_t s, Deq dq = Deq{nullptr, nullptr}) {
+                                     hipStream_t s, Deq dq = Deq{nullptr, nullptr}, int accumulate = 0) {
   if (M <= 0 || N <= 0) return hipSuccess;
   constexpr int KE = 128 / (int)sizeof(ET);
   const int kchunk = (int)std::max<int64_t>(KE, round_up(cdiv(K, slices), KE));
@@ -1103,7 +1154,7 @@ inline hipError_t launch_gemm_splitk(const ET* A, int64_t lda, const ET* B, int6
   if (r != hipSuccess) return r;
   const int64_t work = (int64_t)M * (N / 8);
   LL_LAUNCH("splitk_reduce", splitk_reduce_kernel<OutT>, dim3((unsigned)std::min<int64_t>(cdiv(work, 256), 8192)),
-            dim3(256), 0, s, scratch, sl, (int64_t)M * N, (int64_t)N, M, N, out, ldo, dq);
+            dim3(256), 0, s, scratch, sl, (int64_t)M * N, (int64_t)N, M, N, out, ldo, dq, accumulate);
   return hipGetLastError();
 }
 

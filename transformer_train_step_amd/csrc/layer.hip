@@ -16,7 +16,7 @@ using namespace ll;
 namespace {
 
 struct Dims {
-  int64_t B, T, N, Np, Tp;
+  int64_t B, T, N, Np, Tp, ve_rows;
   int D, Hq, Hkv, DH, F, QD, KVD, QKVD, vcol0;
   bool fp8, bf, ve;
   int es;
@@ -45,6 +45,7 @@ int make_dims(const ll_layer_cfg* c, Dims& d) {
   d.QD = d.Hq * d.DH; d.KVD = d.Hkv * d.DH; d.QKVD = d.QD + 2 * d.KVD; d.vcol0 = d.QD + d.KVD;
   d.fp8 = c->fp8_mlp != 0; d.bf = c->dtype == LL_BF16; d.ve = c->has_value_embed != 0;
   d.es = d.bf ? 2 : 4; d.eps = c->rms_eps; d.theta = c->rope_theta;
+  d.ve_rows = d.ve ? c->ve_rows : 0;
   return LL_OK;
 }
 
@@ -114,6 +115,8 @@ size_t carve_fwd(void* base, const Dims& d, FwdWs& w) {
 // ---------------------------------------------------------------- backward workspace
 struct BwdWs {
   float2* cs;
+  float* sk;             // fp32 partial sums of the weight gradients split along the tokens
+  size_t sk_bytes;
   QScale* qs;            // [2]: dm, du
   void *dm, *du, *dhn, *dh, *dattn, *dout, *qt, *kt, *dot, *dqkv, *dxn;
   void *t0, *t1;         // transposed operand copies: W^T for mm_nn (both types), mm_tn's (fp32 only)
@@ -121,10 +124,32 @@ struct BwdWs {
   uint8_t *dm8, *dm8t, *du8, *du8t;
   float *delta, *dqh, *dkh, *dgp;
 };
+// Floats of split-K partial sums the backward needs: the largest slices x M x N over the weight
+// gradients that split (the FP8 MLP weight gradients; the bf16 O-projection and QKV weight
+// gradients), with the slice counts the launches will pick.
+int64_t splitk_floats(const Dims& d) {
+  int64_t f = 0;
+  auto need = [&](int M, int N, int64_t K, int ke) {
+    const int sl = splitk_slices(cdiv(M, 256) * cdiv(N, 256), K, ke, 8);
+    if (sl > 1) f = std::max<int64_t>(f, (int64_t)sl * M * N);
+  };
+  if (d.fp8) {
+    need(d.D, d.F, d.Np, 128);
+    need(d.F, d.D, d.Np, 128);
+  }
+  if (d.bf) {
+    need(d.D, d.QD, d.N, 64);
+    need(d.QKVD, d.D, d.N, 64);
+  }
+  return f;
+}
+
 size_t carve_bwd(void* base, const Dims& d, BwdWs& w) {
   Carver c(base);
   const size_t e = d.es;
   w.cs = c.take<float2>(d.T * (d.DH / 2) + 1);
+  w.sk_bytes = (size_t)splitk_floats(d) * sizeof(float);
+  w.sk = w.sk_bytes ? c.take<float>(w.sk_bytes / sizeof(float)) : nullptr;
   w.qs = c.take<QScale>(2);
   w.zrow = c.take<char>(256);
   w.dm = c.take<char>(d.N * d.D * e);
@@ -209,7 +234,8 @@ hipError_t mm_tn(const T* X, int64_t ldx, const T* Y, int64_t ldy, int M, int N,
     if constexpr (std::is_same<Epi, EpiStore<T>>::value) {
       const int sl = splitk_slices(cdiv(M, 256) * cdiv(N, 256), K, 64, 8);
       if (sl > 1 && sk && !e.dq.ia && (size_t)sl * M * N * sizeof(float) <= sk_bytes && gemm_config_override() == 0)
-        return launch_gemm_splitk(X, ldx, Y, ldy, M, N, (int)K, sl, e.C, e.ldc, sk, ops, s);
+        return launch_gemm_splitk(X, ldx, Y, ldy, M, N, (int)K, sl, e.C, e.ldc, sk, ops, s, Deq{nullptr, nullptr},
+                                  e.accumulate);
     }
     return launch_gemm(X, ldx, Y, ldy, M, N, (int)K, e, ops, s);
   } else {
@@ -232,7 +258,7 @@ int layer_fwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   // attention block
   LL_HIP(launch_rmsnorm_fwd(x, g1, P<T>(sv.xn), sv.r1, N, d.D, d.eps, (float*)nullptr, s));
   {
-    EpiQkv<T> e{P<T>(sv.qkv), d.QKVD, d.ve ? CP<T>(p->ve_table) : nullptr, d.KVD, ids, d.vcol0};
+    EpiQkv<T> e{P<T>(sv.qkv), d.QKVD, d.ve ? CP<T>(p->ve_table) : nullptr, d.KVD, ids, d.vcol0, d.ve_rows};
     LL_HIP(launch_gemm_nt(CP<T>(sv.xn), d.D, CP<T>(p->w_qkv), d.D, (int)N, d.QKVD, d.D, e, s));
   }
   if (N > 0) {
@@ -306,11 +332,11 @@ int layer_fwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
 // tiles for the chip and the scratch holds the partial sums.
 template <class T>
 hipError_t wgrad_e4m3(const uint8_t* X, const uint8_t* Y, int64_t Np, int M, int N, T* C, Deq dq, float* sk,
-                      size_t sk_bytes, hipStream_t s) {
+                      size_t sk_bytes, int accumulate, hipStream_t s) {
   const int sl = splitk_slices(cdiv(M, 256) * cdiv(N, 256), Np, 128, 8);
   if (sl > 1 && (size_t)sl * M * N * sizeof(float) <= sk_bytes && gemm_config_override() == 0)
-    return launch_gemm_splitk(X, Np, Y, Np, M, N, (int)Np, sl, C, (int64_t)N, sk, GemmOps{}, s, dq);
-  EpiStore<T> e{C, (int64_t)N, dq};
+    return launch_gemm_splitk(X, Np, Y, Np, M, N, (int)Np, sl, C, (int64_t)N, sk, GemmOps{}, s, dq, accumulate);
+  EpiStore<T> e{C, (int64_t)N, dq, accumulate};
   return launch_gemm_nt(X, Np, Y, Np, M, N, (int)Np, e, s);
 }
 
@@ -324,8 +350,11 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   LL_HIP(rope_table(w.cs, d, s));
   LL_HIP(fill_f32(reinterpret_cast<float*>(w.qs), 0.f, 2 * 4, s));
   LL_HIP(fill_f32(reinterpret_cast<float*>(const_cast<void*>(w.zrow)), 0.f, 64, s));
-  LL_HIP(fill_f32(g->resid_mlp, 0.f, 1, s));
-  LL_HIP(fill_f32(g->resid_attn, 0.f, 1, s));
+  const int acc = g->accumulate ? 1 : 0;
+  if (!acc) {   // the residual-scalar gradients are atomic sums: start from 0 unless accumulating
+    LL_HIP(fill_f32(g->resid_mlp, 0.f, 1, s));
+    LL_HIP(fill_f32(g->resid_attn, 0.f, 1, s));
+  }
   // MLP residual branch: dm = a_mlp dy, da_mlp = sum dy m
   LL_HIP(launch_scale_dot(dy, CP<T>(sv.m), p->resid_mlp, P<T>(w.dm), N * d.D, g->resid_mlp,
                           d.fp8 ? &w.qs[0].amax : nullptr, s));
@@ -343,15 +372,14 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
       }
       LL_HIP(launch_cast_e4m3(CP<T>(w.du), N, d.F, d.F, qdu, w.du8, d.F, w.du8t, Np, Np, (float*)nullptr,
                               (float*)nullptr, s));
-      // the bf16 du is dead from here: it holds the split-K partial sums of the weight gradients
-      float* sk = P<float>(w.du);
-      const size_t sk_bytes = (size_t)(d.N * d.F * d.es);
+      float* sk = w.sk;
+      const size_t sk_bytes = w.sk_bytes;
       // dW2 = dm^T r   [D, F]
       LL_HIP(wgrad_e4m3(w.dm8t, sv.r8t, Np, d.D, d.F, P<T>(g->w_proj), Deq{&qdm->inv_scale, &q[QS_R].inv_scale}, sk,
-                        sk_bytes, s));
+                        sk_bytes, acc, s));
       // dW1 = du^T hn  [F, D]
       LL_HIP(wgrad_e4m3(w.du8t, sv.hn8t, Np, d.F, d.D, P<T>(g->w_fc), Deq{&qdu->inv_scale, &q[QS_HN].inv_scale}, sk,
-                        sk_bytes, s));
+                        sk_bytes, acc, s));
       {   // dhn = du W1 (W1^T quantised is [D, F])
         EpiStore<T> e{P<T>(w.dhn), (int64_t)d.D, Deq{&qdu->inv_scale, &q[QS_W1].inv_scale}};
         LL_HIP(launch_gemm_nt(w.du8, d.F, sv.w18t, d.F, (int)N, d.D, d.F, e, s));
@@ -365,11 +393,11 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
       LL_HIP(mm_nn(CP<T>(w.dm), d.D, CP<T>(p->w_proj), d.F, (int)N, d.F, d.D, e, P<T>(w.t0), w.zrow, s));
     }
     {   // dW2 = dm^T r
-      EpiStore<T> e{P<T>(g->w_proj), (int64_t)d.F, Deq{nullptr, nullptr}};
+      EpiStore<T> e{P<T>(g->w_proj), (int64_t)d.F, Deq{nullptr, nullptr}, acc};
       LL_HIP(mm_tn(CP<T>(w.dm), d.D, CP<T>(sv.r), d.F, d.D, d.F, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s));
     }
     {   // dW1 = du^T hn
-      EpiStore<T> e{P<T>(g->w_fc), (int64_t)d.D, Deq{nullptr, nullptr}};
+      EpiStore<T> e{P<T>(g->w_fc), (int64_t)d.D, Deq{nullptr, nullptr}, acc};
       LL_HIP(mm_tn(CP<T>(w.du), d.F, CP<T>(sv.hn), d.D, d.F, d.D, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s));
     }
     {   // dhn = du W1
@@ -381,17 +409,16 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   LL_HIP(launch_rmsnorm_bwd(CP<T>(w.dhn), CP<T>(sv.h), g2, sv.r2, dy, P<T>(w.dh), w.dgp, N, d.D, p->resid_attn,
                             P<T>(w.dattn), CP<T>(sv.attn_out), g->resid_attn, s));
   LL_HIP(launch_colsum(w.dgp, rmsnorm_bwd_partials(N), d.D, P<float>(g->mlp_norm_w),
-                       w.dgp + rmsnorm_bwd_partials(N) * d.D, s));
+                       w.dgp + rmsnorm_bwd_partials(N) * d.D, s, acc));
   // O projection: do = dattn W_o, dW_o = dattn^T o
   {
     EpiStore<T> e{P<T>(w.dout), (int64_t)d.QD, Deq{nullptr, nullptr}};
     LL_HIP(mm_nn(CP<T>(w.dattn), d.D, CP<T>(p->w_o), d.QD, (int)N, d.QD, d.D, e, P<T>(w.t0), w.zrow, s));
   }
   {
-    EpiStore<T> e{P<T>(g->w_o), (int64_t)d.QD, Deq{nullptr, nullptr}};
-    // du (dead after the MLP backward) holds the split-K partial sums
+    EpiStore<T> e{P<T>(g->w_o), (int64_t)d.QD, Deq{nullptr, nullptr}, acc};
     LL_HIP(mm_tn(CP<T>(w.dattn), d.D, CP<T>(sv.o), d.QD, d.D, d.QD, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s,
-                 P<float>(w.du), (size_t)(d.N * d.F * d.es)));
+                 w.sk, w.sk_bytes));
   }
   // attention core
   T* dqkv = P<T>(w.dqkv);
@@ -437,8 +464,9 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
     LL_HIP(hipGetLastError());
     if (d.ve) {
       const int64_t tot = N * d.KVD;
+      if (!acc) LL_HIP(fill_f32(g->ve_table, 0.f, d.ve_rows * d.KVD, s));   // overwrite: scatter-add from zero
       LL_LAUNCH("ve_scatter", (ve_scatter_kernel<T>), dim3((unsigned)std::min<int64_t>(cdiv(tot, 256), 16384)), dim3(256),
-                         0, s, CP<T>(dqkv) + d.vcol0, (int64_t)d.QKVD, ids, g->ve_table, (int64_t)d.KVD, N, d.KVD);
+                         0, s, CP<T>(dqkv) + d.vcol0, (int64_t)d.QKVD, ids, g->ve_table, (int64_t)d.KVD, d.ve_rows, N, d.KVD);
       LL_HIP(hipGetLastError());
     }
   }
@@ -448,15 +476,15 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
     LL_HIP(mm_nn(CP<T>(dqkv), d.QKVD, CP<T>(p->w_qkv), d.D, (int)N, d.D, d.QKVD, e, P<T>(w.t0), w.zrow, s));
   }
   {
-    EpiStore<T> e{P<T>(g->w_qkv), (int64_t)d.D, Deq{nullptr, nullptr}};
+    EpiStore<T> e{P<T>(g->w_qkv), (int64_t)d.D, Deq{nullptr, nullptr}, acc};
     LL_HIP(mm_tn(CP<T>(dqkv), d.QKVD, CP<T>(sv.xn), d.D, d.QKVD, d.D, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s,
-                 P<float>(w.du), (size_t)(d.N * d.F * d.es)));
+                 w.sk, w.sk_bytes));
   }
   // input RMSNorm backward + residual
   LL_HIP(launch_rmsnorm_bwd(CP<T>(w.dxn), x, g1, sv.r1, CP<T>(w.dh), dx, w.dgp, N, d.D, (const float*)nullptr,
                             (T*)nullptr, (const T*)nullptr, (float*)nullptr, s));
   LL_HIP(launch_colsum(w.dgp, rmsnorm_bwd_partials(N), d.D, P<float>(g->attn_norm_w),
-                       w.dgp + rmsnorm_bwd_partials(N) * d.D, s));
+                       w.dgp + rmsnorm_bwd_partials(N) * d.D, s, acc));
   return LL_OK;
 }
 
@@ -537,4 +565,53 @@ extern "C" int ll_layer_bwd(const ll_layer_cfg* cfg, const ll_layer_params* p, c
   if (d.bf)
     return layer_bwd_t<bf16, 128>(d, p, CP<bf16>(x), token_ids, sv, CP<bf16>(dy), P<bf16>(dx), g, w, s);
   return layer_bwd_t<float, 64>(d, p, CP<float>(x), token_ids, sv, CP<float>(dy), P<float>(dx), g, w, s);
+}
+
+extern "C" int llt_layer_buffer(const ll_layer_cfg* cfg, int32_t region, const char* name, size_t* offset,
+                                size_t* bytes) {
+  Dims d;
+  if (int st = make_dims(cfg, d)) return st;
+  LL_CHECK(name && offset && bytes, LL_ERR_INVALID_ARG, "name, offset and bytes must not be null");
+  LL_CHECK(region >= 0 && region <= 2, LL_ERR_INVALID_ARG, "region must be 0 (saved), 1 (fwd ws) or 2 (bwd ws)");
+  // carve over a fake base (never dereferenced) to read the sub-buffer offsets
+  char* const base = reinterpret_cast<char*>(uintptr_t(1) << 40);
+  const std::string n(name);
+  const size_t e = d.es;
+  const void* p = nullptr;
+  size_t sz = 0;
+  if (region == 0) {
+    Saved v;
+    carve_saved(base, d, v);
+    const struct { const char* k; const void* p; size_t sz; } t[] = {
+        {"qs", v.qs, 4 * sizeof(QScale)}, {"xn", v.xn, d.N * d.D * e}, {"qkv", v.qkv, d.N * d.QKVD * e},
+        {"qh", v.qh, d.N * d.QD * e}, {"kh", v.kh, d.N * d.KVD * e}, {"o", v.o, d.N * d.QD * e},
+        {"lse", v.lse, d.B * d.Hq * d.Tp * sizeof(float)}, {"attn_out", v.attn_out, d.N * d.D * e},
+        {"h", v.h, d.N * d.D * e}, {"u", v.u, d.N * d.F * e}, {"m", v.m, d.N * d.D * e},
+        {"r1", v.r1, d.N * sizeof(float)}, {"r2", v.r2, d.N * sizeof(float)},
+        {"hn8", v.hn8, (size_t)(d.N * d.D)}, {"hn8t", v.hn8t, (size_t)(d.D * d.Np)},
+        {"r8t", v.r8t, (size_t)(d.F * d.Np)}, {"w18", v.w18, (size_t)d.F * d.D}, {"w18t", v.w18t, (size_t)d.D * d.F},
+        {"w28", v.w28, (size_t)d.D * d.F}, {"w28t", v.w28t, (size_t)d.F * d.D}};
+    for (const auto& x : t)
+      if (n == x.k) { p = x.p; sz = x.sz; }
+  } else if (region == 1) {
+    FwdWs v;
+    carve_fwd(base, d, v);
+    if (n == "hn") { p = v.hn; sz = d.N * d.D * e; }
+    if (n == "r8") { p = v.r8; sz = (size_t)(d.N * d.F); }
+  } else {
+    BwdWs v;
+    carve_bwd(base, d, v);
+    const struct { const char* k; const void* p; size_t sz; } t[] = {
+        {"qs", v.qs, 2 * sizeof(QScale)}, {"dm", v.dm, d.N * d.D * e}, {"du", v.du, d.N * d.F * e},
+        {"dm8", v.dm8, (size_t)(d.N * d.D)}, {"dm8t", v.dm8t, (size_t)(d.D * d.Np)},
+        {"du8", v.du8, (size_t)(d.N * d.F)}, {"du8t", v.du8t, (size_t)(d.F * d.Np)},
+        {"dhn", v.dhn, d.N * d.D * e}, {"dh", v.dh, d.N * d.D * e}, {"dattn", v.dattn, d.N * d.D * e},
+        {"dout", v.dout, d.N * d.QD * e}, {"dqkv", v.dqkv, d.N * d.QKVD * e}, {"dxn", v.dxn, d.N * d.D * e}};
+    for (const auto& x : t)
+      if (n == x.k) { p = x.p; sz = x.sz; }
+  }
+  LL_CHECK(p, LL_ERR_INVALID_ARG, "no sub-buffer '" + n + "' in this region for this configuration");
+  *offset = static_cast<size_t>(static_cast<const char*>(p) - base);
+  *bytes = sz;
+  return LL_OK;
 }

@@ -9,12 +9,14 @@ using namespace ll;
 
 namespace {
 
-constexpr int kLceBN = 256;   // logits GEMM N tile (never the 128-wide config): one LSE partial per 256 columns
+// Vocabulary tile of the logits GEMM = the columns of one row-sum partial: 256 (256 x 256 block
+// tiles, the default) or 128 (128 x 128 block tiles)
+constexpr int kDefaultVocabTile = 256;
 constexpr int64_t kDefaultChunk = 10240;
 
 struct LcePlan {
   int64_t chunk, chunk_pad, vpad;
-  int nparts;
+  int nparts, vtile;
   float* part = nullptr;
   void* z = nullptr;        // [chunk_pad, Vpad]  (z, then dz in place)
   void* wt = nullptr;       // W^T [D, Vpad], zero past V
@@ -29,8 +31,9 @@ struct LcePlan {
   size_t bytes = 0;
 };
 
-LcePlan plan_lce(void* ws, int es, int64_t n, int d, int64_t v, int64_t token_chunk, bool grads) {
+LcePlan plan_lce(void* ws, int es, int64_t n, int d, int64_t v, int64_t token_chunk, int vocab_tile, bool grads) {
   LcePlan p;
+  p.vtile = vocab_tile > 0 ? vocab_tile : kDefaultVocabTile;
   p.chunk = token_chunk > 0 ? token_chunk : kDefaultChunk;
   if (p.chunk > n) p.chunk = n > 0 ? n : 1;
   // one chunk holds every token: the weight gradient is one contraction over all of them and is
@@ -39,7 +42,7 @@ LcePlan plan_lce(void* ws, int es, int64_t n, int d, int64_t v, int64_t token_ch
   p.single = n > 0 && p.chunk >= n;
   p.chunk_pad = round_up(p.chunk, 64);
   p.vpad = round_up(v, 64);
-  p.nparts = (int)cdiv(v, kLceBN);
+  p.nparts = (int)cdiv(v, p.vtile);
   Carver c(ws);
   p.loss_acc = c.take<float>(4);
   p.nv = c.take<int>(4);
@@ -60,7 +63,7 @@ LcePlan plan_lce(void* ws, int es, int64_t n, int d, int64_t v, int64_t token_ch
 template <class T>
 int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t v, float softcap,
             int32_t ignore, float grad_scale, const LcePlan& p, float* loss, float* lse_out, T* dH, T* dW,
-            hipStream_t s) {
+            int accumulate_dw, hipStream_t s) {
   const bool grads = dH != nullptr;
   constexpr bool kBf16 = std::is_same<T, bf16>::value;
   LL_HIP(fill_f32(p.loss_acc, 0.f, 4, s));
@@ -79,10 +82,11 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     constexpr float kLog2e = 1.4426950408889634f;
     EpiLceLogits<T> epi{z, p.vpad, p.part, p.nparts, 2.f * kLog2e / softcap, softcap * kLog2e};
     {
-      // the row-LSE partials assume 256 vocabulary columns per block tile
+      // one row-sum partial per block tile of vocab_tile columns: 256 -> configuration 9 (or an
+      // override with 256-wide tiles), 128 -> configuration 1 (or 7)
       const int oc = gemm_config_override();
-      const hipError_t e = launch_gemm_with((oc >= 2 && oc <= 6) || oc == 9 || oc == 10 ? oc : 9,
-                                            Hc, (int64_t)d, W, (int64_t)d, rows, (int)v, d, epi, GemmOps{}, s);
+      const int cfg = p.vtile == 128 ? (oc == 7 ? 7 : 1) : ((oc >= 2 && oc <= 6) || oc == 9 || oc == 10 ? oc : 9);
+      const hipError_t e = launch_gemm_with(cfg, Hc, (int64_t)d, W, (int64_t)d, rows, (int)v, d, epi, GemmOps{}, s);
       LL_HIP(e);
     }
     LL_LAUNCH("lce_lse", (lce_lse_kernel<T>), dim3((unsigned)cdiv(rows, kLseRows)), dim3(256), 0, s, p.part, p.nparts, z,
@@ -110,7 +114,7 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     const T* dzt = static_cast<const T*>(p.dzt);
     const T* ht = static_cast<const T*>(p.ht);
     if (p.single) {
-      EpiStore<T> ewd{dW, (int64_t)d, Deq{nullptr, nullptr}};
+      EpiStore<T> ewd{dW, (int64_t)d, Deq{nullptr, nullptr}, accumulate_dw};
       LL_HIP(launch_gemm(dzt, (int64_t)rows_pad, ht, (int64_t)rows_pad, (int)v, d, rows_pad, ewd, GemmOps{}, s));
     } else if (r0 + rows < n) {
       // fp32 sums over the chunks in dw32
@@ -118,11 +122,11 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
       LL_HIP(launch_gemm(dzt, (int64_t)rows_pad, ht, (int64_t)rows_pad, (int)v, d, rows_pad, ew, GemmOps{}, s));
     } else {
       // the last chunk's GEMM rounds the fp32 total into dW
-      EpiAcc32Out<T> ew{p.dw32, dW, (int64_t)d};
+      EpiAcc32Out<T> ew{p.dw32, dW, (int64_t)d, accumulate_dw};
       LL_HIP(launch_gemm(dzt, (int64_t)rows_pad, ht, (int64_t)rows_pad, (int)v, d, rows_pad, ew, GemmOps{}, s));
     }
   }
-  if (grads && n == 0) {                                   // no chunk ran: dW = 0
+  if (grads && n == 0 && !accumulate_dw) {                 // no chunk ran: dW = 0 (unchanged when accumulating)
     LL_HIP(fill_f32(p.dw32, 0.f, v * d, s));
     LL_HIP(launch_convert(p.dw32, dW, v * d, s));
   }
@@ -133,23 +137,31 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
 
 }  // namespace
 
-extern "C" size_t ll_fused_lce_workspace_bytes(int32_t dtype, int64_t n, int32_t d, int64_t v, int64_t token_chunk) {
+extern "C" size_t ll_fused_lce_workspace_bytes(int32_t dtype, int64_t n, int32_t d, int64_t v, int64_t token_chunk,
+                                               int32_t vocab_tile) {
   if ((dtype != LL_F32 && dtype != LL_BF16) || n < 0 || d <= 0 || v <= 0) return 0;
+  if (vocab_tile != 0 && vocab_tile != 128 && vocab_tile != 256) return 0;
   const int es = dtype == LL_F32 ? 4 : 2;
-  return plan_lce(nullptr, es, n, d, v, token_chunk, true).bytes;
+  return plan_lce(nullptr, es, n, d, v, token_chunk, vocab_tile, true).bytes;
 }
 
 extern "C" int ll_fused_lce_fwd_bwd(int32_t dtype, const void* hidden, const void* weight, const int32_t* targets,
                                     int64_t n, int32_t d, int64_t v, float softcap, int32_t ignore_index,
-                                    float grad_scale, int64_t token_chunk, float* loss, float* lse, void* d_hidden,
-                                    void* d_weight, void* ws, size_t ws_bytes, void* stream) {
+                                    float grad_scale, int64_t token_chunk, int32_t vocab_tile, int32_t accumulate_dw,
+                                    float* loss, float* lse, void* d_hidden, void* d_weight, void* ws,
+                                    size_t ws_bytes, void* stream) {
   LL_CHECK(dtype == LL_F32 || dtype == LL_BF16, LL_ERR_INVALID_ARG, "dtype must be LL_F32 or LL_BF16");
   LL_CHECK(n >= 0 && d > 0 && v > 0, LL_ERR_INVALID_ARG, "need n >= 0, d > 0, v > 0");
   LL_CHECK(d % (dtype == LL_F32 ? 32 : 64) == 0, LL_ERR_UNSUPPORTED, "d must be a multiple of 64 (bf16) / 32 (fp32)");
   LL_CHECK(v % 8 == 0, LL_ERR_UNSUPPORTED, "v must be a multiple of 8");
   LL_CHECK(v < (int64_t)1 << 31 && n < (int64_t)1 << 31, LL_ERR_UNSUPPORTED, "n and v must fit in int32");
-  LL_CHECK(softcap > 0.f, LL_ERR_INVALID_ARG, "softcap must be > 0");
+  // the row sums of exp(c) carry no running maximum: |c| <= softcap keeps v * e^softcap far below
+  // the fp32 range (3.4e38) for any vocabulary up to 10^12 rows when softcap <= 60
+  LL_CHECK(softcap > 0.f && softcap <= 60.f, LL_ERR_INVALID_ARG, "softcap must be in (0, 60]");
   LL_CHECK(token_chunk >= 0, LL_ERR_INVALID_ARG, "token_chunk must be >= 0");
+  LL_CHECK(vocab_tile == 0 || vocab_tile == 128 || vocab_tile == 256, LL_ERR_UNSUPPORTED,
+           "vocab_tile must be 0 (default 256), 128 or 256");
+  LL_CHECK(accumulate_dw == 0 || accumulate_dw == 1, LL_ERR_INVALID_ARG, "accumulate_dw must be 0 or 1");
   LL_CHECK(token_chunk == 0 || token_chunk <= (int64_t)65535 * 64, LL_ERR_UNSUPPORTED, "token_chunk too large");
   LL_CHECK(loss, LL_ERR_INVALID_ARG, "loss must not be null");
   LL_CHECK((d_hidden == nullptr) == (d_weight == nullptr), LL_ERR_INVALID_ARG, "d_hidden and d_weight: both or neither");
@@ -158,14 +170,16 @@ extern "C" int ll_fused_lce_fwd_bwd(int32_t dtype, const void* hidden, const voi
   LL_CHECK(!d_hidden || (aligned16(d_hidden) && aligned16(d_weight)), LL_ERR_INVALID_ARG, "gradients must be 16-byte aligned");
   const int es = dtype == LL_F32 ? 4 : 2;
   const bool grads = d_hidden != nullptr;
-  const size_t need = plan_lce(nullptr, es, n, d, v, token_chunk, grads).bytes;
+  const size_t need = plan_lce(nullptr, es, n, d, v, token_chunk, vocab_tile, grads).bytes;
   LL_CHECK(ws && aligned16(ws), LL_ERR_INVALID_ARG, "ws must be a 16-byte aligned device pointer");
   LL_CHECK(ws_bytes >= need, LL_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
-  const LcePlan p = plan_lce(ws, es, n, d, v, token_chunk, grads);
+  const LcePlan p = plan_lce(ws, es, n, d, v, token_chunk, vocab_tile, grads);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == LL_BF16)
     return run_lce(static_cast<const bf16*>(hidden), static_cast<const bf16*>(weight), targets, n, d, v, softcap,
-                   ignore_index, grad_scale, p, loss, lse, static_cast<bf16*>(d_hidden), static_cast<bf16*>(d_weight), s);
+                   ignore_index, grad_scale, p, loss, lse, static_cast<bf16*>(d_hidden), static_cast<bf16*>(d_weight),
+                   accumulate_dw, s);
   return run_lce(static_cast<const float*>(hidden), static_cast<const float*>(weight), targets, n, d, v, softcap,
-                 ignore_index, grad_scale, p, loss, lse, static_cast<float*>(d_hidden), static_cast<float*>(d_weight), s);
+                 ignore_index, grad_scale, p, loss, lse, static_cast<float*>(d_hidden), static_cast<float*>(d_weight),
+                 accumulate_dw, s);
 }

@@ -83,11 +83,11 @@ hipError_t norm_fwd(const void* x, const float* g, int64_t N, int D, float eps, 
 // dx = RMSNorm backward (no residual), dg = column sums of the per-wave partials in dgp (N > 0)
 template <class T>
 int norm_bwd(const void* dy, const void* x, const float* g, const float* rstd, int64_t N, int D, void* dx, float* dg,
-             float* dgp, hipStream_t s) {
+             float* dgp, int accumulate, hipStream_t s) {
   LL_HIP(launch_rmsnorm_bwd(static_cast<const T*>(dy), static_cast<const T*>(x), g, rstd, (const T*)nullptr,
                             static_cast<T*>(dx), dgp, N, D, (const float*)nullptr, (T*)nullptr, (const T*)nullptr,
                             (float*)nullptr, s));
-  LL_HIP(launch_colsum(dgp, rmsnorm_bwd_partials(N), D, dg, dgp + rmsnorm_bwd_partials(N) * D, s));
+  LL_HIP(launch_colsum(dgp, rmsnorm_bwd_partials(N), D, dg, dgp + rmsnorm_bwd_partials(N) * D, s, accumulate));
   return LL_OK;
 }
 
@@ -122,7 +122,7 @@ int make_plan(const ll_layer_cfg* cfg, int32_t n_layers, int64_t vocab, int64_t 
   m.N = c.batch * c.seq;
   m.D = c.d_model;
   m.es = c.dtype == LL_BF16 ? 2 : 4;
-  m.lce_ws = ll_fused_lce_workspace_bytes(c.dtype, std::max<int64_t>(m.N, 1), c.d_model, vocab, token_chunk);
+  m.lce_ws = ll_fused_lce_workspace_bytes(c.dtype, std::max<int64_t>(m.N, 1), c.d_model, vocab, token_chunk, 0);
   LL_CHECK(m.lce_ws > 0, LL_ERR_INVALID_ARG, "invalid head shape: " + std::string(ll_last_error()));
   m.act = (size_t)m.N * m.D * m.es;
   return LL_OK;
@@ -226,8 +226,8 @@ extern "C" int llt_rmsnorm_bwd(int32_t dtype, const void* dy, const void* x, con
     LL_HIP(fill_f32(dg, 0.f, d, s));
     return LL_OK;
   }
-  if (dtype == LL_BF16) return norm_bwd<bf16>(dy, x, g, rstd, n, d, dx, dg, dgp, s);
-  return norm_bwd<float>(dy, x, g, rstd, n, d, dx, dg, dgp, s);
+  if (dtype == LL_BF16) return norm_bwd<bf16>(dy, x, g, rstd, n, d, dx, dg, dgp, 0, s);
+  return norm_bwd<float>(dy, x, g, rstd, n, d, dx, dg, dgp, 0, s);
 }
 
 // ---------------------------------------------------------------- the model
@@ -259,7 +259,7 @@ extern "C" int ll_model_fwd_bwd(const ll_layer_cfg* cfg, int32_t n_layers, int64
            LL_ERR_INVALID_ARG, "null pointer in params/grads/loss");
   LL_CHECK(aligned16(p->embed) && aligned16(p->final_norm_w) && aligned16(p->head) && aligned16(g->head),
            LL_ERR_INVALID_ARG, "embed, final_norm_w and head (and its gradient) must be 16-byte aligned");
-  LL_CHECK(softcap > 0.f, LL_ERR_INVALID_ARG, "softcap must be > 0");
+  LL_CHECK(softcap > 0.f && softcap <= 60.f, LL_ERR_INVALID_ARG, "softcap must be in (0, 60]");
   LL_CHECK(m.N == 0 || (token_ids && targets), LL_ERR_INVALID_ARG, "token_ids and targets must not be null");
   ModelSaved sv;
   ModelWs w;
@@ -280,6 +280,7 @@ extern "C" int ll_model_fwd_bwd(const ll_layer_cfg* cfg, int32_t n_layers, int64
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = cfg->dtype == LL_BF16;
+  const int acc = g->accumulate ? 1 : 0;
   const int64_t N = m.N;
   const int D = m.D;
   const float eps = cfg->rms_eps;
@@ -296,26 +297,31 @@ extern "C" int ll_model_fwd_bwd(const ll_layer_cfg* cfg, int32_t n_layers, int64
   // head: loss and dL/d(final-norm output), dL/d(head)
   {
     const int st = ll_fused_lce_fwd_bwd(cfg->dtype, sv.hn, p->head, targets, N, D, vocab, softcap, ignore_index,
-                                        grad_scale, token_chunk, loss, nullptr, w.dh, g->head, w.inner, w.inner_bytes,
-                                        stream);
+                                        grad_scale, token_chunk, 0, acc, loss, nullptr, w.dh, g->head, w.inner,
+                                        w.inner_bytes, stream);
     LL_CHECK(st == LL_OK, st, std::string("head: ") + ll_last_error());
   }
   // backward
   if (N > 0) {
-    const int st = bf ? norm_bwd<bf16>(w.dh, sv.x[n_layers], p->final_norm_w, sv.rstd, N, D, w.d0, g->final_norm_w, w.dgp, s)
-                      : norm_bwd<float>(w.dh, sv.x[n_layers], p->final_norm_w, sv.rstd, N, D, w.d0, g->final_norm_w, w.dgp, s);
+    const int st = bf ? norm_bwd<bf16>(w.dh, sv.x[n_layers], p->final_norm_w, sv.rstd, N, D, w.d0, g->final_norm_w,
+                                       w.dgp, acc, s)
+                      : norm_bwd<float>(w.dh, sv.x[n_layers], p->final_norm_w, sv.rstd, N, D, w.d0, g->final_norm_w,
+                                        w.dgp, acc, s);
     if (st) return st;
-  } else {
+  } else if (!acc) {
     LL_HIP(fill_f32(g->final_norm_w, 0.f, D, s));
   }
   char* dcur = w.d0;
   char* dnext = w.d1;
   for (int i = n_layers - 1; i >= 0; --i) {
+    ll_layer_grads lg = g->layers[i];
+    lg.accumulate = acc;
     const int st = ll_layer_bwd(&lc[i], &p->layers[i], sv.x[i], token_ids, sv.layer[i], m.layer_saved, dcur, dnext,
-                                &g->layers[i], w.inner, w.inner_bytes, stream);
+                                &lg, w.inner, w.inner_bytes, stream);
     LL_CHECK(st == LL_OK, st, "layer " + std::to_string(i) + " backward: " + ll_last_error());
     std::swap(dcur, dnext);
   }
+  if (!acc) LL_HIP(fill_f32(g->embed, 0.f, vocab * D, s));   // overwrite: start the scatter-add from zero
   if (bf) LL_HIP(scatter<bf16>(dcur, token_ids, N, D, g->embed, vocab, s));
   else LL_HIP(scatter<float>(dcur, token_ids, N, D, g->embed, vocab, s));
   return LL_OK;

@@ -235,7 +235,8 @@ inline hipError_t launch_rmsnorm_bwd(const T* d, const T* x, const float* g, con
 // into mid[y][c]; then one block per 64 columns adds the S rows of mid in order. Deterministic.
 constexpr int kColsumSlabs = 32;
 __global__ void __launch_bounds__(1024)
-colsum_kernel(const float* __restrict__ part, int64_t P, int64_t stride, int D, float* __restrict__ out) {
+colsum_kernel(const float* __restrict__ part, int64_t P, int64_t stride, int D, float* __restrict__ out,
+              int accumulate) {
   __shared__ float red[16][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + lane;
@@ -248,19 +249,22 @@ colsum_kernel(const float* __restrict__ part, int64_t P, int64_t stride, int D, 
     float t = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) t += red[i][lane];
-    out[(int64_t)blockIdx.y * D + c] = t;
+    float* o = out + (int64_t)blockIdx.y * D + c;
+    *o = accumulate ? *o + t : t;
   }
 }
 
 // scratch: kColsumSlabs * D floats
 inline size_t colsum_scratch_floats(int D) { return (size_t)kColsumSlabs * D; }
-inline hipError_t launch_colsum(const float* part, int64_t P, int D, float* out, float* scratch, hipStream_t s) {
+// out = column sums of part [P, D] (out += with accumulate)
+inline hipError_t launch_colsum(const float* part, int64_t P, int D, float* out, float* scratch, hipStream_t s,
+                                int accumulate = 0) {
   LL_LAUNCH("colsum", colsum_kernel, dim3((unsigned)cdiv(D, 64), kColsumSlabs), dim3(1024), 0, s, part, P,
-            (int64_t)kColsumSlabs, D, scratch);
+            (int64_t)kColsumSlabs, D, scratch, 0);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   LL_LAUNCH("colsum", colsum_kernel, dim3((unsigned)cdiv(D, 64), 1), dim3(1024), 0, s, (const float*)scratch,
-            (int64_t)kColsumSlabs, (int64_t)1, D, out);
+            (int64_t)kColsumSlabs, (int64_t)1, D, out, accumulate);
   return hipGetLastError();
 }
 

@@ -80,12 +80,20 @@ __device__ __forceinline__ void scales_from_amax(float amax, float& scale, float
   inv = __fdiv_rn(1.0f, scale);                                   // exact for a power of two
 }
 
-// Codes of 4 values: clamp(fl32(x * scale), -448, 448) rounded to e4m3fn
+// Codes of 4 values: clamp(fl32(x * scale), -448, 448) rounded to e4m3fn; a NaN product (a NaN
+// input, or an infinite one times a zero scale) gives the NaN code 0x7F, so that a non-finite
+// activation reaches the GEMM as NaN instead of being clamped into a finite code
 __device__ __forceinline__ uint32_t quant4(const float* x, float scale) {
   float y[4];
+  uint32_t nan_bytes = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) y[k] = fminf(fmaxf(__fmul_rn(x[k], scale), -448.0f), 448.0f);
-  return f32x4_to_e4m3(y[0], y[1], y[2], y[3]);
+  for (int k = 0; k < 4; ++k) {
+    const float p = __fmul_rn(x[k], scale);
+    nan_bytes |= (p != p) ? (0xFFu << (8 * k)) : 0u;
+    y[k] = fminf(fmaxf(p, -448.0f), 448.0f);
+  }
+  const uint32_t c = f32x4_to_e4m3(y[0], y[1], y[2], y[3]);
+  return (c & ~nan_bytes) | (0x7F7F7F7Fu & nan_bytes);
 }
 
 // Cast of x [rows, cols] with the scale derived from qs->amax. Block = 128 x 128 tile, 256 threads;
@@ -127,7 +135,7 @@ cast_e4m3_kernel(const T* __restrict__ x, int64_t rows, int cols, int64_t ld, QS
       if constexpr (RELU2) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          const float p = fmaxf(v[k], 0.f);
+          const float p = relu_keep_nan(v[k]);
           v[k] = Elem<T>::rnd(p * p);
         }
       }

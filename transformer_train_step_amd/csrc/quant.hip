@@ -37,3 +37,4 @@ extern "C" int ll_fp8_quant_tensorwise(int32_t in_dtype, const void* x, int64_t 
   }
   return LL_OK;
 }
+

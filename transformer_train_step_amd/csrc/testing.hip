@@ -105,7 +105,7 @@ extern "C" int llt_gemm_splitk(int32_t op_dtype, int32_t a_kmajor, int32_t b_kma
 }
 
 extern "C" int llt_set_gemm_config(int32_t cfg) {
-  LL_CHECK(cfg >= 0 && cfg <= 11, LL_ERR_INVALID_ARG, "cfg must be in [0, 11]");
+  LL_CHECK(cfg >= 0 && cfg <= 13, LL_ERR_INVALID_ARG, "cfg must be in [0, 13]");
   set_gemm_config_override(cfg);
   return LL_OK;
 }
