@@ -257,6 +257,18 @@ int ll_fp8_quant_tensorwise(int32_t in_dtype, const void* x, int64_t rows, int64
                             int64_t ld, uint8_t* q, uint8_t* q_t, float* scale, float* inv_scale,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* ll_fp8_quant_tensorwise for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same arguments without the
+ * workspace, the same results bit for bit. Its scratch (the amax accumulator and the two scales,
+ * 16 bytes) lives in a static 256-byte device array, one per GPU, held until the process ends;
+ * the tensor-size limits are those of ll_fp8_quant_tensorwise (the scratch does not grow with the
+ * tensor). Every call on one GPU shares that array and leaves its contents behind (each call
+ * clears the amax itself before use): calls that overlap on one GPU, on different streams or
+ * threads, race and must be ordered by the caller. No hipMalloc, hipFree or other allocation. */
+int ll_fp8_quant_tensorwise_noalloc(int32_t in_dtype, const void* x, int64_t rows, int64_t cols,
+                                    int64_t ld, uint8_t* q, uint8_t* q_t, float* scale,
+                                    float* inv_scale, void* stream);
+
 /* Text of a status code, and a description of the last error raised by this library in the
  * calling thread (empty if none). */
 const char* ll_status_string(int status);

@@ -118,6 +118,9 @@ _SIGS = {
                                    ctypes.POINTER(c_size_t)]),
 }
 
+_SIGS["ll_fp8_quant_tensorwise_noalloc"] = (c_int32, [c_int32, c_void_p, c_int64, c_int64, c_int64, c_void_p,
+                                                      c_void_p, c_void_p, c_void_p, c_void_p])
+
 ENTRY_POINTS = tuple(_SIGS)
 
 
@@ -337,3 +340,8 @@ def llt_layer_buffer(cfg: LayerCfg, region: int, name: str):
     _call("llt_layer_buffer", ctypes.byref(cfg), region, name.encode(), ctypes.byref(off), ctypes.byref(nb))
     return off.value, nb.value
 
+
+def ll_fp8_quant_tensorwise_noalloc(in_dtype, x, rows, cols, ld, q, q_t, scale, inv_scale, stream=None,
+                                    raise_on_error=True):
+    return _call("ll_fp8_quant_tensorwise_noalloc", in_dtype, ptr(x), rows, cols, ld, ptr(q), ptr(q_t),
+                 ptr(scale), ptr(inv_scale), stream_handle(stream), raise_on_error=raise_on_error)
