@@ -8,7 +8,7 @@ layer backward from that gradient. Every kernel is libll's (HIP, gfx950); inputs
 HBM before the timed region. Prints one JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload layer_lce|layer|layer_ve_2k|lce|model|train|muon] [--no-cpu-baseline]
+                    [--workload layer_lce|layer|layer_swiglu|layer_ve_2k|lce|model|train|muon] [--no-cpu-baseline]
                     [--lce-chunk TOKENS] [--lce-vocab-tile 128|256] [--sweep-lce]
 
 FLOP accounting (algorithmic, not executed work): per token of one layer, fwd + bwd,
@@ -87,6 +87,9 @@ WORKLOADS = {
                            "+ fused linear cross-entropy fwd+bwd on its output (40960x3072 @ 50304x3072, softcap 15)"),
     "layer": dict(batch=40, seq=1024, ve=False, layer=True, lce=False,
                   desc="3.8B decoder layer fwd+bwd (40x1024 tokens, FP8 e4m3 MLP)"),
+    "layer_swiglu": dict(batch=40, seq=1024, ve=False, layer=True, lce=False, mlp="swiglu", d_ff=8448, fp8=False,
+                         desc="3.8B-width decoder layer fwd+bwd with the gated variant: bf16 SwiGLU MLP at 2.75x "
+                              "(d_ff 8448, W_fc 16896x3072 gate+up, W_proj 3072x8448), 40x1024 tokens"),
     "layer_ve_2k": dict(batch=20, seq=2048, ve=True, layer=True, lce=False,
                         desc="3.8B value-embedding decoder layer fwd+bwd (20x2048 tokens, FP8 e4m3 MLP)"),
     "lce": dict(batch=40, seq=1024, ve=False, layer=False, lce=True,
@@ -122,13 +125,16 @@ def step_flops(w: dict) -> int:
     n = w["batch"] * w["seq"]
     f = 0
     if w["layer"]:
-        f += w.get("layers", 1) * layer_flops_per_token(w["seq"]) * n
+        ff = w.get("d_ff", F)
+        p_mm = P_MM - 2 * D * F + (3 if w.get("mlp") == "swiglu" else 2) * D * ff
+        f += w.get("layers", 1) * layer_flops_per_token(w["seq"], p_mm=p_mm) * n
     if w["lce"]:
         f += lce_flops(n)
     return f * w.get("accum", 1)
 
 
-def cpu_baseline(seq: int, ve: bool, with_layer: bool, with_lce: bool, layers: int = 1) -> dict:
+def cpu_baseline(seq: int, ve: bool, with_layer: bool, with_lce: bool, layers: int = 1, mlp: str = "relu2",
+                 d_ff: int = F, fp8: bool = True) -> dict:
     """The oracle, as it stands, on a bounded sample: one sequence of `seq` tokens through the same
     step (layer fwd -> loss -> layer bwd) at full model width, float64 numpy on the host. With
     layers > 1 the layer part is timed once and counted `layers` times (the whole model would not
@@ -141,7 +147,7 @@ def cpu_baseline(seq: int, ve: bool, with_layer: bool, with_lce: bool, layers: i
         threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or os.cpu_count()
     except Exception:
         threads = os.cpu_count()
-    s = synth.LayerShape(batch=1, seq=seq, value_embed=ve)
+    s = synth.LayerShape(batch=1, seq=seq, value_embed=ve, mlp=mlp, d_ff=d_ff, fp8_mlp=fp8)
     inp = synth.layer_inputs(s, seed=0)
     if with_lce:
         w_head = synth.normal((V, D), 0.02, 0, synth.K_WHEAD, "bf16")
@@ -183,6 +189,11 @@ def main():
                     help="tokens per chunk of the fused linear cross-entropy (logits of one chunk are stored)")
     ap.add_argument("--lce-vocab-tile", type=int, default=256, choices=(128, 256),
                     help="vocabulary columns per partial row sum (the logits GEMM's N tile)")
+    ap.add_argument("--gemm-config", type=int, default=0, metavar="CFG",
+                    help="GEMM block configuration override for every GEMM (llt_set_gemm_config; 0 = automatic)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph after the warmup and time its replays (the same "
+                         "launches without the host's per-launch gaps)")
     ap.add_argument("--sweep-lce", action="store_true",
                     help="also time the loss alone over token_chunk x vocab_tile (reported as lce_sweep)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -204,6 +215,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     L.lib()
+    if args.gemm_config:
+        L.llt_set_gemm_config(args.gemm_config)
     w = WORKLOADS[args.workload]
     B, T = w["batch"], w["seq"]
     N = B * T
@@ -238,6 +251,17 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] warmup step {i + 1}/{args.warmup} done")
 
+    run = step
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
+        log("[bench] step captured in a HIP graph")
+
     # timed region: K steps, synchronised on both sides
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -245,7 +269,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        step()
+        run()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -258,14 +282,15 @@ def layer_lce_step(w, dev, torch, synth, LayerConfig, Layer, FusedLCE, to_dev, l
     """Inputs and the step closure of the layer / loss workloads (inputs drawn by synth)."""
     B, T = w["batch"], w["seq"]
     N = B * T
-    s = synth.LayerShape(batch=B, seq=T, value_embed=w["ve"])
+    mlp, ff, fp8 = w.get("mlp", "relu2"), w.get("d_ff", F), w.get("fp8", True)
+    s = synth.LayerShape(batch=B, seq=T, value_embed=w["ve"], mlp=mlp, d_ff=ff, fp8_mlp=fp8)
     inp = synth.layer_inputs(s, seed=0)
     x = to_dev(inp.x)
     ids = torch.from_numpy(inp.ids).to(dev)
     p = None
     layer = None
     if w["layer"]:
-        cfg = LayerConfig(batch=B, seq=T, value_embed=w["ve"])
+        cfg = LayerConfig(batch=B, seq=T, value_embed=w["ve"], mlp=mlp, d_ff=ff, fp8_mlp=fp8)
         layer = Layer(cfg, dev)
         p = {"attn_norm_w": torch.from_numpy(inp.g_attn).to(dev), "mlp_norm_w": torch.from_numpy(inp.g_mlp).to(dev),
              "w_qkv": to_dev(inp.w_qkv), "w_o": to_dev(inp.w_o), "w_fc": to_dev(inp.w_fc), "w_proj": to_dev(inp.w_proj),
@@ -382,10 +407,12 @@ def report(args, w, ms, step, stream, ev0, ev1, L, n_launch_trace):
     out = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16+e4m3",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16+e4m3" if w.get("fp8", True) and (w["layer"] or w.get("layers")) else "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, uniform token ids)",
         "config": {"workload": w["desc"], "tokens_per_step": N, "batch": B, "seq_len": T,
-                   "lce_token_chunk": args.lce_chunk, "lce_vocab_tile": args.lce_vocab_tile},
+                   "lce_token_chunk": args.lce_chunk, "lce_vocab_tile": args.lce_vocab_tile,
+                   "hip_graph": bool(args.graph), "gemm_config_override": args.gemm_config},
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
         "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / PEAK_BF16, 2),
         "algorithmic_flops_per_step": flops,
@@ -439,7 +466,8 @@ def report(args, w, ms, step, stream, ev0, ev1, L, n_launch_trace):
     if not args.no_cpu_baseline and not w.get("muon") and not w.get("accum"):
         log("[bench] timing the oracle on the host (bounded sample)...")
         seq = T if w["layer"] else 1024
-        out["cpu_baseline"] = cpu_baseline(seq, w["ve"], w["layer"], w["lce"], w.get("layers", 1))
+        out["cpu_baseline"] = cpu_baseline(seq, w["ve"], w["layer"], w["lce"], w.get("layers", 1),
+                                           w.get("mlp", "relu2"), w.get("d_ff", F), w.get("fp8", True))
         log(f"[bench] oracle: {out['cpu_baseline']['value']} tokens/s on {out['cpu_baseline']['cores']} threads")
     print(json.dumps(out), flush=True)
 
@@ -456,7 +484,7 @@ def lce_sweep(args, torch):
     y = torch.from_numpy(synth.uniform_ints((n,), V_REAL, 0, synth.K_TARGETS)).cuda()
     dh, dw = torch.empty_like(h), torch.empty_like(wt)
     res = []
-    for chunk in (4096, 8192, 10240, 20480):
+    for chunk in (8192, 10240, 20480, 40960):
         for tile in (128, 256):
             lce = FusedLCE("bf16", n, D, V, token_chunk=chunk, vocab_tile=tile)
             lce(h, wt, y, d_hidden=dh, d_weight=dw)

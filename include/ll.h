@@ -48,6 +48,11 @@ typedef enum {
 
 typedef enum { LL_F32 = 0, LL_BF16 = 1 } ll_dtype;
 
+/* MLP of the layer: the run's non-gated relu^2 MLP, or the gated SwiGLU MLP it replaced
+ * [linlog.top article, 吞吐量优化: removing the SwiGLU gate (three matmuls -> two) raised
+ * throughput; manulx summary: SwiGLU's intermediate ratio 2.75 vs 4 for relu^2]. */
+typedef enum { LL_MLP_RELU2 = 0, LL_MLP_SWIGLU = 1 } ll_mlp_kind;
+
 /* Static shape and precision of one decoder layer. */
 typedef struct {
   int32_t dtype;            /* ll_dtype of activations and weight matrices */
@@ -62,6 +67,9 @@ typedef struct {
   float rope_theta;         /* 10000 */
   int32_t has_value_embed;  /* 1 on value-embedding layers (v += ve_table[token_ids]) */
   int64_t ve_rows;          /* rows of ve_table (padded vocabulary, 50304) */
+  int32_t mlp_kind;         /* ll_mlp_kind. LL_MLP_SWIGLU: w_fc is [2 d_ff, D] (gate rows, then up
+                               rows), a = silu(x w_gate^T) (x w_up^T), m = a w_proj^T; bf16 / fp32
+                               GEMMs only (fp8_mlp must be 0); d_ff = 8448 = 2.75 D in the variant */
 } ll_layer_cfg;
 
 /* Parameters of one layer (read only). Matrices are in cfg.dtype; gains and scalars are fp32. */
@@ -70,7 +78,7 @@ typedef struct {
   const void* w_qkv;         /* [(Hq + 2 Hkv) * Dh, D]: q rows, then k rows, then v rows, head-major */
   const void* w_o;           /* [D, Hq * Dh] */
   const void* mlp_norm_w;    /* fp32 [D]: gain of the pre-MLP RMSNorm */
-  const void* w_fc;          /* [F, D] */
+  const void* w_fc;          /* [F, D] ([2F, D] for SwiGLU) */
   const void* w_proj;        /* [D, F] */
   const void* ve_table;      /* [ve_rows, Hkv * Dh] in cfg.dtype, or NULL when !has_value_embed */
   const float* resid_attn;   /* device fp32 scalar a_attn:  h = x + a_attn * attention branch */

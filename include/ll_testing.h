@@ -113,6 +113,15 @@ int llt_trace_get_gemm(int32_t i, int32_t* gemm_cfg, int32_t* slices);
  * Returns LL_ERR_INVALID_ARG for an invalid cfg or a name the configuration does not hold. */
 int llt_layer_buffer(const ll_layer_cfg* cfg, int32_t region, const char* name, size_t* offset, size_t* bytes);
 
+/* The cast step of the e4m3 quantiser alone, with the same device code as ll_fp8_quant_tensorwise
+ * and the layer's casts [hn.213312.xyz translation, 提升吞吐量 / Increasing throughput: FP8 with
+ * dynamic scaling], for a caller-chosen scale:
+ *   q[i] = e4m3fn_rne(clamp(fl32(x[i] * scale), -448, 448)), and the NaN code 0x7F where the
+ *   product is NaN (so +-inf inputs give +-448 at any nonzero scale).
+ * x: n fp32 values (device, 16-byte aligned); q: n bytes (device, 4-byte aligned); n % 4 == 0.
+ * Asynchronous on `stream`. Used to sweep every fp32 bit pattern against a host emulator. */
+int llt_e4m3_cast(const float* x, int64_t n, float scale, uint8_t* q, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

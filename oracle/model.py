@@ -200,6 +200,42 @@ def mlp_bwd(dm, c, w_fc, w_proj, fp8: bool, R):
 
 
 # ----------------------------------------------------------------------------------------------
+# SwiGLU MLP (the gated variant the run replaced by relu^2)
+# ----------------------------------------------------------------------------------------------
+def silu(x):
+    """x * sigmoid(x)."""
+    return x / (1.0 + np.exp(-x))
+
+
+def swiglu_mlp_fwd(hn, w_fc, w_proj, R):
+    """The gated MLP the pages ablated against relu^2 [linlog.top article, 吞吐量优化: SwiGLU has
+    three matmuls where relu^2 has two; manulx summary: intermediate ratio 2.75 for SwiGLU, 4x for
+    the non-gated MLP]: with w_fc [2F, D] holding the gate rows then the up rows,
+    [g | u] = hn w_fc^T,  a = silu(g) * u,  m = a w_proj^T  (w_proj [D, F]).
+    Rounded where the GPU path stores: [g | u], a, m. Returns (m, cache)."""
+    F = w_proj.shape[1]
+    gu = R(hn @ w_fc.T)
+    g, u = gu[:, :F], gu[:, F:]
+    a = R(silu(g) * u)
+    m = R(a @ w_proj.T)
+    return m, dict(hn=hn, gu=gu, a=a, m=m)
+
+
+def swiglu_mlp_bwd(dm, c, w_fc, w_proj, R):
+    """Backward of swiglu_mlp_fwd: da = dm w_proj; dg = da u silu'(g), du = da silu(g) with
+    silu'(g) = s (1 + g (1 - s)), s = sigmoid(g); returns (dhn, dW_fc, dW_proj)."""
+    F = w_proj.shape[1]
+    g, u = c["gu"][:, :F], c["gu"][:, F:]
+    da = R(dm @ w_proj)
+    sg = 1.0 / (1.0 + np.exp(-g))
+    dgu = R(np.concatenate([da * u * sg * (1.0 + g * (1.0 - sg)), da * g * sg], axis=1))
+    dw_proj = R(dm.T @ c["a"])
+    dw_fc = R(dgu.T @ c["hn"])
+    dhn = R(dgu @ w_fc)
+    return dhn, dw_fc, dw_proj
+
+
+# ----------------------------------------------------------------------------------------------
 # table rows picked by token ids (value embeddings; the model's token embedding)
 # ----------------------------------------------------------------------------------------------
 def gather_rows(table, ids):
@@ -228,7 +264,7 @@ def scatter_rows(d, ids, rows):
 class LayerParams:
     w_qkv: np.ndarray      # [(Hq + 2 Hkv) * Dh, D]: q rows, then k rows, then v rows, head-major
     w_o: np.ndarray        # [D, Hq * Dh]
-    w_fc: np.ndarray       # [F, D]
+    w_fc: np.ndarray       # [F, D] ([2F, D] for SwiGLU: gate rows, then up rows)
     w_proj: np.ndarray     # [D, F]
     g_attn: np.ndarray     # [D]
     g_mlp: np.ndarray      # [D]
@@ -248,6 +284,7 @@ class LayerDims:
     rope_theta: float = 10000.0
     fp8_mlp: bool = False
     mode: str = "bf16"
+    mlp: str = "relu2"        # "relu2" (the run's MLP) or "swiglu" (the ablated gated variant)
 
 
 def params_from_inputs(inp) -> LayerParams:
@@ -259,7 +296,7 @@ def params_from_inputs(inp) -> LayerParams:
 
 def dims_from_shape(s) -> LayerDims:
     return LayerDims(s.batch, s.seq, s.n_q_heads, s.n_kv_heads, s.head_dim, s.rms_eps,
-                     s.rope_theta, bool(s.fp8_mlp), s.dtype)
+                     s.rope_theta, bool(s.fp8_mlp), s.dtype, getattr(s, "mlp", "relu2"))
 
 
 def layer_fwd(p: LayerParams, x, ids, d: LayerDims):
@@ -288,7 +325,10 @@ def layer_fwd(p: LayerParams, x, ids, d: LayerDims):
     h = R(x + p.a_attn * attn_out)
     hn_raw, r2 = rmsnorm(h, p.g_mlp, d.rms_eps)
     hn = R(hn_raw)
-    m, mc = mlp_fwd(hn, p.w_fc, p.w_proj, d.fp8_mlp, R)
+    if d.mlp == "swiglu":
+        m, mc = swiglu_mlp_fwd(hn, p.w_fc, p.w_proj, R)
+    else:
+        m, mc = mlp_fwd(hn, p.w_fc, p.w_proj, d.fp8_mlp, R)
     c.update(mc)
     y = R(h + p.a_mlp * m)
     c.update(x=x, ids=ids, xn=xn, r1=r1, q=q, k=k, v=v, rq=rq, rk=rk, qh=qh, kh=kh, o=o, lse=lse,
@@ -308,7 +348,10 @@ def layer_bwd(p: LayerParams, c: dict, dy, d: LayerDims):
     # MLP residual branch
     g["a_mlp"] = float(np.sum(dy * c["m"]))
     dm = R(p.a_mlp * dy)
-    dhn, g["w_fc"], g["w_proj"] = mlp_bwd(dm, c, p.w_fc, p.w_proj, d.fp8_mlp, R)
+    if d.mlp == "swiglu":
+        dhn, g["w_fc"], g["w_proj"] = swiglu_mlp_bwd(dm, c, p.w_fc, p.w_proj, R)
+    else:
+        dhn, g["w_fc"], g["w_proj"] = mlp_bwd(dm, c, p.w_fc, p.w_proj, d.fp8_mlp, R)
     dh_norm, g["g_mlp"] = rmsnorm_bwd(dhn, c["h"], p.g_mlp, c["r2"])
     dh = R(dy + dh_norm)
     # attention residual branch

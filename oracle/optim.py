@@ -77,19 +77,28 @@ def muon_update(w, g, buf, lr: float = 0.02, momentum: float = 0.95, nesterov: b
     return R(w * (1.0 - lr * weight_decay) - lr * scale * o), buf
 
 
+def adamw_param_update(p, m, v, step: int, lr: float, beta1: float, beta2: float, eps: float,
+                       weight_decay: float, mode: str = "fp32"):
+    """The parameter half of one AdamW step, from the step's updated moments m and v:
+    p (1 - lr wd) - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps), rounded by mode."""
+    R = _rounder(mode)
+    p = np.asarray(p, np.float64)
+    m = np.asarray(m, np.float64)
+    v = np.asarray(v, np.float64)
+    bc1 = 1.0 - beta1 ** step
+    bc2 = 1.0 - beta2 ** step
+    return R(p * (1.0 - lr * weight_decay) - lr * (m / bc1) / (np.sqrt(v / bc2) + eps))
+
+
 def adamw_update(p, g, m, v, step: int, lr: float, beta1: float, beta2: float, eps: float,
                  weight_decay: float, mode: str = "fp32", state_mode: str | None = None):
     """One AdamW step (module docstring) at step number `step` (1 for the first). mode rounds the
     parameter, state_mode (default: mode) the two moments. Returns (new p, new m, new v)."""
-    R = _rounder(mode)
     Rs = _rounder(state_mode or mode)
-    p = np.asarray(p, np.float64)
     g = np.asarray(g, np.float64)
     m = Rs(beta1 * np.asarray(m, np.float64) + (1.0 - beta1) * g)
     v = Rs(beta2 * np.asarray(v, np.float64) + (1.0 - beta2) * g * g)
-    bc1 = 1.0 - beta1 ** step
-    bc2 = 1.0 - beta2 ** step
-    p = R(p * (1.0 - lr * weight_decay) - lr * (m / bc1) / (np.sqrt(v / bc2) + eps))
+    p = adamw_param_update(p, m, v, step, lr, beta1, beta2, eps, weight_decay, mode)
     return p, m, v
 
 

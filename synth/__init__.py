@@ -77,6 +77,7 @@ class LayerShape:
     value_embed: bool = False
     rms_eps: float = 1e-6
     rope_theta: float = 10000.0
+    mlp: str = "relu2"          # "relu2", or "swiglu" (w_fc then holds 2 * d_ff rows: gate, then up)
 
     @property
     def tokens(self) -> int:
@@ -123,7 +124,7 @@ def layer_inputs(s: LayerShape, seed: int = 0, layer: int = 0, perturb: bool = F
     dy = normal((N, D), dy_std, seed, K_DY + o, dt)
     w_qkv = normal((s.qkv_dim, D), w_std, seed, K_WQKV + o, dt)
     w_o = normal((D, s.n_q_heads * s.head_dim), w_std, seed, K_WO + o, dt)
-    w_fc = normal((s.d_ff, D), w_std, seed, K_W1 + o, dt)
+    w_fc = normal(((2 if s.mlp == "swiglu" else 1) * s.d_ff, D), w_std, seed, K_W1 + o, dt)
     w_proj = normal((D, s.d_ff), w_std, seed, K_W2 + o, dt)
     if perturb:
         g1 = (1.0 + 0.1 * rng(seed, K_G1 + o).standard_normal(D)).astype(np.float32)

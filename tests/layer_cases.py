@@ -18,7 +18,7 @@ def config_of(s: synth.LayerShape) -> LayerConfig:
     return LayerConfig(batch=s.batch, seq=s.seq, d_model=s.d_model, n_q_heads=s.n_q_heads,
                        n_kv_heads=s.n_kv_heads, head_dim=s.head_dim, d_ff=s.d_ff, dtype=s.dtype,
                        fp8_mlp=s.fp8_mlp, value_embed=s.value_embed, ve_rows=s.vocab,
-                       rms_eps=s.rms_eps, rope_theta=s.rope_theta)
+                       rms_eps=s.rms_eps, rope_theta=s.rope_theta, mlp=s.mlp)
 
 
 def _dev(a, dt):

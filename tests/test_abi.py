@@ -67,6 +67,14 @@ def test_layer_size_queries_and_validation():
     saved, ws = ll.ll_layer_saved_bytes(c), ll.ll_layer_workspace_bytes(c)
     assert saved > 40 * 1024 * 3072 * 2 * 8 and ws > 0
     assert saved + ws < 200 * 2 ** 30                  # fits one MI355X (288 GB) with room to spare
+    sw8 = LayerConfig(batch=2, seq=8, mlp="swiglu").c_struct()        # SwiGLU with FP8 GEMMs
+    assert ll.ll_layer_saved_bytes(sw8) == 0 and ll.ll_layer_workspace_bytes(sw8) == 0
+    sw = LayerConfig(batch=2, seq=8, mlp="swiglu", fp8_mlp=False, d_ff=8448).c_struct()
+    assert ll.ll_layer_saved_bytes(sw) > ll.ll_layer_saved_bytes(
+        LayerConfig(batch=2, seq=8, fp8_mlp=False, d_ff=8448).c_struct())
+    odd = LayerConfig(batch=2, seq=8).c_struct()
+    odd.mlp_kind = 7
+    assert ll.ll_layer_saved_bytes(odd) == 0
     bad = LayerConfig(batch=2, seq=8, dtype="fp32", fp8_mlp=True, head_dim=64).c_struct()
     assert ll.ll_layer_saved_bytes(bad) == 0
     keep, p = _fake()

@@ -85,6 +85,22 @@ def test_layer_bf16_real_dims(batch, seq, fp8, ve, seed):
     _compare(gpu, ref, 2e-2, None, BARS_FP8 if fp8 else BARS_BF16)
 
 
+@pytest.mark.parametrize("dtype,batch,seq,d,hq,hkv,dh,f,rtol", [
+    ("fp32", 2, 37, 256, 4, 2, 64, 768, 1e-5),        # tiny fp32, ragged T
+    ("bf16", 1, 130, 3072, 24, 8, 128, 8448, 2e-2),   # the 3.8B width with the 2.75x SwiGLU MLP
+])
+def test_layer_swiglu_variant(dtype, batch, seq, d, hq, hkv, dh, f, rtol):
+    """The gated SwiGLU MLP the run replaced by relu^2: forward and backward against the oracle."""
+    need_gpu()
+    s = synth.LayerShape(batch=batch, seq=seq, d_model=d, n_q_heads=hq, n_kv_heads=hkv, head_dim=dh, d_ff=f,
+                         vocab=512 if dtype == "fp32" else 50304, real_vocab=512 if dtype == "fp32" else 50257,
+                         dtype=dtype, fp8_mlp=False, value_embed=dtype == "fp32", mlp="swiglu")
+    inp = synth.layer_inputs(s, seed=70, perturb=True)
+    print(f"layer swiglu {dtype} {batch}x{seq} F={f}", flush=True)
+    gpu, ref = run_gpu(inp), run_oracle(inp)
+    _compare(gpu, ref, rtol, 1e-3 if dtype == "fp32" else None, None if dtype == "fp32" else BARS_BF16)
+
+
 def test_tiny_fp32_layer_ragged_and_single_token():
     need_gpu()
     for b, t in ((3, 37), (1, 1)):

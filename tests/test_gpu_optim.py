@@ -4,12 +4,16 @@ tall ones transposed into the wide orientation), and AdamW on bf16 parameters wi
 gradients and on fp32 parameters, over three steps with a ragged element count.
 
 Hyperparameters reach the kernels as fp32 values, so the oracle is called with the same fp32
-values. Bars: the momentum buffer and the AdamW moments and bf16 parameters agree with the oracle
-to within one bf16 ulp on at most 1e-3 of the elements, plus 2^-20 of the magnitude of the terms
-summed where they cancel (the GPU forms each value in fp32, the oracle in float64, and both round
-once where the value is stored); fp32 state to 2^-20 of that magnitude; the Muon update
-w_new - w (bf16 iterates rounded at the same points on both sides) within 2e-2 norm-wise, and
-every row within 5e-2 of its norm."""
+values. Every stored bf16 value is checked against the oracle given the GPU's own inputs to that
+step: within one bf16 ulp (plus 2^-20 of the magnitude of the terms summed, which matters only
+where they cancel), with at most 5% of the elements one ulp apart. The kernels evaluate each
+chain in fp32 and round that to bf16; the oracle rounds the exact value once, and the two roundings
+differ in up to ~1.5% of the elements for inputs that are themselves bf16 values (measured; an
+fp32 emulation on the host gives the same fraction). The Newton-Schulz output itself (lr 1, no
+momentum, w = 0, so that w_new is the orthogonalised matrix exactly) is compared at 2e-2
+norm-wise (measured 0.38% after 5 steps). A Muon update w_new - w on realistic weights is smaller
+than the weights' bf16 resolution allows to compare norm-wise (one ulp of |w| ~ 0.02 is ~10% of
+the update), so w_new is checked in ulps."""
 import numpy as np
 import pytest
 import torch
@@ -27,7 +31,21 @@ pytestmark = pytest.mark.gpu
 # iteration's cancellation (a X + B X with a = 3.4 and a result near 0.7) amplifies those flips.
 # An fp32-accumulation emulation of the same iteration on the host differs from the float64 one by
 # 0.4% norm-wise after 5 steps; the bound leaves 5x room.
-MUON_RTOL, MUON_ELEM, MUON_ROW = 2e-2, 0.25, 5e-2
+MUON_RTOL, MUON_ELEM, MUON_ROW = 2e-2, 0.1, 5e-2
+FLIP_FRAC = 0.05          # stored bf16 values one ulp apart (fp32-then-bf16 vs exact-then-bf16)
+
+
+def check_muon_w(got, ref, w0, name, elem=MUON_ELEM):
+    """w_new = round(w - lr s X): each element within one bf16 ulp of the oracle's plus `elem` of
+    (|update| + rms(update)) - the orthogonalised matrices X agree to 0.4% norm-wise and their
+    elements to ~2% of (|X| + rms(X)) (test_newton_schulz_iterates_vs_oracle), and where w and the
+    update cancel that is many ulps of the small result."""
+    upd = np.abs(ref - w0)
+    rms = np.sqrt(np.mean(upd * upd))
+    slack = _ulp(ref) * 1.0001 + elem * (upd + rms)
+    bad = np.abs(got - ref) > slack
+    worst = float(np.max((np.abs(got - ref) - _ulp(ref)) / (upd + rms)))
+    assert not bad.any(), f"{name}: {int(bad.sum())} elements beyond the bound (worst {worst:.3f} of |upd| + rms)"
 
 
 def _bf(a):
@@ -79,10 +97,10 @@ def test_muon_step_vs_oracle(rows, cols, nesterov):
     ll._lib.ll_muon_step(ll.LL_BF16, W, G, B, rows, cols, lr, mu, nesterov, 0.0, 5, ws, ws.numel())
     torch.cuda.synchronize()
     w_ref, buf_ref = oo.muon_update(w, g, buf, lr=lr, momentum=mu, nesterov=bool(nesterov), mode="bf16")
-    _ulp_close(_h(B), buf_ref, "momentum buffer", scale=np.abs(mu * buf) + np.abs(g))
+    _ulp_close(_h(B), buf_ref, "momentum buffer", frac=FLIP_FRAC, scale=np.abs(mu * buf) + np.abs(g))
     upd, upd_ref = _h(W) - w, w_ref - w
     print("update", error_stats(upd, upd_ref), flush=True)
-    assert_close(upd, upd_ref, MUON_RTOL, "update", elem_rtol=MUON_ELEM, row_rtol=MUON_ROW)
+    check_muon_w(_h(W), w_ref, w, "w")
 
 
 @pytest.mark.parametrize("steps", [0, 1, 2, 5])
@@ -153,19 +171,19 @@ def test_adamw_step_vs_oracle(group, pdt, gdt):
         torch.cuda.synchronize()
         b1, b2 = h["betas"]
         m_scale = np.abs(b1 * m) + np.abs((1 - b1) * g)
-        p_prev = p
-        p, m, v = oo.adamw_update(p, g, m, v, step, h["lr"], b1, b2, h["eps"], h["weight_decay"], mode=pdt)
+        # the moments from the previous (GPU) state, the parameter from the GPU's new moments, so
+        # that each stored value is checked on its own inputs
+        _, m_ref, v_ref = oo.adamw_update(p, g, m, v, step, h["lr"], b1, b2, h["eps"], h["weight_decay"], mode=pdt)
+        gm, gv, gp = _h(M), _h(V), _h(P)
+        p_ref = oo.adamw_param_update(p, gm, gv, step, h["lr"], b1, b2, h["eps"], h["weight_decay"], mode=pdt)
+        p_scale = np.abs(p) + np.abs(p_ref - p)
         if pdt == "bf16":
-            _ulp_close(_h(M), m, f"m step {step}", scale=m_scale)
-            _ulp_close(_h(V), v, f"v step {step}")
-            # p = p (1 - lr wd) - update: the terms' magnitudes are |p| and |p_prev - p|
-            _ulp_close(_h(P), p, f"p step {step}", scale=np.abs(p_prev) + np.abs(p_prev - p))
-            # keep the oracle on the GPU's state so that one-ulp differences do not compound
-            p, m, v = _h(P), _h(M), _h(V)
+            _ulp_close(gm, m_ref, f"m step {step}", frac=FLIP_FRAC, scale=m_scale)
+            _ulp_close(gv, v_ref, f"v step {step}", frac=FLIP_FRAC)
+            _ulp_close(gp, p_ref, f"p step {step}", frac=FLIP_FRAC, scale=p_scale)
         else:
             # fp32 state: a few fp32 roundings, relative to the magnitudes of the terms summed
-            for name, a, b, sc in (("p", _h(P), p, np.abs(p_prev) + np.abs(p_prev - p)), ("m", _h(M), m, m_scale),
-                                   ("v", _h(V), v, np.abs(v))):
+            for name, a, b, sc in (("p", gp, p_ref, p_scale), ("m", gm, m_ref, m_scale), ("v", gv, v_ref, np.abs(v_ref))):
                 bad = np.abs(a - b) > 2.0 ** -20 * sc + 1e-30
                 assert not bad.any(), (name, step, int(bad.sum()), a[bad][:3], b[bad][:3])
-            p, m, v = _h(P), _h(M), _h(V)
+        p, m, v = gp, gm, gv

@@ -321,3 +321,72 @@ def test_gather_and_scatter_rows_out_of_range_ids():
     np.testing.assert_array_equal(om.gather_rows(table, ids), onehot @ table)
     d = rng.standard_normal((len(ids), 3))
     np.testing.assert_allclose(om.scatter_rows(d, ids, 6), onehot.T @ d, rtol=1e-14)
+
+
+# ---------------------------------------------------------------- SwiGLU variant
+def test_swiglu_mlp_matches_torch_autograd():
+    """The gated MLP against torch float64 (F.silu, autograd as an independent backward)."""
+    rng = np.random.default_rng(20)
+    N, D, F = 12, 32, 40
+    hn = rng.standard_normal((N, D))
+    w_fc = rng.standard_normal((2 * F, D)) * 0.3
+    w_proj = rng.standard_normal((D, F)) * 0.3
+    dm = rng.standard_normal((N, D))
+    R = om.rounder("fp32")
+    m, c = om.swiglu_mlp_fwd(hn, w_fc, w_proj, R)
+    dhn, dw_fc, dw_proj = om.swiglu_mlp_bwd(dm, c, w_fc, w_proj, R)
+    th, t1, t2 = _t(hn).requires_grad_(), _t(w_fc).requires_grad_(), _t(w_proj).requires_grad_()
+    gu = th @ t1.T
+    mt = (F_silu(gu[:, :F]) * gu[:, F:]) @ t2.T
+    np.testing.assert_allclose(m, mt.detach().numpy(), rtol=1e-12, atol=1e-12)
+    mt.backward(_t(dm))
+    np.testing.assert_allclose(dhn, th.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dw_fc, t1.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dw_proj, t2.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def F_silu(x):
+    return torch.nn.functional.silu(x)
+
+
+def test_swiglu_layer_finite_differences_and_planted_mistake(monkeypatch):
+    """The whole layer with the SwiGLU MLP in fp32 mode: central finite differences along random
+    directions of x and both MLP weights; a planted mistake (silu'(g) taken as sigmoid(g)) fails."""
+    s = synth.LayerShape(batch=1, seq=12, d_model=32, n_q_heads=4, n_kv_heads=2, head_dim=8, d_ff=24, vocab=40,
+                         real_vocab=40, dtype="fp32", fp8_mlp=False, value_embed=False, mlp="swiglu")
+    inp = synth.layer_inputs(s, seed=21, perturb=True, w_std=0.2)
+    p, d = om.params_from_inputs(inp), om.dims_from_shape(s)
+    assert p.w_fc.shape == (48, 32)
+    rng = np.random.default_rng(21)
+    dy = np.asarray(inp.dy, np.float64)
+    y, cache = om.layer_fwd(p, inp.x, inp.ids, d)
+    g = om.layer_bwd(p, cache, dy, d)
+    L = lambda yy: float(np.sum(yy * dy))
+    eps = 1e-6
+    x0 = np.asarray(inp.x, np.float64)
+    for name in ("x", "w_fc", "w_proj"):
+        base = x0 if name == "x" else getattr(p, name)
+        u = rng.standard_normal(np.shape(base))
+        def f(sign):
+            if name == "x":
+                return L(om.layer_fwd(p, x0 + sign * eps * u, inp.ids, d)[0])
+            q = om.LayerParams(**{**p.__dict__, name: base + sign * eps * u})
+            return L(om.layer_fwd(q, x0, inp.ids, d)[0])
+        fd = (f(1) - f(-1)) / (2 * eps)
+        an = float(np.sum(np.asarray(g["dx" if name == "x" else name]) * u))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), name
+    # planted: the gradient through silu without its (1 + g (1 - s)) factor
+    real_exp = np.exp
+    calls = {"n": 0}
+    def planted_bwd(dm, c, w_fc, w_proj, R):
+        F_ = w_proj.shape[1]
+        gg, uu = c["gu"][:, :F_], c["gu"][:, F_:]
+        da = R(dm @ w_proj)
+        sg = 1.0 / (1.0 + real_exp(-gg))
+        dgu = R(np.concatenate([da * uu * sg, da * gg * sg], axis=1))
+        return R(dgu @ w_fc), R(dgu.T @ c["hn"]), R(dm.T @ c["a"])
+    monkeypatch.setattr(om, "swiglu_mlp_bwd", planted_bwd)
+    gb = om.layer_bwd(p, cache, dy, d)
+    u = rng.standard_normal(x0.shape)
+    fd = (L(om.layer_fwd(p, x0 + eps * u, inp.ids, d)[0]) - L(om.layer_fwd(p, x0 - eps * u, inp.ids, d)[0])) / (2 * eps)
+    assert abs(fd - float(np.sum(gb["dx"] * u))) > 1e-4 * abs(fd)

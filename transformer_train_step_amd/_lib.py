@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libll.so")
 
 LL_OK, LL_ERR_INVALID_ARG, LL_ERR_UNSUPPORTED, LL_ERR_WORKSPACE, LL_ERR_HIP = 0, 1, 2, 3, 4
 LL_F32, LL_BF16 = 0, 1
+LL_MLP_RELU2, LL_MLP_SWIGLU = 0, 1
 LLT_OP_F32, LLT_OP_BF16, LLT_OP_E4M3 = 0, 1, 2
 
 c_void_p, c_int32, c_int64, c_size_t, c_float = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
@@ -32,7 +33,8 @@ class LayerCfg(ctypes.Structure):
     _fields_ = [("dtype", c_int32), ("fp8_mlp", c_int32), ("batch", c_int64), ("seq", c_int64),
                 ("d_model", c_int32), ("n_q_heads", c_int32), ("n_kv_heads", c_int32),
                 ("head_dim", c_int32), ("d_ff", c_int32), ("rms_eps", c_float),
-                ("rope_theta", c_float), ("has_value_embed", c_int32), ("ve_rows", c_int64)]
+                ("rope_theta", c_float), ("has_value_embed", c_int32), ("ve_rows", c_int64),
+                ("mlp_kind", c_int32)]
 
 
 class LayerParams(ctypes.Structure):
@@ -116,8 +118,8 @@ _SIGS = {
                                 c_float, c_float, c_float, c_int64, c_void_p]),
     "llt_layer_buffer": (c_int32, [ctypes.POINTER(LayerCfg), c_int32, ctypes.c_char_p, ctypes.POINTER(c_size_t),
                                    ctypes.POINTER(c_size_t)]),
+    "llt_e4m3_cast": (c_int32, [c_void_p, c_int64, c_float, c_void_p, c_void_p]),
 }
-
 _SIGS["ll_fp8_quant_tensorwise_noalloc"] = (c_int32, [c_int32, c_void_p, c_int64, c_int64, c_int64, c_void_p,
                                                       c_void_p, c_void_p, c_void_p, c_void_p])
 
@@ -341,7 +343,27 @@ def llt_layer_buffer(cfg: LayerCfg, region: int, name: str):
     return off.value, nb.value
 
 
+def llt_e4m3_cast(x, n: int, scale: float, q, stream=None, raise_on_error=True):
+    return _call("llt_e4m3_cast", ptr(x), n, scale, ptr(q), stream_handle(stream), raise_on_error=raise_on_error)
+
+
 def ll_fp8_quant_tensorwise_noalloc(in_dtype, x, rows, cols, ld, q, q_t, scale, inv_scale, stream=None,
                                     raise_on_error=True):
     return _call("ll_fp8_quant_tensorwise_noalloc", in_dtype, ptr(x), rows, cols, ld, ptr(q), ptr(q_t),
                  ptr(scale), ptr(inv_scale), stream_handle(stream), raise_on_error=raise_on_error)
+
+
+def ll_muon_workspace_bytes(rows: int, cols: int) -> int:
+    return lib().ll_muon_workspace_bytes(rows, cols)
+
+
+def ll_muon_step(dtype, w, grad, momentum_buf, rows, cols, lr, momentum, nesterov, weight_decay, ns_steps, ws,
+                 ws_bytes, stream=None, raise_on_error=True):
+    return _call("ll_muon_step", dtype, ptr(w), ptr(grad), ptr(momentum_buf), rows, cols, lr, momentum, int(nesterov),
+                 weight_decay, ns_steps, ptr(ws), ws_bytes, stream_handle(stream), raise_on_error=raise_on_error)
+
+
+def ll_adamw_step(param_dtype, grad_dtype, param, grad, exp_avg, exp_avg_sq, n, lr, beta1, beta2, eps,
+                  weight_decay, step, stream=None, raise_on_error=True):
+    return _call("ll_adamw_step", param_dtype, grad_dtype, ptr(param), ptr(grad), ptr(exp_avg), ptr(exp_avg_sq), n,
+                 lr, beta1, beta2, eps, weight_decay, step, stream_handle(stream), raise_on_error=raise_on_error)

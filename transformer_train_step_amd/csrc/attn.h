@@ -39,21 +39,22 @@ __global__ void rope_table_kernel(float2* cs, int T, int half, double theta) {
 // ------------------------------------------------------------------ QK-norm + RoPE (forward)
 // A head vector is handled by DH/16 consecutive lanes, each owning 8 consecutive rotation pairs
 // (i, i + DH/2), i = i0 .. i0 + 7: 16-byte loads and stores, the sum of squares reduced across the
-// head's lanes by DPP. Heads 0..Hq-1 of a token are q heads, Hq..Hq+Hkv-1 k heads.
+// head's lanes by DPP. Heads 0..Hq-1 of a token are q heads, Hq..Hq+Hkv-1 k heads; the kernel takes
+// the Hp heads h0 .. h0 + Hp - 1 of every token (all of them, or only the k heads when the
+// attention forward normalises and rotates q itself as it loads it).
 template <class T, int DH>
 __global__ void __launch_bounds__(256)
 qk_prep_kernel(const T* __restrict__ qkv, int64_t ldqkv, const float2* __restrict__ cs, T* __restrict__ qh,
                T* __restrict__ kh, float* __restrict__ rq, float* __restrict__ rk, int64_t N, int T_, int Hq,
-               int Hkv, float eps) {
+               int Hkv, float eps, int h0, int Hp) {
   constexpr int P = DH / 2, TPH = P / 8;
   static_assert(P % 8 == 0 && 64 % TPH == 0, "head_dim a multiple of 16, at most 128 per 8 lanes");
   const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  const int H = Hq + Hkv;
   const int i0 = (int)(gid % TPH) * 8;
   const int64_t ht = gid / TPH;
-  const bool valid = ht < N * H;
-  const int64_t n = valid ? ht / H : 0;
-  const int hh = valid ? (int)(ht % H) : 0;
+  const bool valid = ht < N * Hp;
+  const int64_t n = valid ? ht / Hp : 0;
+  const int hh = valid ? h0 + (int)(ht % Hp) : 0;
   float a[8], b[8];
   if (valid) {
     const T* src = qkv + n * ldqkv + (int64_t)hh * DH;

@@ -121,13 +121,21 @@ __device__ __forceinline__ FaBlock fa_block(int B, int Hq, int Hkv, int nblk) {
 
 // ------------------------------------------------------------------ forward
 // Block: one (b, h) and 128 queries, wave w the 32 queries q0 + 32 w .. (Q in registers as the
-// `second` operand). Per 64-key tile: S^T = K Q^T (lane: query column, 4 key rows), online softmax
-// in the exp2 domain, O^T += V^T P^T with P split into bf16 high and low parts. Writes o [N, Hq*128]
-// and lse [B, Hq, ldl] (natural log; entries of queries >= T untouched).
+// `second` operand). QK-norm and RoPE of q happen in this load: lane (c16, g) reads elements
+// 8 g + 32 c .. + 7 (c = 0..3) of its query's raw head vector from the QKV projection, so the
+// rotation pairs (i, i + 64) are chunks c and c + 2 of the same lane and the head's sum of squares
+// is the sum over the 4 lanes g = 0..3; the lane rounds q^ = RoPE(q / rms(q)) to bf16 as the MFMA
+// operand and writes q^ and 1 / rms(q) for the backward. Per 64-key tile: S^T = K Q^T (lane: query
+// column, 4 key rows), online softmax in the exp2 domain, O^T += V^T P^T with P split into bf16
+// high and low parts. Writes o [N, Hq*128] and lse [B, Hq, ldl] (natural log; entries of queries
+// >= T untouched).
+//   qkv [N, ldqkv]: q of head h at columns h * 128 ..; cs [T, 64] (cos, sin) of the RoPE angles;
+//   qh [N, Hq * 128] and rq [N, Hq] are written.
 template <bool kSplit>
 __global__ void __launch_bounds__(256, 2)
-fa_fwd_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const bf16* __restrict__ v, int64_t ldv,
-              bf16* __restrict__ o, float* __restrict__ lse, int64_t ldl, int B, int T, int Hq, int Hkv) {
+fa_fwd_kernel(const bf16* __restrict__ qkv, int64_t ldqkv, const float2* __restrict__ cs, float eps,
+              bf16* __restrict__ qh, float* __restrict__ rq, const bf16* __restrict__ kh, const bf16* __restrict__ v,
+              int64_t ldv, bf16* __restrict__ o, float* __restrict__ lse, int64_t ldl, int B, int T, int Hq, int Hkv) {
   constexpr int DH = 128, STAGE = 2 * 64 * 256;
   __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE];
@@ -141,10 +149,44 @@ fa_fwd_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const bf
   u32x4 qf[2][4];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int q = min(qw + 16 * j + c16, T - 1);
-    const bf16* rowp = qh + (((int64_t)b * T + q) * Hq + h) * DH + 8 * g;
+    const int qq = qw + 16 * j + c16, q = min(qq, T - 1);
+    const bf16* rowp = qkv + ((int64_t)b * T + q) * ldqkv + (int64_t)h * DH + 8 * g;
+    float x[4][8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qf[j][c] = *reinterpret_cast<const u32x4*>(rowp + 32 * c);
+    for (int c = 0; c < 4; ++c) Vec8<bf16>::load(rowp + 32 * c, x[c]);
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[c][e] * x[c][e];
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float r = 1.0f / sqrtf(ss / (float)DH + eps);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      // (cos, sin) of pairs i = 32 c + 8 g .. + 7
+      const float4* c4 = reinterpret_cast<const float4*>(cs + (int64_t)q * (DH / 2) + 32 * c + 8 * g);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 cc = c4[u];
+        const float cv[2] = {cc.x, cc.z}, sv[2] = {cc.y, cc.w};
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const int e = 2 * u + e2;
+          const float a0 = x[c][e] * r, a1 = x[c + 2][e] * r;
+          x[c][e] = a0 * cv[e2] - a1 * sv[e2];
+          x[c + 2][e] = a0 * sv[e2] + a1 * cv[e2];
+        }
+      }
+    }
+    bf16* qrow = qh + (((int64_t)b * T + q) * Hq + h) * DH + 8 * g;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      qf[j][c] = u32x4{fa_pack(x[c][0], x[c][1]), fa_pack(x[c][2], x[c][3]), fa_pack(x[c][4], x[c][5]),
+                       fa_pack(x[c][6], x[c][7])};
+      if (qq < T) *reinterpret_cast<u32x4*>(qrow + 32 * c) = qf[j][c];
+    }
+    if (qq < T && g == 0) rq[((int64_t)b * T + q) * Hq + h] = r;
   }
   const bf16* kb = kh + ((int64_t)b * T * Hkv + hk) * DH;
   const bf16* vb = v + (int64_t)b * T * ldv + (int64_t)hk * DH;

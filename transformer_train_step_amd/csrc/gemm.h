@@ -146,6 +146,29 @@ __device__ __forceinline__ void issue_tile(const char* g, int64_t ldb, int r0, i
   }
 }
 
+// The same loads for a K-major operand with the block's base address in scalar registers:
+// `gbase` = row r0 of the block tile at byte kt * KB (wave-uniform), each lane adds a 32-bit offset
+// (global_load_lds with an SGPR base), rows clamped to rlast (the last valid row of the block).
+// lrow / lchunk: the lane's row within one instruction's rows and its swizzled 16-byte chunk.
+// With S32 the chunk map is kmaj_swz32 (32-row fragments), whose row-bit-4 term is the same for all
+// lanes of one instruction (RPI = 8 rows), so it is applied as a wave-uniform XOR.
+template <int ROWS, int KB, int NW, bool S32 = false>
+__device__ __forceinline__ void issue_tile_sbase(const char* gbase, int lrow, int lchunk, int rlast, int ldb,
+                                                 unsigned char* lds_op, int wave_s) {
+  constexpr int TILE = ROWS * KB;
+  constexpr int NI = TILE / 1024 / NW;
+  constexpr int RPI = 1024 / KB;                           // rows per load instruction
+  static_assert(NI >= 1 && NI * 1024 * NW == TILE, "tile must split evenly over the waves");
+  static_assert(!S32 || KB == 128, "32-row map: 128-byte rows");
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = min((wave_s * NI + i) * RPI + lrow, rlast);
+    const int lc = S32 ? lchunk ^ (((((wave_s * NI + i) * RPI) >> 4) & 1) << 1) : lchunk;
+    const char* src = gbase + (uint32_t)(row * ldb + (lc << 4));
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(lds_op + (wave_s * NI + i) * 1024), 16, 0, 0);
+  }
+}
+
 // Fragment of 16 rows (K-major) or 16 columns (MN-major) starting at f0: KB/4 bytes per lane;
 // lane (index l & 15, group g = l >> 4) holds chunks [g * KB/64, (g+1) * KB/64) of 16 bytes of
 // the K tile, in the same K order for both layouts. The tile starts at byte off of the stage array
@@ -332,6 +355,13 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   constexpr bool IL = MODE == 2;   // ... with the reads and half the loads interleaved into the MFMAs
   constexpr int NV0 = NIW / 2;     // loads issued together right after the barrier (IL, SP32)
   constexpr bool SP32 = MODE == 3; // split-phase K loop on the 32x32 MFMAs (x64 e4m3, x16 bf16), interleaved
+  constexpr bool PP = MODE == 4;   // ping-pong: two wave groups alternate MFMA-only and LDS/load phases
+  constexpr bool PP32 = MODE == 5; // the same on the 32x32x64 e4m3 MFMA
+  constexpr bool ACC32 = SP32 || PP32;   // accumulators in the 32 x 32 fragment layout
+  static_assert(!PP || (sizeof(ET) == 2 && NS == 2 && KB == 128 && AK && BK && NW == 8),
+                "ping-pong loop: bf16, 2 stages, 128-byte K tiles, K-major operands, 8 waves");
+  static_assert(!PP32 || (sizeof(ET) == 1 && NS == 2 && KB == 128 && AK && BK && NW == 8 && FM % 2 == 0 && FN % 2 == 0),
+                "e4m3 ping-pong loop: 2 stages, 128-byte K tiles, K-major operands, 8 waves");
   static_assert(!SP32 || (sizeof(ET) <= 2 && NS == 2 && KB == 128 && AK && BK && FM % 2 == 0 && FN % 2 == 0),
                 "32x32 split-phase loop: e4m3 or bf16, 2 stages, 128-byte K tiles, K-major operands");
   // One LDS array per stage: distinct objects let the compiler see that the direct loads into the
@@ -394,9 +424,9 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
     for (int j = 0; j < FM; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   // SP32: 32 x 32 fragments (lane l: m = l & 31 of fragment j, n = 8 q + 4 (l >> 5) + r of fragment
   // i in element 4 q + r)
-  constexpr int FM2 = SP32 ? FM / 2 : 1, FN2 = SP32 ? FN / 2 : 1;
+  constexpr int FM2 = ACC32 ? FM / 2 : 1, FN2 = ACC32 ? FN / 2 : 1;
   floatx16 acc32[FN2][FM2];
-  if constexpr (SP32) {
+  if constexpr (ACC32) {
 #pragma unroll
     for (int i = 0; i < FN2; ++i)
 #pragma unroll
@@ -521,6 +551,149 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
       half_step(I1{}, kt + 1);
     }
     if (kt < nk) half_step(I0{}, kt);
+  } else if constexpr (PP || PP32) {
+    // Ping-pong K loop. Waves w and w + 4 share SIMD w % 4; group 0 (waves 0-3) runs one phase
+    // ahead of group 1 (waves 4-7), and every phase ends at a block barrier:
+    //   phase 2t:     group 0 reads tile t's fragments (LDS -> registers); group 1 multiplies t - 1
+    //   phase 2t + 1: group 0 multiplies tile t;                          group 1 reads tile t
+    // so on each SIMD one wave issues only MFMAs while the other reads, and the MFMA pipe is fed
+    // by a single wave from registers. Group 1 takes one extra barrier before its loop and group 0
+    // one after it, so both pass the same number of barriers.
+    // Each wave loads its eighth of every tile (global -> LDS) in the phase two phases before the
+    // tile is first read: group 0 during its read phase of tile t - 1 (phase 2t - 2), group 1
+    // during its MFMA phase of tile t - 2 (the same phase), each into the stage of tile t - 2,
+    // which both groups finished reading by then; each wave waits for its own loads at the end of
+    // the following phase. Past the last tile the loads repeat it into a stage that is not read
+    // again.
+    // bf16: 16x16x32 MFMAs, fragments [FM or FN][2 chunks of 16 bytes]; e4m3 (PP32): 32x32x64
+    // MFMAs, fragments [FM2 or FN2][2 halves of K][2 chunks] (the split-phase e4m3 loop's layout).
+    const bool lead = wave < 4;
+    constexpr int RA = PP32 ? FM2 : FM, RB = PP32 ? FN2 : FN;
+    u32x4 fa[RA][2][2], fb[RB][2][2];
+    auto rd = [&](const unsigned char* sa) __attribute__((always_inline)) {
+      if constexpr (PP32) {
+#pragma unroll
+        for (int i = 0; i < FN2; ++i) {
+          read_frag32<0>(sa, BM * KB, wn * TN + i * 32, lane, fb[i][0]);
+          read_frag32<1>(sa, BM * KB, wn * TN + i * 32, lane, fb[i][1]);
+        }
+#pragma unroll
+        for (int j = 0; j < FM2; ++j) {
+          read_frag32<0>(sa, 0, wm * TM + j * 32, lane, fa[j][0]);
+          read_frag32<1>(sa, 0, wm * TM + j * 32, lane, fa[j][1]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          fb[i][0][0] = read_chunk<BK, BN, KB, 0>(sa, BM * KB, wn * TN + i * 16, lane);
+          fb[i][1][0] = read_chunk<BK, BN, KB, 1>(sa, BM * KB, wn * TN + i * 16, lane);
+        }
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          fa[j][0][0] = read_chunk<AK, BM, KB, 0>(sa, 0, wm * TM + j * 16, lane);
+          fa[j][1][0] = read_chunk<AK, BM, KB, 1>(sa, 0, wm * TM + j * 16, lane);
+        }
+      }
+    };
+    auto mm = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if constexpr (PP32) {
+#pragma unroll
+          for (int j = 0; j < FM2; ++j)
+#pragma unroll
+            for (int i = 0; i < FN2; ++i) {
+              const intx8 vb = __builtin_bit_cast(intx8, __builtin_shufflevector(fb[i][c][0], fb[i][c][1], 0, 1, 2, 3, 4, 5, 6, 7));
+              const intx8 va = __builtin_bit_cast(intx8, __builtin_shufflevector(fa[j][c][0], fa[j][c][1], 0, 1, 2, 3, 4, 5, 6, 7));
+              // format 0 = e4m3 for both operands; E8M0 block scales 127 = 2^0
+              acc32[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, va, acc32[i][j], 0, 0, 0, 0x7f7f7f7f, 0,
+                                                                             0x7f7f7f7f);
+            }
+        } else {
+#pragma unroll
+          for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fb[i][c][0]),
+                                                                  __builtin_bit_cast(bf16x8_t, fa[j][c][0]), acc[i][j], 0, 0, 0);
+        }
+      }
+    };
+    auto bar = []() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // loads with scalar base addresses (see issue_tile_sbase): the lane's row and chunk are its
+    // only per-lane state, which keeps the register budget (128 accumulators + 96 fragment
+    // registers) under 256
+    const int ldai = (int)ldab, ldbi = (int)ldbb;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform: LDS targets and row offsets in SGPRs
+    constexpr int CPR = KB / 16;
+    const int lrow = lane / CPR, lchunk = (lane % CPR) ^ kmaj_swz<KB>(lane / CPR);
+    const int alast = min(BM, M - m0) - 1, blast = min(BN, N - n0) - 1;
+    auto issue = [&](int kt, unsigned char* sa) __attribute__((always_inline)) {
+      // opaque copies: the per-instruction offsets are formed at each issue, not held in registers
+      int lr = lrow, lc = lchunk;
+      asm volatile("" : "+v"(lr), "+v"(lc));
+      const int64_t ko = (int64_t)kt * KB;
+      issue_tile_sbase<BM, KB, NW, PP32>(Ab + (int64_t)m0 * ldab + ko, lr, lc, alast, ldai, sa, wave_s);
+      issue_tile_sbase<BN, KB, NW, PP32>(Bb + (int64_t)n0 * ldbb + ko, lr, lc, blast, ldbi, sa + BM * KB, wave_s);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    // One loop per group, each without run-time conditions inside, so that the compiler knows
+    // which loads are in flight at every LDS read and inserts no wait of its own.
+    auto body_lead = [&](auto si, int t) __attribute__((always_inline)) {
+      constexpr int S = decltype(si)::value;
+      rd(stage(std::integral_constant<int, S>{}));
+      __builtin_amdgcn_sched_barrier(0);
+      issue(min(t + 1, nk - 1), stage(std::integral_constant<int, S ^ 1>{}));
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkm0();
+      bar();
+      mm();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<0>();                                      // this wave's part of tile t + 1
+      bar();
+    };
+    auto body_lag = [&](auto si, int t) __attribute__((always_inline)) {
+      constexpr int S = decltype(si)::value;
+      rd(stage(std::integral_constant<int, S>{}));
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt_lgkm0<0>();                                // this wave's part of tile t + 1
+      bar();
+      issue(min(t + 2, nk - 1), stage(std::integral_constant<int, S>{}));
+      __builtin_amdgcn_sched_barrier(0);
+      mm();
+      __builtin_amdgcn_sched_barrier(0);
+      bar();
+    };
+    if (nk > 0) {
+      issue(0, st0);
+      if (lead) {
+        wait_vmcnt<0>();
+        bar();                                              // tile 0 is in LDS
+        int t = 0;
+        for (; t + 2 <= nk; t += 2) {
+          body_lead(I0{}, t);
+          body_lead(I1{}, t + 1);
+        }
+        if (t < nk) body_lead(I0{}, t);
+        bar();                                              // group 1's last MFMA phase
+      } else {
+        issue(min(1, nk - 1), st1);                         // group 1's part of tile 1
+        wait_vmcnt<NIW>();
+        bar();                                              // tile 0 is in LDS
+        bar();                                              // one phase behind group 0
+        int t = 0;
+        for (; t + 2 <= nk; t += 2) {
+          body_lag(I0{}, t);
+          body_lag(I1{}, t + 1);
+        }
+        if (t < nk) body_lag(I0{}, t);
+      }
+    }
   } else if constexpr (SP32) {
     // The bf16 split-phase structure with e4m3 fragments: half C of a 128-byte K tile is one 32x32x64
     // MFMA step (64 bytes of K), so each half holds FM/2 + FN/2 fragments of 2 x 16 bytes per lane
@@ -678,7 +851,7 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   float red_amax = 0.f;
 #pragma unroll 1
   for (int s0 = 0; s0 < BM; s0 += PR) {
-    if constexpr (SP32) {
+    if constexpr (ACC32) {
 #pragma unroll
       for (int j = 0; j < FM2; ++j) {
         const int rloc = wm * TM + j * 32 + (lane & 31) - s0;
@@ -874,6 +1047,49 @@ template <class T> struct EpiRelu2Bwd {
   }
 };
 
+// SwiGLU MLP, up projection (the gate half g = round(hn W_gate^T) is already stored at gu[m, n]):
+// u = round(acc) is stored at gu[m, F + n] and a = round(silu(g) u) at a[m, n]
+template <class T> struct EpiSwigluUp {
+  static constexpr const char* kName = "swiglu_up";
+  static constexpr int kKind = kEpiPlain;
+  T* gu; int64_t ldgu; int F; T* a; int64_t lda;
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
+    T* row = gu + (int64_t)m * ldgu;
+    float g[8], av[8];
+    Vec8<T>::load(row + n, g);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[k] = Elem<T>::rnd(v[k]);
+      av[k] = g[k] / (1.f + expf(-g[k])) * v[k];
+    }
+    Vec8<T>::store(row + F + n, v);
+    Vec8<T>::store(a + (int64_t)m * lda + n, av);
+  }
+};
+
+// SwiGLU MLP backward: da = round(acc) (= dm W_proj); with g = gu[m, n], u = gu[m, F + n],
+// s = sigmoid(g): dgu[m, n] = round(da u s (1 + g (1 - s))) and dgu[m, F + n] = round(da g s)
+template <class T> struct EpiSwigluBwd {
+  static constexpr const char* kName = "swiglu_bwd";
+  static constexpr int kKind = kEpiPlain;
+  T* dgu; const T* gu; int64_t ld; int F;
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
+    const int64_t o = (int64_t)m * ld + n;
+    float g[8], u[8], dg[8], du[8];
+    Vec8<T>::load(gu + o, g);
+    Vec8<T>::load(gu + o + F, u);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float da = Elem<T>::rnd(v[k]);
+      const float sg = 1.f / (1.f + expf(-g[k]));
+      dg[k] = da * u[k] * sg * (1.f + g[k] * (1.f - sg));
+      du[k] = da * g[k] * sg;
+    }
+    Vec8<T>::store(dgu + o, dg);
+    Vec8<T>::store(dgu + o + F, du);
+  }
+};
+
 // qkv = round(acc); on the v columns (n >= vcol0) of value-embedding layers:
 // v = round(v + table[ids[m], n - vcol0]), nothing added for ids outside [0, rows)
 template <class T> struct EpiQkv {
@@ -1008,7 +1224,7 @@ inline hipError_t launch_gemm_cfg(int cfg_id, const ET* A, int64_t lda, const ET
   const dim3 nb((unsigned)nbt, slices);
   const ET* z = static_cast<const ET*>(o.zrow);
   constexpr int NT = 64 * WGM * WGN;
-  if constexpr (sizeof(ET) == 2 && MODE != 3) {   // MODE 3: K-major operands only (the callers check)
+  if constexpr (sizeof(ET) == 2 && MODE != 3 && MODE != 4) {   // MODE 3, 4: K-major operands only (the callers check)
     if (!o.a_kmajor && !o.b_kmajor) {
       const char* tag = gemm_tag<ET, Epi, false, false>();
       LL_LAUNCH_GEMM(tag, M, N, K, cfg_id, (int)slices, (gemm_kernel<ET, BM, BN, WGM, WGN, KB, NS, false, false, Epi, MODE>), nb, dim3(NT),
@@ -1044,6 +1260,9 @@ inline hipError_t launch_gemm_cfg(int cfg_id, const ET* A, int64_t lda, const ET
 //   9 = 256 x 256, 8 waves (4 x 2), 128 B, 2, split-phase K loop with the LDS reads and half the
 //       loads interleaved into the MFMAs (bf16; e4m3 falls back to 4)
 //  10 = 256 x 256, 4 waves (2 x 2, one per SIMD), 128 B, 2, split-phase K loop (bf16; e4m3: 4)
+//  14 = 256 x 256, 8 waves (4 x 2), 128 B, 2, ping-pong K loop (two wave groups alternating MFMA-only
+//       and read/load phases) on the 16x16x32 bf16 MFMA; e4m3 runs it as 15, an MN-major operand as 9
+//  15 = the ping-pong loop on the 32x32x64 e4m3 MFMA (bf16 runs it as 14)
 //  11 = 256 x 256, 8 waves (4 x 2), 128 B, 2, split-phase K loop on the 32x32 MFMAs (32x32x64 e4m3,
 //       32x32x16 bf16) with reads and half the loads interleaved (fp32 runs it as 4; bf16 with an
 //       MN-major operand as 9). bf16 measured ~7% slower than 9 on the loss's shapes, so only e4m3
@@ -1077,6 +1296,26 @@ inline hipError_t launch_gemm_with(int cfg, const ET* A, int64_t lda, const ET* 
     if (cfg == 12 || cfg == 13) cfg = 9;
   } else {
     if (cfg == 12 || cfg == 13) cfg = 4;
+  }
+  if constexpr (sizeof(ET) == 2) {
+    // 14 (and 15): 256 x 256, 8 waves (4 x 2), 128 B, 2, ping-pong K loop (K-major operands;
+    // otherwise 9)
+    if (cfg == 14 || cfg == 15) {
+      // lane offsets are 32-bit: 256 rows of either operand must span less than 2^31 bytes
+      const bool fits = lda < (int64_t(1) << 22) && ldb < (int64_t(1) << 22);
+      if (o.a_kmajor && o.b_kmajor && fits)
+        return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 4>(14, A, lda, B, ldb, M, N, K, epi, o, s);
+      cfg = 9;
+    }
+  } else if constexpr (sizeof(ET) == 1) {
+    // 15: 256 x 256, 8 waves (4 x 2), 128 B, 2, ping-pong K loop on the 32x32x64 e4m3 MFMA
+    if (cfg == 15 || cfg == 14) {
+      const bool fits = lda < (int64_t(1) << 22) && ldb < (int64_t(1) << 22);
+      if (fits) return launch_gemm_cfg<ET, 256, 256, 4, 2, 128, 2, 5>(15, A, lda, B, ldb, M, N, K, epi, o, s);
+      cfg = 11;
+    }
+  } else {
+    if (cfg == 14 || cfg == 15) cfg = 4;
   }
   switch (cfg) {
     case 1: return launch_gemm_cfg<ET, 128, 128, 2, 2, 128, 2>(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
@@ -1117,10 +1356,11 @@ inline hipError_t launch_gemm(const ET* A, int64_t lda, const ET* B, int64_t ldb
     const double e256 = (double)t256 / (double)(cdiv(t256, 256) * 256);
     const double e128 = 0.75 * (double)t128 / (double)(cdiv(t128, 256) * 256);
     // 4 x 2 waves, except 2 x 4 when B is MN-major (measured ~3% faster there); bf16 with both
-    // operands K-major takes the split-phase K loop (measured 2-5% faster than config 4), e4m3 the
-    // split-phase loop on the 32x32x64 MFMA (6-9% faster than config 4 on the MLP shapes)
+    // operands K-major takes the ping-pong K loop (measured 1-7% faster than the split-phase loop of
+    // configuration 9, which was 2-5% faster than configuration 4), e4m3 the split-phase loop on the
+    // 32x32x64 MFMA (6-9% faster than configuration 4 on the MLP shapes)
     const bool kk16 = sizeof(ET) == 2 && o.a_kmajor && o.b_kmajor;
-    cfg = e256 >= e128 ? (sizeof(ET) == 1 ? 11 : kk16 ? 9 : o.b_kmajor ? 4 : 3) : 1;
+    cfg = e256 >= e128 ? (sizeof(ET) == 1 ? 11 : kk16 ? 14 : o.b_kmajor ? 4 : 3) : 1;
   }
   return launch_gemm_with(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
 }
@@ -1149,7 +1389,7 @@ inline hipError_t launch_gemm_splitk(const ET* A, int64_t lda, const ET* B, int6
   const int sl = (int)std::max<int64_t>(1, cdiv(K, kchunk));
   EpiSplitK32 e{scratch, (int64_t)N, (int64_t)M * N, kchunk};
   int cfg = gemm_config_override();
-  if (cfg == 0) cfg = sizeof(ET) == 1 ? 11 : sizeof(ET) == 2 && o.a_kmajor && o.b_kmajor ? 9 : o.b_kmajor ? 4 : 3;
+  if (cfg == 0) cfg = sizeof(ET) == 1 ? 11 : sizeof(ET) == 2 && o.a_kmajor && o.b_kmajor ? 14 : o.b_kmajor ? 4 : 3;
   hipError_t r = launch_gemm_with(cfg, A, lda, B, ldb, M, N, K, e, o, s);
   if (r != hipSuccess) return r;
   const int64_t work = (int64_t)M * (N / 8);

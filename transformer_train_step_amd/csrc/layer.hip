@@ -17,8 +17,8 @@ namespace {
 
 struct Dims {
   int64_t B, T, N, Np, Tp, ve_rows;
-  int D, Hq, Hkv, DH, F, QD, KVD, QKVD, vcol0;
-  bool fp8, bf, ve;
+  int D, Hq, Hkv, DH, F, FW, QD, KVD, QKVD, vcol0;   // FW: rows of w_fc (F, or 2F for SwiGLU)
+  bool fp8, bf, ve, swiglu;
   int es;
   float eps, theta;
 };
@@ -39,11 +39,16 @@ int make_dims(const ll_layer_cfg* c, Dims& d) {
   LL_CHECK(c->rms_eps >= 0.f && c->rope_theta > 0.f, LL_ERR_INVALID_ARG, "rms_eps >= 0, rope_theta > 0");
   LL_CHECK(!c->has_value_embed || c->ve_rows > 0, LL_ERR_INVALID_ARG, "ve_rows must be > 0 on value-embedding layers");
   LL_CHECK(c->batch * c->seq < ((int64_t)1 << 31) / 64, LL_ERR_UNSUPPORTED, "too many tokens");
+  LL_CHECK(c->mlp_kind == LL_MLP_RELU2 || c->mlp_kind == LL_MLP_SWIGLU, LL_ERR_INVALID_ARG,
+           "mlp_kind must be LL_MLP_RELU2 or LL_MLP_SWIGLU");
+  LL_CHECK(!(c->mlp_kind == LL_MLP_SWIGLU && c->fp8_mlp), LL_ERR_UNSUPPORTED,
+           "the SwiGLU MLP runs on bf16 / fp32 GEMMs (fp8_mlp must be 0)");
   d.B = c->batch; d.T = c->seq; d.N = d.B * d.T;
   d.Np = round_up(d.N, 128); d.Tp = round_up(d.T, 64);
   d.D = c->d_model; d.Hq = c->n_q_heads; d.Hkv = c->n_kv_heads; d.DH = c->head_dim; d.F = c->d_ff;
   d.QD = d.Hq * d.DH; d.KVD = d.Hkv * d.DH; d.QKVD = d.QD + 2 * d.KVD; d.vcol0 = d.QD + d.KVD;
   d.fp8 = c->fp8_mlp != 0; d.bf = c->dtype == LL_BF16; d.ve = c->has_value_embed != 0;
+  d.swiglu = c->mlp_kind == LL_MLP_SWIGLU; d.FW = d.swiglu ? 2 * d.F : d.F;
   d.es = d.bf ? 2 : 4; d.eps = c->rms_eps; d.theta = c->rope_theta;
   d.ve_rows = d.ve ? c->ve_rows : 0;
   return LL_OK;
@@ -74,7 +79,7 @@ size_t carve_saved(void* base, const Dims& d, Saved& s) {
   s.lse = c.take<float>(d.B * d.Hq * d.Tp);     // [B, Hq, Tp] (bf16) / [B, Hq, T] (fp32)
   s.attn_out = c.take<char>(d.N * d.D * e);
   s.h = c.take<char>(d.N * d.D * e);
-  s.u = c.take<char>(d.N * d.F * e);
+  s.u = c.take<char>(d.N * d.FW * e);      // u, or [g | u] for SwiGLU
   s.m = c.take<char>(d.N * d.D * e);
   s.hn = s.r = nullptr;
   s.hn8 = s.hn8t = s.r8t = s.w18 = s.w18t = s.w28 = s.w28t = nullptr;
@@ -88,7 +93,7 @@ size_t carve_saved(void* base, const Dims& d, Saved& s) {
     s.w28t = c.take<uint8_t>((int64_t)d.F * d.D);
   } else {
     s.hn = c.take<char>(d.N * d.D * e);
-    s.r = c.take<char>(d.N * d.F * e);
+    s.r = c.take<char>(d.N * d.F * e);    // r = relu(u)^2, or a = silu(g) u for SwiGLU
   }
   return c.bytes();
 }
@@ -153,7 +158,7 @@ size_t carve_bwd(void* base, const Dims& d, BwdWs& w) {
   w.qs = c.take<QScale>(2);
   w.zrow = c.take<char>(256);
   w.dm = c.take<char>(d.N * d.D * e);
-  w.du = c.take<char>(d.N * d.F * e);
+  w.du = c.take<char>(d.N * d.FW * e);     // du, or [dg | du] for SwiGLU
   w.dhn = c.take<char>(d.N * d.D * e);
   w.dh = c.take<char>(d.N * d.D * e);
   w.dattn = c.take<char>(d.N * d.D * e);
@@ -173,13 +178,13 @@ size_t carve_bwd(void* base, const Dims& d, BwdWs& w) {
   w.t0 = w.t1 = nullptr;
   w.dm8 = w.dm8t = w.du8 = w.du8t = nullptr;
   if (!d.bf) {
-    const int64_t big = std::max<int64_t>({(int64_t)d.QKVD, (int64_t)d.F, (int64_t)d.D, (int64_t)d.QD});
+    const int64_t big = std::max<int64_t>({(int64_t)d.QKVD, (int64_t)d.FW, (int64_t)d.D, (int64_t)d.QD});
     const int64_t t = std::max<int64_t>(big * d.Np, big * big);
     w.t0 = c.take<char>(t * e);
     w.t1 = c.take<char>(t * e);
   } else {
     // transposed weight of an input-gradient GEMM
-    w.t0 = c.take<char>(std::max<int64_t>({(int64_t)d.QKVD * d.D, (int64_t)d.F * d.D, (int64_t)d.QD * d.D}) * e);
+    w.t0 = c.take<char>(std::max<int64_t>({(int64_t)d.QKVD * d.D, (int64_t)d.FW * d.D, (int64_t)d.QD * d.D}) * e);
   }
   if (d.fp8) {
     w.dm8 = c.take<uint8_t>(d.N * d.D);
@@ -262,18 +267,24 @@ int layer_fwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
     LL_HIP(launch_gemm_nt(CP<T>(sv.xn), d.D, CP<T>(p->w_qkv), d.D, (int)N, d.QKVD, d.D, e, s));
   }
   if (N > 0) {
-    const int64_t threads = N * (d.Hq + d.Hkv) * (DH / 16);   // 8 rotation pairs per lane
+    // QK-norm + RoPE: the bf16 attention forward applies them to q as it loads it (and saves q^
+    // and 1/rms(q) for the backward); k^, shared by every query block of its group, is formed
+    // once here. The fp32 kernels take both from this pass.
+    constexpr bool kFusedQ = std::is_same<T, bf16>::value;
+    const int h0 = kFusedQ ? d.Hq : 0, hp = kFusedQ ? d.Hkv : d.Hq + d.Hkv;
+    const int64_t threads = N * hp * (DH / 16);   // 8 rotation pairs per lane
     LL_LAUNCH("qk_prep", (qk_prep_kernel<T, DH>), dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, s, CP<T>(sv.qkv),
-                       (int64_t)d.QKVD, w.cs, P<T>(sv.qh), P<T>(sv.kh), sv.rq, sv.rk, N, (int)d.T, d.Hq, d.Hkv, d.eps);
+                       (int64_t)d.QKVD, w.cs, P<T>(sv.qh), P<T>(sv.kh), sv.rq, sv.rk, N, (int)d.T, d.Hq, d.Hkv, d.eps,
+                       h0, hp);
     LL_HIP(hipGetLastError());
     const int nqb = (int)cdiv(d.T, 128);
     // algorithmic work, traced as 2 M N K: causal (query, key) pairs x head_dim x 2 products
     const int64_t pairs = d.B * d.Hq * d.T * (d.T + 1) / 2;
     if constexpr (std::is_same<T, bf16>::value) {
       LL_LAUNCH_MNK("attn_fwd", pairs, DH, 2, (fa_fwd_kernel<true>), dim3((unsigned)(d.B * d.Hq * nqb)), dim3(256), 0, s,
-                    CP<T>(sv.qh),
-                CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, P<T>(sv.o), sv.lse, d.Tp, (int)d.B,
-                (int)d.T, d.Hq, d.Hkv);
+                    CP<T>(sv.qkv), (int64_t)d.QKVD, w.cs, d.eps, P<T>(sv.qh), sv.rq, CP<T>(sv.kh),
+                    CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, P<T>(sv.o), sv.lse, d.Tp, (int)d.B, (int)d.T, d.Hq,
+                    d.Hkv);
     } else {
       LL_HIP(launch_transpose(CP<T>(sv.qkv) + d.vcol0, d.T, DH, (int64_t)d.QKVD, P<T>(w.vt), d.Tp, d.Tp,
                               (int)(d.B * d.Hkv), d.Hkv, d.T * d.QKVD, (int64_t)DH, (int64_t)DH * d.Tp, s));
@@ -316,7 +327,14 @@ int layer_fwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
     }
   }
   LL_HIP(launch_rmsnorm_fwd(CP<T>(sv.h), g2, P<T>(sv.hn), sv.r2, N, d.D, d.eps, (float*)nullptr, s));
-  {
+  if (d.swiglu) {
+    // g = hn W_gate^T into the first F columns of [g | u], then the up GEMM whose epilogue stores
+    // u beside it and a = silu(g) u
+    EpiStore<T> eg{P<T>(sv.u), (int64_t)d.FW, Deq{nullptr, nullptr}};
+    LL_HIP(launch_gemm_nt(CP<T>(sv.hn), d.D, CP<T>(p->w_fc), d.D, (int)N, d.F, d.D, eg, s));
+    EpiSwigluUp<T> eu{P<T>(sv.u), (int64_t)d.FW, d.F, P<T>(sv.r), (int64_t)d.F};
+    LL_HIP(launch_gemm_nt(CP<T>(sv.hn), d.D, CP<T>(p->w_fc) + (int64_t)d.F * d.D, d.D, (int)N, d.F, d.D, eu, s));
+  } else {
     EpiRelu2<T> e{P<T>(sv.u), P<T>(sv.r), (int64_t)d.F, Deq{nullptr, nullptr}, &sv.qs[QS_R].amax};
     LL_HIP(launch_gemm_nt(CP<T>(sv.hn), d.D, CP<T>(p->w_fc), d.D, (int)N, d.F, d.D, e, s));
   }
@@ -388,7 +406,10 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
     }
   }
   if (!done) {
-    {   // dr = dm W2; du = dr * 2 relu(u)
+    if (d.swiglu) {   // da = dm W2; [dg | du] from da, g and u in the epilogue
+      EpiSwigluBwd<T> e{P<T>(w.du), CP<T>(sv.u), (int64_t)d.FW, d.F};
+      LL_HIP(mm_nn(CP<T>(w.dm), d.D, CP<T>(p->w_proj), d.F, (int)N, d.F, d.D, e, P<T>(w.t0), w.zrow, s));
+    } else {   // dr = dm W2; du = dr * 2 relu(u)
       EpiRelu2Bwd<T> e{P<T>(w.du), CP<T>(sv.u), (int64_t)d.F, Deq{nullptr, nullptr}, &w.qs[1].amax};
       LL_HIP(mm_nn(CP<T>(w.dm), d.D, CP<T>(p->w_proj), d.F, (int)N, d.F, d.D, e, P<T>(w.t0), w.zrow, s));
     }
@@ -396,13 +417,13 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
       EpiStore<T> e{P<T>(g->w_proj), (int64_t)d.F, Deq{nullptr, nullptr}, acc};
       LL_HIP(mm_tn(CP<T>(w.dm), d.D, CP<T>(sv.r), d.F, d.D, d.F, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s));
     }
-    {   // dW1 = du^T hn
+    {   // dW1 = du^T hn  ([dg | du]^T hn for SwiGLU)
       EpiStore<T> e{P<T>(g->w_fc), (int64_t)d.D, Deq{nullptr, nullptr}, acc};
-      LL_HIP(mm_tn(CP<T>(w.du), d.F, CP<T>(sv.hn), d.D, d.F, d.D, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s));
+      LL_HIP(mm_tn(CP<T>(w.du), d.FW, CP<T>(sv.hn), d.D, d.FW, d.D, N, Np, e, P<T>(w.t0), P<T>(w.t1), w.zrow, s));
     }
     {   // dhn = du W1
       EpiStore<T> e{P<T>(w.dhn), (int64_t)d.D, Deq{nullptr, nullptr}};
-      LL_HIP(mm_nn(CP<T>(w.du), d.F, CP<T>(p->w_fc), d.D, (int)N, d.D, d.F, e, P<T>(w.t0), w.zrow, s));
+      LL_HIP(mm_nn(CP<T>(w.du), d.FW, CP<T>(p->w_fc), d.D, (int)N, d.D, d.FW, e, P<T>(w.t0), w.zrow, s));
     }
   }
   // MLP RMSNorm backward + residual, fused with the attention-branch scaling

@@ -13,6 +13,9 @@ namespace {
 // tiles, the default) or 128 (128 x 128 block tiles)
 constexpr int kDefaultVocabTile = 256;
 constexpr int64_t kDefaultChunk = 10240;
+// block configuration of the logits GEMM with 256-wide vocabulary tiles (configuration 14: 16x16x32
+// MFMAs, ping-pong K loop)
+constexpr int kLogitsConfig = 14;
 
 struct LcePlan {
   int64_t chunk, chunk_pad, vpad;
@@ -82,10 +85,11 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     constexpr float kLog2e = 1.4426950408889634f;
     EpiLceLogits<T> epi{z, p.vpad, p.part, p.nparts, 2.f * kLog2e / softcap, softcap * kLog2e};
     {
-      // one row-sum partial per block tile of vocab_tile columns: 256 -> configuration 9 (or an
+      // one row-sum partial per block tile of vocab_tile columns: 256 -> configuration 14 (or an
       // override with 256-wide tiles), 128 -> configuration 1 (or 7)
       const int oc = gemm_config_override();
-      const int cfg = p.vtile == 128 ? (oc == 7 ? 7 : 1) : ((oc >= 2 && oc <= 6) || oc == 9 || oc == 10 ? oc : 9);
+      const int cfg = p.vtile == 128 ? (oc == 7 ? 7 : 1)
+                                     : ((oc >= 2 && oc <= 6) || (oc >= 8 && oc <= 14) ? oc : kLogitsConfig);
       const hipError_t e = launch_gemm_with(cfg, Hc, (int64_t)d, W, (int64_t)d, rows, (int)v, d, epi, GemmOps{}, s);
       LL_HIP(e);
     }

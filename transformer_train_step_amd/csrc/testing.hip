@@ -105,7 +105,32 @@ extern "C" int llt_gemm_splitk(int32_t op_dtype, int32_t a_kmajor, int32_t b_kma
 }
 
 extern "C" int llt_set_gemm_config(int32_t cfg) {
-  LL_CHECK(cfg >= 0 && cfg <= 13, LL_ERR_INVALID_ARG, "cfg must be in [0, 13]");
+  LL_CHECK(cfg >= 0 && cfg <= 15, LL_ERR_INVALID_ARG, "cfg must be in [0, 15]");
   set_gemm_config_override(cfg);
+  return LL_OK;
+}
+
+// The cast step of the quantiser alone, on four values per thread with the kernels' own quant4:
+// q[i] = e4m3fn_rne(clamp(fl32(x[i] * scale), -448, 448)), the NaN code 0x7F for a NaN product.
+__global__ void __launch_bounds__(256) e4m3_cast_kernel(const float* __restrict__ x, int64_t n4, float scale,
+                                                        uint32_t* __restrict__ q) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    const floatx4 v = reinterpret_cast<const floatx4*>(x)[i];
+    const float a[4] = {v[0], v[1], v[2], v[3]};
+    q[i] = quant4(a, scale);
+  }
+}
+
+extern "C" int llt_e4m3_cast(const float* x, int64_t n, float scale, uint8_t* q, void* stream) {
+  LL_CHECK(n >= 0 && n % 4 == 0, LL_ERR_INVALID_ARG, "n must be a non-negative multiple of 4");
+  if (n == 0) return LL_OK;
+  LL_CHECK(x && q, LL_ERR_INVALID_ARG, "null pointer");
+  LL_CHECK(aligned16(x) && reinterpret_cast<uintptr_t>(q) % 4 == 0, LL_ERR_INVALID_ARG,
+           "x must be 16-byte and q 4-byte aligned");
+  const int64_t n4 = n / 4;
+  const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(n4, 256), 16384);
+  LL_LAUNCH("e4m3_cast", e4m3_cast_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), x, n4, scale,
+            reinterpret_cast<uint32_t*>(q));
+  LL_HIP(hipGetLastError());
   return LL_OK;
 }

@@ -25,13 +25,15 @@ class LayerConfig:
     ve_rows: int = 50304
     rms_eps: float = 1e-6
     rope_theta: float = 10000.0
+    mlp: str = "relu2"           # 'relu2' or 'swiglu' (w_fc [2 d_ff, D]: gate rows, then up rows)
 
     def c_struct(self) -> L.LayerCfg:
         return L.LayerCfg(dtype=L.LL_BF16 if self.dtype == "bf16" else L.LL_F32, fp8_mlp=int(self.fp8_mlp),
                           batch=self.batch, seq=self.seq, d_model=self.d_model, n_q_heads=self.n_q_heads,
                           n_kv_heads=self.n_kv_heads, head_dim=self.head_dim, d_ff=self.d_ff,
                           rms_eps=self.rms_eps, rope_theta=self.rope_theta,
-                          has_value_embed=int(self.value_embed), ve_rows=self.ve_rows if self.value_embed else 0)
+                          has_value_embed=int(self.value_embed), ve_rows=self.ve_rows if self.value_embed else 0,
+                          mlp_kind=L.LL_MLP_SWIGLU if self.mlp == "swiglu" else L.LL_MLP_RELU2)
 
     @property
     def torch_dtype(self):
@@ -52,7 +54,8 @@ PARAM_NAMES = ("attn_norm_w", "w_qkv", "w_o", "mlp_norm_w", "w_fc", "w_proj", "v
 def param_shapes(c: LayerConfig) -> dict:
     D, F = c.d_model, c.d_ff
     s = {"attn_norm_w": (D,), "w_qkv": (c.qkv_dim, D), "w_o": (D, c.n_q_heads * c.head_dim),
-         "mlp_norm_w": (D,), "w_fc": (F, D), "w_proj": (D, F), "resid_attn": (1,), "resid_mlp": (1,)}
+         "mlp_norm_w": (D,), "w_fc": ((2 if c.mlp == "swiglu" else 1) * F, D), "w_proj": (D, F),
+         "resid_attn": (1,), "resid_mlp": (1,)}
     if c.value_embed:
         s["ve_table"] = (c.ve_rows, c.n_kv_heads * c.head_dim)
     return s
