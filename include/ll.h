@@ -14,7 +14,11 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers to caller-owned memory, 16-byte aligned, row-major,
  *     densely packed unless a leading dimension is given. The library never allocates device
- *     memory and keeps no state between calls other than the text of the last error.
+ *     memory (ll_fp8_quant_tensorwise_noalloc's scratch is a static device array, below). State
+ *     kept between calls: the text of the last error; and, set only through the test entry points
+ *     of ll_testing.h, a process-wide GEMM block-configuration override (llt_set_gemm_config,
+ *     0 = automatic, the default) and an optional launch trace (llt_trace_begin/end), which the
+ *     calls here read.
  *   - `stream` is a hipStream_t (NULL = the default stream). All work is enqueued on it with no
  *     host synchronisation; outputs are valid once the stream has reached the enqueued work.
  *   - Every call validates its arguments before enqueuing anything and returns an ll_status.

@@ -306,6 +306,13 @@ __device__ __forceinline__ void sched_interleave() {
   }
 }
 
+// Epilogues that read global memory at the output's position may declare `struct Pf` with
+// `Pf load(int m, int n) const` and take it as a fourth argument of seg: the GEMM then issues every
+// such load of a pass before staging the pass's accumulators through LDS, so that their latency is
+// paid once per pass instead of once per row segment.
+template <class E, class = void> struct HasPf : std::false_type { using type = char; };
+template <class E> struct HasPf<E, std::void_t<typename E::Pf>> : std::true_type { using type = typename E::Pf; };
+
 // Split-K epilogues (static constexpr bool kSplitK = true, int kchunk): block row blockIdx.y of the
 // grid takes K elements [blockIdx.y kchunk, min(K, (blockIdx.y + 1) kchunk)) and the epilogue
 // stores its partial sums apart from the other slices'.
@@ -849,8 +856,21 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   };
   auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
   float red_amax = 0.f;
+  constexpr bool PF = HasPf<Epi>::value;
+  constexpr int ITERS = (PR + NW * RPI - 1) / (NW * RPI);   // row groups per wave and pass
+  using PfT = typename HasPf<Epi>::type;
 #pragma unroll 1
   for (int s0 = 0; s0 < BM; s0 += PR) {
+    PfT pf[PF ? ITERS : 1];
+    if constexpr (PF) {
+      // this pass's global reads, issued before the accumulators go through LDS
+#pragma unroll
+      for (int it = 0; it < ITERS; ++it) {
+        const int p = wave * RPI + it * NW * RPI;
+        const int m = m0 + s0 + p + lane / SPR, n = n0 + 8 * (lane % SPR);
+        if (p < PR && s0 + p < BM && m < M && n < N) pf[it] = epi.load(m, n);
+      }
+    }
     if constexpr (ACC32) {
 #pragma unroll
       for (int j = 0; j < FM2; ++j) {
@@ -884,8 +904,7 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
       }
     }
     __syncthreads();
-#pragma unroll 1
-    for (int p = wave * RPI; p < PR && s0 + p < BM; p += NW * RPI) {
+    auto emit = [&](int p, const PfT& f) __attribute__((always_inline)) {
       const int rloc = p + lane / SPR, sg = lane % SPR;
       const int m = m0 + s0 + rloc, n = n0 + 8 * sg;
       const float* row = slab_row(rloc);
@@ -896,9 +915,17 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
       float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       const bool ok = (m < M) && (n < N);
       if constexpr (Epi::kKind == kEpiPlain) {
-        if (ok) epi.seg(m, n, v);
+        if constexpr (PF) {
+          if (ok) epi.seg(m, n, v, f);
+        } else {
+          if (ok) epi.seg(m, n, v);
+        }
       } else if constexpr (Epi::kKind == kEpiAmax) {
-        if (ok) red_amax = fmaxf(red_amax, epi.seg(m, n, v));
+        if constexpr (PF) {
+          if (ok) red_amax = fmaxf(red_amax, epi.seg(m, n, v, f));
+        } else {
+          if (ok) red_amax = fmaxf(red_amax, epi.seg(m, n, v));
+        }
       } else {
         float se = 0.f;
         if (ok) se = epi.seg(m, n, v);
@@ -906,6 +933,16 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
         se = group_sum<SPR>(se);
         if (sg == 0 && m < M) epi.row(m, bn, se);
       }
+    };
+    if constexpr (PF) {
+#pragma unroll
+      for (int it = 0; it < ITERS; ++it) {
+        const int p = wave * RPI + it * NW * RPI;
+        if (p < PR && s0 + p < BM) emit(p, pf[it]);
+      }
+    } else {
+#pragma unroll 1
+      for (int p = wave * RPI; p < PR && s0 + p < BM; p += NW * RPI) emit(p, pf[0]);
     }
     __syncthreads();
   }
@@ -925,6 +962,28 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
 }
 
 // ------------------------------------------------------------------ epilogue functors
+// The raw bytes of one 8-column segment (8 bf16 = 16 B or 8 fp32 = 32 B), loaded ahead of use.
+template <class T> struct Raw8;
+template <> struct Raw8<bf16> {
+  uint4 r{0u, 0u, 0u, 0u};
+  __device__ __forceinline__ void load(const bf16* p) { r = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void to(float (&v)[8]) const {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = __uint_as_float(w[i] << 16); v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u); }
+  }
+};
+template <> struct Raw8<float> {
+  float4 a{0.f, 0.f, 0.f, 0.f}, b{0.f, 0.f, 0.f, 0.f};
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void to(float (&v)[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
 // Dequantisation factor of an FP8 GEMM (product of the operands' inverse scales), 1 otherwise.
 struct Deq {
   const float* ia;
@@ -958,10 +1017,16 @@ template <class T> struct EpiLin {
   static constexpr const char* kName = "lin";
   static constexpr int kKind = kEpiPlain;
   T* out; const T* other; int64_t ld; float alpha; float beta;
-  __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
+  using Pf = Raw8<T>;
+  __device__ __forceinline__ Pf load(int m, int n) const {
+    Pf f;
+    f.load(other + (int64_t)m * ld + n);
+    return f;
+  }
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8], const Pf& f) const {
     const int64_t o = (int64_t)m * ld + n;
     float x[8];
-    Vec8<T>::load(other + o, x);
+    f.to(x);
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = alpha * x[k] + beta * v[k];
     Vec8<T>::store(out + o, v);
@@ -973,10 +1038,16 @@ template <class T> struct EpiResidual {
   static constexpr const char* kName = "residual";
   static constexpr int kKind = kEpiPlain;
   T* out; const T* x; T* branch; int64_t ld; const float* a; Deq dq;
-  __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
+  using Pf = Raw8<T>;
+  __device__ __forceinline__ Pf load(int m, int n) const {
+    Pf f;
+    f.load(x + (int64_t)m * ld + n);
+    return f;
+  }
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8], const Pf& f) const {
     const int64_t o = (int64_t)m * ld + n;
     float xv[8];
-    Vec8<T>::load(x + o, xv);
+    f.to(xv);
     const float s = *a;
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = Elem<T>::rnd(dq.apply(v[k]));
@@ -1032,10 +1103,16 @@ template <class T> struct EpiRelu2Bwd {
   static constexpr const char* kName = "relu2_bwd";
   static constexpr int kKind = kEpiAmax;
   T* du; const T* u; int64_t ld; Deq dq; float* amax;
-  __device__ __forceinline__ float seg(int m, int n, float (&v)[8]) const {
+  using Pf = Raw8<T>;
+  __device__ __forceinline__ Pf load(int m, int n) const {
+    Pf f;
+    f.load(u + (int64_t)m * ld + n);
+    return f;
+  }
+  __device__ __forceinline__ float seg(int m, int n, float (&v)[8], const Pf& f) const {
     const int64_t o = (int64_t)m * ld + n;
     float uv[8], mx = 0.f;
-    Vec8<T>::load(u + o, uv);
+    f.to(uv);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float dr = Elem<T>::rnd(dq.apply(v[k]));
@@ -1053,10 +1130,16 @@ template <class T> struct EpiSwigluUp {
   static constexpr const char* kName = "swiglu_up";
   static constexpr int kKind = kEpiPlain;
   T* gu; int64_t ldgu; int F; T* a; int64_t lda;
-  __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
+  using Pf = Raw8<T>;
+  __device__ __forceinline__ Pf load(int m, int n) const {
+    Pf f;
+    f.load(gu + (int64_t)m * ldgu + n);
+    return f;
+  }
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8], const Pf& f) const {
     T* row = gu + (int64_t)m * ldgu;
     float g[8], av[8];
-    Vec8<T>::load(row + n, g);
+    f.to(g);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       v[k] = Elem<T>::rnd(v[k]);
@@ -1073,11 +1156,18 @@ template <class T> struct EpiSwigluBwd {
   static constexpr const char* kName = "swiglu_bwd";
   static constexpr int kKind = kEpiPlain;
   T* dgu; const T* gu; int64_t ld; int F;
-  __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
+  struct Pf { Raw8<T> g, u; };
+  __device__ __forceinline__ Pf load(int m, int n) const {
+    Pf f;
+    f.g.load(gu + (int64_t)m * ld + n);
+    f.u.load(gu + (int64_t)m * ld + n + F);
+    return f;
+  }
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8], const Pf& f) const {
     const int64_t o = (int64_t)m * ld + n;
     float g[8], u[8], dg[8], du[8];
-    Vec8<T>::load(gu + o, g);
-    Vec8<T>::load(gu + o + F, u);
+    f.g.to(g);
+    f.u.to(u);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float da = Elem<T>::rnd(v[k]);
@@ -1117,11 +1207,17 @@ struct EpiAcc32 {
   static constexpr const char* kName = "acc32";
   static constexpr int kKind = kEpiPlain;
   float* C; int64_t ldc; int accumulate;
-  __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
+  using Pf = Raw8<float>;                                   // C32 before the call (accumulate only)
+  __device__ __forceinline__ Pf load(int m, int n) const {
+    Pf f;
+    if (accumulate) f.load(C + (int64_t)m * ldc + n);
+    return f;
+  }
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8], const Pf& f) const {
     float* p = C + (int64_t)m * ldc + n;
     if (accumulate) {
       float o[8];
-      Vec8<float>::load(p, o);
+      f.to(o);
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] += o[k];
     }
@@ -1135,10 +1231,16 @@ template <class OutT> struct EpiAcc32Out {
   static constexpr const char* kName = "acc32";
   static constexpr int kKind = kEpiPlain;
   const float* C; OutT* out; int64_t ldc; int accumulate = 0;
-  __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
+  using Pf = Raw8<float>;                                   // C32
+  __device__ __forceinline__ Pf load(int m, int n) const {
+    Pf f;
+    f.load(C + (int64_t)m * ldc + n);
+    return f;
+  }
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8], const Pf& f) const {
     const int64_t o = (int64_t)m * ldc + n;
     float c[8];
-    Vec8<float>::load(C + o, c);
+    f.to(c);
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] += c[k];
     if (accumulate) {
