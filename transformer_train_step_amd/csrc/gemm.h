@@ -310,6 +310,11 @@ __device__ __forceinline__ void sched_interleave() {
 // `Pf load(int m, int n) const` and take it as a fourth argument of seg: the GEMM then issues every
 // such load of a pass before staging the pass's accumulators through LDS, so that their latency is
 // paid once per pass instead of once per row segment.
+// Epilogues with a `prepare()` (reading per-launch scalars such as dequantisation factors into
+// registers) get it called once per block before their first segment.
+template <class E, class = void> struct HasPrepare : std::false_type {};
+template <class E> struct HasPrepare<E, std::void_t<decltype(std::declval<E&>().prepare())>> : std::true_type {};
+
 template <class E, class = void> struct HasPf : std::false_type { using type = char; };
 template <class E> struct HasPf<E, std::void_t<typename E::Pf>> : std::true_type { using type = typename E::Pf; };
 
@@ -835,6 +840,8 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   }
   wait_vmcnt<0>();                                          // drain the repeated tail loads
   __syncthreads();
+  Epi ep = epi;                                             // per-launch scalars read once
+  if constexpr (HasPrepare<Epi>::value) ep.prepare();
 
   const int g = lane >> 4, r16 = lane & 15;
   // ---------------- epilogue: accumulators -> LDS slab -> functor on 8-column segments of rows.
@@ -868,7 +875,7 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
       for (int it = 0; it < ITERS; ++it) {
         const int p = wave * RPI + it * NW * RPI;
         const int m = m0 + s0 + p + lane / SPR, n = n0 + 8 * (lane % SPR);
-        if (p < PR && s0 + p < BM && m < M && n < N) pf[it] = epi.load(m, n);
+        if (p < PR && s0 + p < BM && m < M && n < N) pf[it] = ep.load(m, n);
       }
     }
     if constexpr (ACC32) {
@@ -916,22 +923,22 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
       const bool ok = (m < M) && (n < N);
       if constexpr (Epi::kKind == kEpiPlain) {
         if constexpr (PF) {
-          if (ok) epi.seg(m, n, v, f);
+          if (ok) ep.seg(m, n, v, f);
         } else {
-          if (ok) epi.seg(m, n, v);
+          if (ok) ep.seg(m, n, v);
         }
       } else if constexpr (Epi::kKind == kEpiAmax) {
         if constexpr (PF) {
-          if (ok) red_amax = fmaxf(red_amax, epi.seg(m, n, v, f));
+          if (ok) red_amax = fmaxf(red_amax, ep.seg(m, n, v, f));
         } else {
-          if (ok) red_amax = fmaxf(red_amax, epi.seg(m, n, v));
+          if (ok) red_amax = fmaxf(red_amax, ep.seg(m, n, v));
         }
       } else {
         float se = 0.f;
-        if (ok) se = epi.seg(m, n, v);
+        if (ok) se = ep.seg(m, n, v);
         // add the SPR segment sums of this row (consecutive lanes)
         se = group_sum<SPR>(se);
-        if (sg == 0 && m < M) epi.row(m, bn, se);
+        if (sg == 0 && m < M) ep.row(m, bn, se);
       }
     };
     if constexpr (PF) {
@@ -956,7 +963,7 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
       float m = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) m = fmaxf(m, red_w[w]);
-      atomic_max_nonneg(epi.amax, m);
+      atomic_max_nonneg(ep.amax, m);
     }
   }
 }
@@ -985,10 +992,20 @@ template <> struct Raw8<float> {
 };
 
 // Dequantisation factor of an FP8 GEMM (product of the operands' inverse scales), 1 otherwise.
+// The factors are read once per block (load(), from the epilogue's prepare()) and kept in
+// registers: read through the pointers at each use, they were fetched again for every element,
+// each fetch waited for, since the epilogue's stores might alias them.
 struct Deq {
   const float* ia;
   const float* ib;
-  __device__ __forceinline__ float apply(float acc) const { return ia ? (acc * *ia) * *ib : acc; }
+  float a = 1.f, b = 1.f;
+  __device__ __forceinline__ void load() {
+    if (ia) {
+      a = *ia;
+      b = *ib;
+    }
+  }
+  __device__ __forceinline__ float apply(float acc) const { return ia ? (acc * a) * b : acc; }
 };
 
 // C = round(deq(acc)), or with accumulate C = round(C + deq(acc)) (gradient accumulation over
@@ -997,6 +1014,7 @@ template <class OutT> struct EpiStore {
   static constexpr const char* kName = "store";
   static constexpr int kKind = kEpiPlain;
   OutT* C; int64_t ldc; Deq dq; int accumulate = 0;
+  __device__ __forceinline__ void prepare() { dq.load(); }
   __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
     OutT* p = C + (int64_t)m * ldc + n;
 #pragma unroll
@@ -1038,6 +1056,11 @@ template <class T> struct EpiResidual {
   static constexpr const char* kName = "residual";
   static constexpr int kKind = kEpiPlain;
   T* out; const T* x; T* branch; int64_t ld; const float* a; Deq dq;
+  float as = 1.f;                                           // *a, read once per block
+  __device__ __forceinline__ void prepare() {
+    dq.load();
+    as = *a;
+  }
   using Pf = Raw8<T>;
   __device__ __forceinline__ Pf load(int m, int n) const {
     Pf f;
@@ -1048,7 +1071,7 @@ template <class T> struct EpiResidual {
     const int64_t o = (int64_t)m * ld + n;
     float xv[8];
     f.to(xv);
-    const float s = *a;
+    const float s = as;
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = Elem<T>::rnd(dq.apply(v[k]));
     if (branch) Vec8<T>::store(branch + o, v);
@@ -1063,6 +1086,7 @@ template <class T> struct EpiRelu2 {
   static constexpr const char* kName = "relu2";
   static constexpr int kKind = kEpiAmax;
   T* u; T* r; int64_t ld; Deq dq; float* amax;
+  __device__ __forceinline__ void prepare() { dq.load(); }
   __device__ __forceinline__ float seg(int m, int n, float (&v)[8]) const {
     const int64_t o = (int64_t)m * ld + n;
     float rr[8], mx = 0.f;
@@ -1085,6 +1109,7 @@ template <class T> struct EpiRelu2Amax {
   static constexpr const char* kName = "relu2";
   static constexpr int kKind = kEpiAmax;
   T* u; int64_t ld; Deq dq; float* amax;
+  __device__ __forceinline__ void prepare() { dq.load(); }
   __device__ __forceinline__ float seg(int m, int n, float (&v)[8]) const {
     float mx = 0.f;
 #pragma unroll
@@ -1103,6 +1128,7 @@ template <class T> struct EpiRelu2Bwd {
   static constexpr const char* kName = "relu2_bwd";
   static constexpr int kKind = kEpiAmax;
   T* du; const T* u; int64_t ld; Deq dq; float* amax;
+  __device__ __forceinline__ void prepare() { dq.load(); }
   using Pf = Raw8<T>;
   __device__ __forceinline__ Pf load(int m, int n) const {
     Pf f;
@@ -1270,6 +1296,7 @@ template <class T>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int S, int64_t slice,
                                                            int64_t ldp, int M, int N, T* __restrict__ out, int64_t ldo,
                                                            Deq dq, int accumulate) {
+  dq.load();
   const int nseg = N / 8;
   const int64_t total = (int64_t)M * nseg;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
