@@ -40,15 +40,15 @@ P_MM = D * (HQ + 2 * HKV) * DH + D * HQ * DH + 2 * D * F          # 100,663,296
 # the same counters on a 1 GiB device copy; valid only for the kernel sources they were taken on
 # (sha256 of the listed files, first 16 hex digits), else the roofline reports traffic null.
 SOURCES = ("transformer_train_step_amd/csrc/gemm.h", "transformer_train_step_amd/csrc/lce.h",
-           "transformer_train_step_amd/csrc/common.h")
+           "transformer_train_step_amd/csrc/common.h", "transformer_train_step_amd/csrc/lce.hip")
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated (valid while the sources
 # hash to sha256_16; otherwise the roofline reports traffic null)
 TRAFFIC = {
-    "gemm_bf16_acc32_kk": {"sources": SOURCES, "sha256_16": "6113901dc6e12607", "read_bytes": 7.0199e+09,
+    "gemm_bf16_acc32_kk": {"sources": SOURCES, "sha256_16": "a9429f20b7be246a", "read_bytes": 7.0470e+09,
                            "write_bytes": 5.4087e+08,
                            "profile": "profiles/gemm_bf16_acc32_kk_hbm_bytes_layer_lce_40x1024.md"},
-    "gemm_bf16_lce_logits_kk": {"sources": SOURCES, "sha256_16": "6113901dc6e12607", "read_bytes": 8.1246e+09,
-                                "write_bytes": 1.0676e+09,
+    "gemm_bf16_lce_logits_kk": {"sources": SOURCES, "sha256_16": "a9429f20b7be246a", "read_bytes": 5.9146e+09,
+                                "write_bytes": 1.0539e+09,
                                 "profile": "profiles/gemm_bf16_lce_logits_kk_hbm_bytes_layer_lce_40x1024.md"},
 }
 

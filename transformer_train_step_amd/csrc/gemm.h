@@ -1338,16 +1338,20 @@ inline const char* gemm_tag() {
 struct GemmOps {
   bool a_kmajor = true, b_kmajor = true;
   const void* zrow = nullptr;       // >= 16 zero bytes: K-tail rows of MN-major operands
+  int group = 0;                    // block-order group (tile rows or columns); 0 = automatic (2)
 };
 
 template <class ET, int BM, int BN, int WGM, int WGN, int KB, int NS, int MODE = 0, class Epi>
 inline hipError_t launch_gemm_cfg(int cfg_id, const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
                                   const Epi& epi, const GemmOps& o, hipStream_t s) {
   const int64_t nbt = cdiv(M, BM) * cdiv(N, BN);
-  // Block order: along the longer side of the output, 2 tile rows (or columns) at a time (measured
-  // on the step's shapes over groups of 2, 3, 4, 8, 16 rows or columns: 3-9% faster than 8 rows for
-  // the e4m3 GEMMs and the loss's dW GEMM, 4% for the logits GEMM, 5x wider than tall)
-  const int G = cdiv(M, BM) >= cdiv(N, BN) ? 2 : -2;
+  // Block order: along the longer side of the output, `group` tile rows (or columns) at a time,
+  // 2 unless the call site asks otherwise. Measured over groups of 1, 2, 3, 4, 8 on the ping-pong
+  // loop: the loss's logits and dH GEMMs run ~1% faster at 4 (their call sites ask for it); the e4m3
+  // MLP GEMMs with their own epilogues 1-4% slower at 4 than at 2 in the step (same box), the loss's
+  // dW GEMM 2.4% slower.
+  const int g = o.group > 0 ? o.group : 2;
+  const int G = cdiv(M, BM) >= cdiv(N, BN) ? g : -g;
   unsigned slices = 1;
   if constexpr (IsSplitK<Epi>::value) slices = (unsigned)std::max<int64_t>(1, cdiv(K, epi.kchunk));
   const dim3 nb((unsigned)nbt, slices);

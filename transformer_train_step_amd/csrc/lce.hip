@@ -16,6 +16,9 @@ constexpr int64_t kDefaultChunk = 10240;
 // block configuration of the logits GEMM with 256-wide vocabulary tiles (configuration 14: 16x16x32
 // MFMAs, ping-pong K loop)
 constexpr int kLogitsConfig = 14;
+// block order of the logits and dH GEMMs: four tile columns (rows) at a time (~1% faster than the
+// default two; the dW GEMM keeps two)
+const GemmOps kGroup4Ops{true, true, nullptr, 4};
 
 struct LcePlan {
   int64_t chunk, chunk_pad, vpad;
@@ -90,7 +93,7 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
       const int oc = gemm_config_override();
       const int cfg = p.vtile == 128 ? (oc == 7 ? 7 : 1)
                                      : ((oc >= 2 && oc <= 6) || (oc >= 8 && oc <= 14) ? oc : kLogitsConfig);
-      const hipError_t e = launch_gemm_with(cfg, Hc, (int64_t)d, W, (int64_t)d, rows, (int)v, d, epi, GemmOps{}, s);
+      const hipError_t e = launch_gemm_with(cfg, Hc, (int64_t)d, W, (int64_t)d, rows, (int)v, d, epi, kGroup4Ops, s);
       LL_HIP(e);
     }
     LL_LAUNCH("lce_lse", (lce_lse_kernel<T>), dim3((unsigned)cdiv(rows, kLseRows)), dim3(256), 0, s, p.part, p.nparts, z,
@@ -110,7 +113,7 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     LL_HIP(hipGetLastError());
     EpiLceDh<T> eh{{dH + r0 * d, (int64_t)d, Deq{nullptr, nullptr}}};
     // dH_c = dz W: A = dz [rows, Vpad] (K-major), B(n = d, k = v) = W^T[d, v] (K-major, zero past V)
-    LL_HIP(launch_gemm(z, p.vpad, static_cast<const T*>(p.wt), p.vpad, rows, d, (int)p.vpad, eh, GemmOps{}, s));
+    LL_HIP(launch_gemm(z, p.vpad, static_cast<const T*>(p.wt), p.vpad, rows, d, (int)p.vpad, eh, kGroup4Ops, s));
     // dW += dz^T H_c: A = dz^T [Vpad, rows_pad], B = H_c^T [D, rows_pad], both K-major over the
     // chunk's tokens (zero past rows); with one chunk the exact fp32 sum over all tokens is
     // rounded straight into dW
