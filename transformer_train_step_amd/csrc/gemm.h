@@ -324,6 +324,11 @@ template <class E> struct HasPf<E, std::void_t<typename E::Pf>> : std::true_type
 template <class E, class = void> struct IsSplitK : std::false_type {};
 template <class E> struct IsSplitK<E, std::void_t<decltype(E::kSplitK)>> : std::bool_constant<E::kSplitK> {};
 
+// Two-GEMM epilogues (static constexpr bool kPair = true; EpiPair below): the grid's blocks from
+// epi.skip on compute a second GEMM, whose operands and shape the epilogue carries.
+template <class E, class = void> struct IsPair : std::false_type {};
+template <class E> struct IsPair<E, std::void_t<decltype(E::kPair)>> : std::bool_constant<E::kPair> {};
+
 // The same for fewer MFMAs than reads: NV0 loads first, then NMF groups each of a share of the
 // NRD reads and NVM loads followed by one MFMA.
 template <int NMF, int NRD, int NVM, int NV0 = 0>
@@ -384,9 +389,30 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   __shared__ __attribute__((aligned(16))) unsigned char st2[NS > 2 ? STAGE : 16];
   __shared__ __attribute__((aligned(16))) unsigned char st3[NS > 3 ? STAGE : 16];
 
+  int bid = (int)blockIdx.x;
+  bool second = false;
+  if constexpr (IsPair<Epi>::value) {
+    static_assert(!IsSplitK<Epi>::value, "a two-GEMM grid has no K slices");
+    // blocks [0, tiles of the first GEMM) take it, [nb0, skip) have nothing to do (skip is a
+    // multiple of 8, so block skip + j runs on XCD j % 8 like block j of a grid of its own), the
+    // rest take the second GEMM
+    if (bid >= (int)(cdiv(M, BM) * cdiv(N, BN))) {
+      if (bid < epi.skip) return;
+      bid -= epi.skip;
+      A = static_cast<const ET*>(epi.a1);
+      B = static_cast<const ET*>(epi.b1);
+      lda = epi.lda1;
+      ldb = epi.ldb1;
+      M = epi.m1;
+      N = epi.n1;
+      K = epi.k1;
+      G = epi.g1;
+      second = true;
+    }
+  }
   const int nbm = (int)cdiv(M, BM), nbn = (int)cdiv(N, BN);
   const int nb = nbm * nbn;
-  int b = xcd_remap(blockIdx.x, nb);
+  int b = xcd_remap(bid, nb);
   // Each XCD walks its share of the tiles G tile rows at a time (G > 0), or -G tile columns at a
   // time (G < 0)
   int bm, bn;
@@ -841,6 +867,7 @@ gemm_kernel(const ET* __restrict__ A, int64_t lda, const ET* __restrict__ B, int
   wait_vmcnt<0>();                                          // drain the repeated tail loads
   __syncthreads();
   Epi ep = epi;                                             // per-launch scalars read once
+  if constexpr (IsPair<Epi>::value) ep.sel = second;
   if constexpr (HasPrepare<Epi>::value) ep.prepare();
 
   const int g = lane >> 4, r16 = lane & 15;
@@ -1279,6 +1306,64 @@ template <class OutT> struct EpiAcc32Out {
   }
 };
 
+// Two independent GEMMs in one grid: the kernel's own operands with e0, then (blocks from skip on)
+// C1 = A1 B1^T with e1 (operands a1, b1 of the kernel's element type, leading dimensions lda1,
+// ldb1, shape m1 x n1 x k1, block order g1). One grid lets the second GEMM's tiles fill the CUs
+// that the first one's last wave of blocks leaves idle. Both epilogues must be plain; sel (set by
+// the kernel) picks the one of the block's GEMM.
+template <class E0, class E1> struct EpiPair {
+  static constexpr bool kPair = true;
+  static constexpr int kKind = kEpiPlain;
+  static_assert(E0::kKind == kEpiPlain && E1::kKind == kEpiPlain, "plain epilogues only");
+  static constexpr bool kPf0 = HasPf<E0>::value, kPf1 = HasPf<E1>::value;
+  E0 e0; E1 e1;
+  const void* a1; int64_t lda1; const void* b1; int64_t ldb1;
+  int m1, n1, k1, g1;
+  int skip = 0;
+  int sel = 0;
+  struct PfPair {
+    typename HasPf<E0>::type p0;
+    typename HasPf<E1>::type p1;
+  };
+  __device__ __forceinline__ void prepare() {
+    if (sel) {
+      if constexpr (HasPrepare<E1>::value) e1.prepare();
+    } else {
+      if constexpr (HasPrepare<E0>::value) e0.prepare();
+    }
+  }
+  __device__ __forceinline__ PfPair pf_load(int m, int n) const {
+    PfPair f;
+    if (sel) {
+      if constexpr (kPf1) f.p1 = e1.load(m, n);
+    } else {
+      if constexpr (kPf0) f.p0 = e0.load(m, n);
+    }
+    return f;
+  }
+  __device__ __forceinline__ void seg_pf(int m, int n, float (&v)[8], const PfPair& f) const {
+    if (sel) {
+      if constexpr (kPf1) e1.seg(m, n, v, f.p1);
+      else e1.seg(m, n, v);
+    } else {
+      if constexpr (kPf0) e0.seg(m, n, v, f.p0);
+      else e0.seg(m, n, v);
+    }
+  }
+};
+
+// EpiPair with the prefetch interface when either epilogue has one
+template <class E0, class E1, bool = HasPf<E0>::value || HasPf<E1>::value> struct EpiPairOf : EpiPair<E0, E1> {
+  using Pf = typename EpiPair<E0, E1>::PfPair;
+  __device__ __forceinline__ Pf load(int m, int n) const { return this->pf_load(m, n); }
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8], const Pf& f) const { this->seg_pf(m, n, v, f); }
+};
+template <class E0, class E1> struct EpiPairOf<E0, E1, false> : EpiPair<E0, E1> {
+  __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
+    this->seg_pf(m, n, v, typename EpiPair<E0, E1>::PfPair{});
+  }
+};
+
 // fp32 partial sums of K slice blockIdx.y: C[blockIdx.y slice + m ldc + n] = acc
 struct EpiSplitK32 {
   static constexpr const char* kName = "splitk";
@@ -1496,6 +1581,38 @@ inline hipError_t launch_gemm(const ET* A, int64_t lda, const ET* B, int64_t ldb
     cfg = e256 >= e128 ? (sizeof(ET) == 1 ? 11 : kk16 ? 14 : o.b_kmajor ? 4 : 3) : 1;
   }
   return launch_gemm_with(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
+}
+
+// Whether two bf16 GEMMs with K-major operands of these leading dimensions can share one grid
+// (launch_gemm_pair): the ping-pong loop is the configuration in force (automatic or 14) and its
+// 32-bit lane offsets reach every row.
+inline bool gemm_pair_ok(int64_t lda0, int64_t ldb0, int64_t lda1, int64_t ldb1) {
+  const int oc = gemm_config_override();
+  const int64_t lim = int64_t(1) << 22;
+  return (oc == 0 || oc == 14) && lda0 < lim && ldb0 < lim && lda1 < lim && ldb1 < lim;
+}
+
+// C0 = A B^T (M x N x K, epilogue epi.e0, block-order group group0) and C1 = A1 B1^T (epi's second
+// GEMM, group epi.g1) in one grid of the ping-pong loop (configuration 14): the first GEMM's tiles
+// are dispatched first, then the second's, so that with the longer-K GEMM first the shorter tiles
+// fill the CUs the first one's last wave leaves idle. bf16, both operands of both GEMMs K-major,
+// K a multiple of 64 (rows zero-padded), N a multiple of 8; the caller checks gemm_pair_ok. The
+// launch trace records the pair's FLOPs as a 1 x 1 x (M N K + M1 N1 K1) GEMM.
+template <class ET, class Epi>
+inline hipError_t launch_gemm_pair(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
+                                   int group0, Epi epi, hipStream_t s) {
+  static_assert(sizeof(ET) == 2 && IsPair<Epi>::value, "bf16 two-GEMM epilogue");
+  if (M <= 0 || N <= 0 || epi.m1 <= 0 || epi.n1 <= 0) return hipErrorInvalidValue;
+  const int64_t nb0 = cdiv(M, 256) * cdiv(N, 256), nb1 = cdiv(epi.m1, 256) * cdiv(epi.n1, 256);
+  epi.skip = (int)round_up(nb0, 8);
+  const int g0 = cdiv(M, 256) >= cdiv(N, 256) ? group0 : -group0;
+  epi.g1 = cdiv(epi.m1, 256) >= cdiv(epi.n1, 256) ? epi.g1 : -epi.g1;
+  const int64_t work = (int64_t)M * N * K + (int64_t)epi.m1 * epi.n1 * epi.k1;
+  const char* tag = gemm_tag<ET, Epi, true, true>();
+  LL_LAUNCH_GEMM(tag, 1, 1, work, 14, 1, (gemm_kernel<ET, 256, 256, 4, 2, 128, 2, true, true, Epi, 4>),
+                 dim3((unsigned)(epi.skip + nb1)), dim3(512), 0, s, A, lda, B, ldb, M, N, K,
+                 static_cast<const ET*>(nullptr), epi, g0);
+  return hipGetLastError();
 }
 
 // Number of K slices (1..smax) for a GEMM of `tiles` 256 x 256 output tiles: the one that fills the

@@ -62,6 +62,11 @@ template <class T> struct EpiLceDh : EpiStore<T> {
   static constexpr const char* kName = "lce_dh";
 };
 
+// dH_c (EpiLceDh) and the chunk's dW GEMM (epilogue EW) in one grid
+template <class T, class EW> struct EpiLceGrads : EpiPairOf<EpiLceDh<T>, EW> {
+  static constexpr const char* kName = "lce_grads";
+};
+
 __global__ void count_valid_kernel(const int32_t* __restrict__ y, int64_t n, int32_t ignore, int* __restrict__ nv) {
   int c = 0;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)

@@ -112,25 +112,44 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     }
     LL_HIP(hipGetLastError());
     EpiLceDh<T> eh{{dH + r0 * d, (int64_t)d, Deq{nullptr, nullptr}}};
-    // dH_c = dz W: A = dz [rows, Vpad] (K-major), B(n = d, k = v) = W^T[d, v] (K-major, zero past V)
-    LL_HIP(launch_gemm(z, p.vpad, static_cast<const T*>(p.wt), p.vpad, rows, d, (int)p.vpad, eh, kGroup4Ops, s));
     // dW += dz^T H_c: A = dz^T [Vpad, rows_pad], B = H_c^T [D, rows_pad], both K-major over the
     // chunk's tokens (zero past rows); with one chunk the exact fp32 sum over all tokens is
     // rounded straight into dW
     LL_HIP(transpose2d(Hc, rows, d, (int64_t)d, static_cast<T*>(p.ht), (int64_t)rows_pad, (int64_t)rows_pad, s));
     const T* dzt = static_cast<const T*>(p.dzt);
     const T* ht = static_cast<const T*>(p.ht);
+    const T* wt = static_cast<const T*>(p.wt);
+    // dH_c = dz W: A = dz [rows, Vpad] (K-major), B(n = d, k = v) = W^T[d, v] (K-major, zero past V).
+    // bf16 runs dH_c and dW's GEMM in one grid, dH's long-K tiles first.
+    auto grads_gemms = [&](auto ew) -> hipError_t {
+      if constexpr (kBf16) {
+        if (gemm_pair_ok(p.vpad, p.vpad, rows_pad, rows_pad)) {
+          EpiLceGrads<T, decltype(ew)> e{};
+          e.e0 = eh;
+          e.e1 = ew;
+          e.a1 = dzt;
+          e.lda1 = rows_pad;
+          e.b1 = ht;
+          e.ldb1 = rows_pad;
+          e.m1 = (int)v;
+          e.n1 = d;
+          e.k1 = rows_pad;
+          e.g1 = 2;
+          return launch_gemm_pair(z, p.vpad, wt, p.vpad, rows, d, (int)p.vpad, 4, e, s);
+        }
+      }
+      const hipError_t r = launch_gemm(z, p.vpad, wt, p.vpad, rows, d, (int)p.vpad, eh, kGroup4Ops, s);
+      if (r != hipSuccess) return r;
+      return launch_gemm(dzt, (int64_t)rows_pad, ht, (int64_t)rows_pad, (int)v, d, rows_pad, ew, GemmOps{}, s);
+    };
     if (p.single) {
-      EpiStore<T> ewd{dW, (int64_t)d, Deq{nullptr, nullptr}, accumulate_dw};
-      LL_HIP(launch_gemm(dzt, (int64_t)rows_pad, ht, (int64_t)rows_pad, (int)v, d, rows_pad, ewd, GemmOps{}, s));
+      LL_HIP(grads_gemms(EpiStore<T>{dW, (int64_t)d, Deq{nullptr, nullptr}, accumulate_dw}));
     } else if (r0 + rows < n) {
       // fp32 sums over the chunks in dw32
-      EpiAcc32 ew{p.dw32, (int64_t)d, r0 > 0 ? 1 : 0};
-      LL_HIP(launch_gemm(dzt, (int64_t)rows_pad, ht, (int64_t)rows_pad, (int)v, d, rows_pad, ew, GemmOps{}, s));
+      LL_HIP(grads_gemms(EpiAcc32{p.dw32, (int64_t)d, r0 > 0 ? 1 : 0}));
     } else {
       // the last chunk's GEMM rounds the fp32 total into dW
-      EpiAcc32Out<T> ew{p.dw32, dW, (int64_t)d, accumulate_dw};
-      LL_HIP(launch_gemm(dzt, (int64_t)rows_pad, ht, (int64_t)rows_pad, (int)v, d, rows_pad, ew, GemmOps{}, s));
+      LL_HIP(grads_gemms(EpiAcc32Out<T>{p.dw32, dW, (int64_t)d, accumulate_dw}));
     }
   }
   if (grads && n == 0 && !accumulate_dw) {                 // no chunk ran: dW = 0 (unchanged when accumulating)
