@@ -4,8 +4,9 @@ layer's own e4m3 quantisation state checked bit for bit.
 At 4 x 1024 tokens (and 2 x 2048 on a value-embedding layer) every e4m3 GEMM of the MLP runs the
 block configuration the 40 x 1024 benchmark runs (configuration 11: 256 x 256 tiles, split-phase K
 loop on the 32x32x64 MFMA) with its fused epilogues (relu^2 + amax, residual, relu^2 backward),
-the two FP8 weight gradients split along the tokens in 4 slices, and the bf16 O-projection weight
-gradient split in 7 slices; the tests assert this from the launch trace. y, dx, every weight
+the two FP8 weight gradients unsplit over the tokens, each in one grid with the input-side GEMM of
+the same backward step (dW2 beside the relu^2 backward GEMM, dW1 beside dhn), and the bf16
+O-projection weight gradient split in 7 slices; the tests assert this from the launch trace. y, dx, every weight
 gradient and the value-embedding gradient are compared with the float64 oracle on the same inputs.
 
 Bit-exact: the scale, inverse scale and amax of all six quantised tensors (hn, W1, r, W2, dm, du)
@@ -123,18 +124,23 @@ def test_fp8_layer_takes_the_production_paths(key):
     need_gpu()
     s, _, _, _, _, launches = run_case(key)
     D, F, QD = s.d_model, s.d_ff, s.n_q_heads * s.head_dim
+    N, Np = s.tokens, -(-s.tokens // 128) * 128
     e4 = [l for l in launches if l[0].startswith("gemm_e4m3")]
-    assert len(e4) == 6, [l[0] for l in e4]
+    assert len(e4) == 4, [l[0] for l in e4]
     # every e4m3 GEMM on the 32x32x64 split-phase loop (configuration 11)
     assert all(l[2] == 11 for l in e4), [(l[0], l[2]) for l in e4]
-    tags = {l[0] for l in e4}
-    assert {"gemm_e4m3_relu2_kk", "gemm_e4m3_residual_kk", "gemm_e4m3_relu2_bwd_kk", "gemm_e4m3_store_kk",
-            "gemm_e4m3_splitk_kk"} == tags, tags
-    split8 = sorted((l[1][0], l[1][1], l[3]) for l in e4 if l[0] == "gemm_e4m3_splitk_kk")
-    assert split8 == sorted([(D, F, 4), (F, D, 4)]), split8
+    tags = [l[0] for l in e4]
+    assert tags == ["gemm_e4m3_relu2_kk", "gemm_e4m3_residual_kk", "gemm_e4m3_wgrad_relu2_bwd_kk",
+                    "gemm_e4m3_wgrad_dgrad_kk"], tags
+    # the backward's two grids, each an unsplit weight gradient over the Np tokens beside the input-side
+    # GEMM (recorded as 1 x 1 x total MNK)
+    pairs = {l[0]: l for l in e4[2:]}
+    assert pairs["gemm_e4m3_wgrad_relu2_bwd_kk"][1] == (1, 1, D * F * Np + N * F * D)
+    assert pairs["gemm_e4m3_wgrad_dgrad_kk"][1] == (1, 1, F * D * Np + N * D * F)
+    assert all(l[3] == 1 for l in e4)
     wo = [l for l in launches if l[0].startswith("gemm_bf16_splitk") and l[1][:2] == (D, QD)]
     assert len(wo) == 1 and wo[0][3] == 7, wo
-    assert sum(l[0] == "splitk_reduce" for l in launches) == 3
+    assert sum(l[0] == "splitk_reduce" for l in launches) == 1
 
 
 @pytest.mark.parametrize("key", sorted(CASES))

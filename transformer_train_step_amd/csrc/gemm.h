@@ -1309,22 +1309,29 @@ template <class OutT> struct EpiAcc32Out {
 // Two independent GEMMs in one grid: the kernel's own operands with e0, then (blocks from skip on)
 // C1 = A1 B1^T with e1 (operands a1, b1 of the kernel's element type, leading dimensions lda1,
 // ldb1, shape m1 x n1 x k1, block order g1). One grid lets the second GEMM's tiles fill the CUs
-// that the first one's last wave of blocks leaves idle. Both epilogues must be plain; sel (set by
-// the kernel) picks the one of the block's GEMM.
+// that the first one's last wave of blocks leaves idle. Each epilogue is plain or amax-reducing (at
+// most one of the two reducing); sel (set by the kernel) picks the one of the block's GEMM, and the
+// blocks of a plain one contribute 0 to the other's amax.
 template <class E0, class E1> struct EpiPair {
   static constexpr bool kPair = true;
-  static constexpr int kKind = kEpiPlain;
-  static_assert(E0::kKind == kEpiPlain && E1::kKind == kEpiPlain, "plain epilogues only");
-  static constexpr bool kPf0 = HasPf<E0>::value, kPf1 = HasPf<E1>::value;
+  static constexpr bool kAmax0 = E0::kKind == kEpiAmax, kAmax1 = E1::kKind == kEpiAmax;
+  static constexpr int kKind = kAmax0 || kAmax1 ? kEpiAmax : kEpiPlain;
+  static_assert((E0::kKind == kEpiPlain || kAmax0) && (E1::kKind == kEpiPlain || kAmax1) && !(kAmax0 && kAmax1),
+                "plain epilogues, at most one of them amax-reducing");
   E0 e0; E1 e1;
   const void* a1; int64_t lda1; const void* b1; int64_t ldb1;
   int m1, n1, k1, g1;
   int skip = 0;
   int sel = 0;
+  float* amax = nullptr;                                    // the reducing epilogue's (set by the launch)
   struct PfPair {
     typename HasPf<E0>::type p0;
     typename HasPf<E1>::type p1;
   };
+  __host__ __device__ void set_amax() {
+    if constexpr (kAmax0) amax = e0.amax;
+    if constexpr (kAmax1) amax = e1.amax;
+  }
   __device__ __forceinline__ void prepare() {
     if (sel) {
       if constexpr (HasPrepare<E1>::value) e1.prepare();
@@ -1335,20 +1342,25 @@ template <class E0, class E1> struct EpiPair {
   __device__ __forceinline__ PfPair pf_load(int m, int n) const {
     PfPair f;
     if (sel) {
-      if constexpr (kPf1) f.p1 = e1.load(m, n);
+      if constexpr (HasPf<E1>::value) f.p1 = e1.load(m, n);
     } else {
-      if constexpr (kPf0) f.p0 = e0.load(m, n);
+      if constexpr (HasPf<E0>::value) f.p0 = e0.load(m, n);
     }
     return f;
   }
-  __device__ __forceinline__ void seg_pf(int m, int n, float (&v)[8], const PfPair& f) const {
-    if (sel) {
-      if constexpr (kPf1) e1.seg(m, n, v, f.p1);
-      else e1.seg(m, n, v);
+  template <class E, class F>
+  __device__ __forceinline__ static float run(const E& e, int m, int n, float (&v)[8], const F& f) {
+    if constexpr (HasPf<E>::value) {
+      if constexpr (E::kKind == kEpiAmax) return e.seg(m, n, v, f);
+      else e.seg(m, n, v, f);
     } else {
-      if constexpr (kPf0) e0.seg(m, n, v, f.p0);
-      else e0.seg(m, n, v);
+      if constexpr (E::kKind == kEpiAmax) return e.seg(m, n, v);
+      else e.seg(m, n, v);
     }
+    return 0.f;
+  }
+  __device__ __forceinline__ float seg_pf(int m, int n, float (&v)[8], const PfPair& f) const {
+    return sel ? run(e1, m, n, v, f.p1) : run(e0, m, n, v, f.p0);
   }
 };
 
@@ -1356,11 +1368,11 @@ template <class E0, class E1> struct EpiPair {
 template <class E0, class E1, bool = HasPf<E0>::value || HasPf<E1>::value> struct EpiPairOf : EpiPair<E0, E1> {
   using Pf = typename EpiPair<E0, E1>::PfPair;
   __device__ __forceinline__ Pf load(int m, int n) const { return this->pf_load(m, n); }
-  __device__ __forceinline__ void seg(int m, int n, float (&v)[8], const Pf& f) const { this->seg_pf(m, n, v, f); }
+  __device__ __forceinline__ float seg(int m, int n, float (&v)[8], const Pf& f) const { return this->seg_pf(m, n, v, f); }
 };
 template <class E0, class E1> struct EpiPairOf<E0, E1, false> : EpiPair<E0, E1> {
-  __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
-    this->seg_pf(m, n, v, typename EpiPair<E0, E1>::PfPair{});
+  __device__ __forceinline__ float seg(int m, int n, float (&v)[8]) const {
+    return this->seg_pf(m, n, v, typename EpiPair<E0, E1>::PfPair{});
   }
 };
 
@@ -1583,33 +1595,44 @@ inline hipError_t launch_gemm(const ET* A, int64_t lda, const ET* B, int64_t ldb
   return launch_gemm_with(cfg, A, lda, B, ldb, M, N, K, epi, o, s);
 }
 
-// Whether two bf16 GEMMs with K-major operands of these leading dimensions can share one grid
-// (launch_gemm_pair): the ping-pong loop is the configuration in force (automatic or 14) and its
-// 32-bit lane offsets reach every row.
+// Whether two GEMMs with K-major operands of these leading dimensions can share one grid
+// (launch_gemm_pair): the configuration in force is the automatic one or the pair's own (bf16: the
+// ping-pong loop, 14, whose 32-bit lane offsets must reach every row; e4m3: the 32x32x64
+// split-phase loop, 11).
+template <class ET>
 inline bool gemm_pair_ok(int64_t lda0, int64_t ldb0, int64_t lda1, int64_t ldb1) {
+  static_assert(sizeof(ET) <= 2, "bf16 or e4m3");
   const int oc = gemm_config_override();
-  const int64_t lim = int64_t(1) << 22;
-  return (oc == 0 || oc == 14) && lda0 < lim && ldb0 < lim && lda1 < lim && ldb1 < lim;
+  if constexpr (sizeof(ET) == 1) {
+    return oc == 0 || oc == 11;
+  } else {
+    const int64_t lim = int64_t(1) << 22;
+    return (oc == 0 || oc == 14) && lda0 < lim && ldb0 < lim && lda1 < lim && ldb1 < lim;
+  }
 }
 
 // C0 = A B^T (M x N x K, epilogue epi.e0, block-order group group0) and C1 = A1 B1^T (epi's second
-// GEMM, group epi.g1) in one grid of the ping-pong loop (configuration 14): the first GEMM's tiles
-// are dispatched first, then the second's, so that with the longer-K GEMM first the shorter tiles
-// fill the CUs the first one's last wave leaves idle. bf16, both operands of both GEMMs K-major,
-// K a multiple of 64 (rows zero-padded), N a multiple of 8; the caller checks gemm_pair_ok. The
+// GEMM, group epi.g1) in one grid: the first GEMM's tiles are dispatched first, then the second's,
+// so that with the longer-K GEMM first the shorter tiles fill the CUs the first one's last wave
+// leaves idle. 256 x 256 tiles, 8 waves: bf16 on the ping-pong loop (configuration 14), e4m3 on the
+// 32x32x64 split-phase loop (11). Both operands of both GEMMs K-major, K a multiple of the K tile
+// (64 bf16, 128 e4m3; rows zero-padded), N a multiple of 8; the caller checks gemm_pair_ok. The
 // launch trace records the pair's FLOPs as a 1 x 1 x (M N K + M1 N1 K1) GEMM.
 template <class ET, class Epi>
 inline hipError_t launch_gemm_pair(const ET* A, int64_t lda, const ET* B, int64_t ldb, int M, int N, int K,
                                    int group0, Epi epi, hipStream_t s) {
-  static_assert(sizeof(ET) == 2 && IsPair<Epi>::value, "bf16 two-GEMM epilogue");
+  static_assert(sizeof(ET) <= 2 && IsPair<Epi>::value, "bf16 or e4m3 two-GEMM epilogue");
   if (M <= 0 || N <= 0 || epi.m1 <= 0 || epi.n1 <= 0) return hipErrorInvalidValue;
   const int64_t nb0 = cdiv(M, 256) * cdiv(N, 256), nb1 = cdiv(epi.m1, 256) * cdiv(epi.n1, 256);
   epi.skip = (int)round_up(nb0, 8);
+  epi.set_amax();
   const int g0 = cdiv(M, 256) >= cdiv(N, 256) ? group0 : -group0;
   epi.g1 = cdiv(epi.m1, 256) >= cdiv(epi.n1, 256) ? epi.g1 : -epi.g1;
   const int64_t work = (int64_t)M * N * K + (int64_t)epi.m1 * epi.n1 * epi.k1;
   const char* tag = gemm_tag<ET, Epi, true, true>();
-  LL_LAUNCH_GEMM(tag, 1, 1, work, 14, 1, (gemm_kernel<ET, 256, 256, 4, 2, 128, 2, true, true, Epi, 4>),
+  constexpr int kMode = sizeof(ET) == 1 ? 3 : 4;
+  LL_LAUNCH_GEMM(tag, 1, 1, work, sizeof(ET) == 1 ? 11 : 14, 1,
+                 (gemm_kernel<ET, 256, 256, 4, 2, 128, 2, true, true, Epi, kMode>),
                  dim3((unsigned)(epi.skip + nb1)), dim3(512), 0, s, A, lda, B, ldb, M, N, K,
                  static_cast<const ET*>(nullptr), epi, g0);
   return hipGetLastError();

@@ -130,18 +130,14 @@ struct BwdWs {
   float *delta, *dqh, *dkh, *dgp;
 };
 // Floats of split-K partial sums the backward needs: the largest slices x M x N over the weight
-// gradients that split (the FP8 MLP weight gradients; the bf16 O-projection and QKV weight
-// gradients), with the slice counts the launches will pick.
+// gradients that split (the bf16 O-projection and QKV weight gradients; the FP8 MLP weight
+// gradients run unsplit beside another GEMM), with the slice counts the launches will pick.
 int64_t splitk_floats(const Dims& d) {
   int64_t f = 0;
   auto need = [&](int M, int N, int64_t K, int ke) {
     const int sl = splitk_slices(cdiv(M, 256) * cdiv(N, 256), K, ke, 8);
     if (sl > 1) f = std::max<int64_t>(f, (int64_t)sl * M * N);
   };
-  if (d.fp8) {
-    need(d.D, d.F, d.Np, 128);
-    need(d.F, d.D, d.Np, 128);
-  }
   if (d.bf) {
     need(d.D, d.QD, d.N, 64);
     need(d.QKVD, d.D, d.N, 64);
@@ -346,16 +342,39 @@ int layer_fwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
 }
 
 // FP8 weight gradient C [M, N] = deq(X Y^T) over the token axis (both operands the quantiser's
-// transposed codes, K-major, Np tokens): split along the tokens when the output has too few 256 x 256
-// tiles for the chip and the scratch holds the partial sums.
+// transposed codes, K-major, Np tokens), as its own launch: the path of a GEMM-configuration
+// override that the two-GEMM grids below do not run.
 template <class T>
-hipError_t wgrad_e4m3(const uint8_t* X, const uint8_t* Y, int64_t Np, int M, int N, T* C, Deq dq, float* sk,
-                      size_t sk_bytes, int accumulate, hipStream_t s) {
-  const int sl = splitk_slices(cdiv(M, 256) * cdiv(N, 256), Np, 128, 8);
-  if (sl > 1 && (size_t)sl * M * N * sizeof(float) <= sk_bytes && gemm_config_override() == 0)
-    return launch_gemm_splitk(X, Np, Y, Np, M, N, (int)Np, sl, C, (int64_t)N, sk, GemmOps{}, s, dq, accumulate);
+hipError_t wgrad_e4m3(const uint8_t* X, const uint8_t* Y, int64_t Np, int M, int N, T* C, Deq dq, int accumulate,
+                      hipStream_t s) {
   EpiStore<T> e{C, (int64_t)N, dq, accumulate};
   return launch_gemm_nt(X, Np, Y, Np, M, N, (int)Np, e, s);
+}
+
+// The FP8 MLP backward's GEMMs as two grids: each weight gradient (K = the Np tokens, unsplit) with
+// the input-side GEMM of the same step, the weight gradient's long tiles first
+template <class E0, class E1> struct EpiWgradRelu2Bwd : EpiPairOf<E0, E1> {
+  static constexpr const char* kName = "wgrad_relu2_bwd";
+};
+template <class E0, class E1> struct EpiWgradDgrad : EpiPairOf<E0, E1> {
+  static constexpr const char* kName = "wgrad_dgrad";
+};
+template <class Pair, class E0, class E1>
+hipError_t wgrad_pair_e4m3(const uint8_t* X, const uint8_t* Y, int64_t Np, int M, int N, const E0& ew,
+                           const uint8_t* A1, const uint8_t* B1, int64_t K1, int M1, int N1, const E1& e1,
+                           hipStream_t s) {
+  Pair e{};
+  e.e0 = ew;
+  e.e1 = e1;
+  e.a1 = A1;
+  e.lda1 = K1;
+  e.b1 = B1;
+  e.ldb1 = K1;
+  e.m1 = M1;
+  e.n1 = N1;
+  e.k1 = (int)K1;
+  e.g1 = 2;
+  return launch_gemm_pair(X, Np, Y, Np, M, N, (int)Np, 2, e, s);
 }
 
 // ------------------------------------------------------------------------------------------ bwd
@@ -384,23 +403,29 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
       QScale* qdu = &w.qs[1];
       LL_HIP(launch_cast_e4m3(CP<T>(w.dm), N, d.D, d.D, qdm, w.dm8, d.D, w.dm8t, Np, Np, (float*)nullptr,
                               (float*)nullptr, s));
-      {   // dr = dm W2 (W2^T quantised is [F, D]); du = dr * 2 relu(u)
-        EpiRelu2Bwd<T> e{P<T>(w.du), CP<T>(sv.u), (int64_t)d.F, Deq{&qdm->inv_scale, &q[QS_W2].inv_scale}, &qdu->amax};
-        LL_HIP(launch_gemm_nt(w.dm8, d.D, sv.w28t, d.D, (int)N, d.F, d.D, e, s));
-      }
-      LL_HIP(launch_cast_e4m3(CP<T>(w.du), N, d.F, d.F, qdu, w.du8, d.F, w.du8t, Np, Np, (float*)nullptr,
-                              (float*)nullptr, s));
-      float* sk = w.sk;
-      const size_t sk_bytes = w.sk_bytes;
+      // dr = dm W2 (W2^T quantised is [F, D]); du = dr * 2 relu(u)
+      const EpiRelu2Bwd<T> erb{P<T>(w.du), CP<T>(sv.u), (int64_t)d.F, Deq{&qdm->inv_scale, &q[QS_W2].inv_scale},
+                               &qdu->amax};
       // dW2 = dm^T r   [D, F]
-      LL_HIP(wgrad_e4m3(w.dm8t, sv.r8t, Np, d.D, d.F, P<T>(g->w_proj), Deq{&qdm->inv_scale, &q[QS_R].inv_scale}, sk,
-                        sk_bytes, acc, s));
+      const EpiStore<T> ew2{P<T>(g->w_proj), (int64_t)d.F, Deq{&qdm->inv_scale, &q[QS_R].inv_scale}, acc};
       // dW1 = du^T hn  [F, D]
-      LL_HIP(wgrad_e4m3(w.du8t, sv.hn8t, Np, d.F, d.D, P<T>(g->w_fc), Deq{&qdu->inv_scale, &q[QS_HN].inv_scale}, sk,
-                        sk_bytes, acc, s));
-      {   // dhn = du W1 (W1^T quantised is [D, F])
-        EpiStore<T> e{P<T>(w.dhn), (int64_t)d.D, Deq{&qdu->inv_scale, &q[QS_W1].inv_scale}};
-        LL_HIP(launch_gemm_nt(w.du8, d.F, sv.w18t, d.F, (int)N, d.D, d.F, e, s));
+      const EpiStore<T> ew1{P<T>(g->w_fc), (int64_t)d.D, Deq{&qdu->inv_scale, &q[QS_HN].inv_scale}, acc};
+      // dhn = du W1 (W1^T quantised is [D, F])
+      const EpiStore<T> edh{P<T>(w.dhn), (int64_t)d.D, Deq{&qdu->inv_scale, &q[QS_W1].inv_scale}};
+      if (gemm_pair_ok<uint8_t>(Np, Np, d.D, d.F)) {
+        LL_HIP((wgrad_pair_e4m3<EpiWgradRelu2Bwd<EpiStore<T>, EpiRelu2Bwd<T>>>(
+            w.dm8t, sv.r8t, Np, d.D, d.F, ew2, w.dm8, sv.w28t, d.D, (int)N, d.F, erb, s)));
+        LL_HIP(launch_cast_e4m3(CP<T>(w.du), N, d.F, d.F, qdu, w.du8, d.F, w.du8t, Np, Np, (float*)nullptr,
+                                (float*)nullptr, s));
+        LL_HIP((wgrad_pair_e4m3<EpiWgradDgrad<EpiStore<T>, EpiStore<T>>>(
+            w.du8t, sv.hn8t, Np, d.F, d.D, ew1, w.du8, sv.w18t, d.F, (int)N, d.D, edh, s)));
+      } else {
+        LL_HIP(launch_gemm_nt(w.dm8, d.D, sv.w28t, d.D, (int)N, d.F, d.D, erb, s));
+        LL_HIP(launch_cast_e4m3(CP<T>(w.du), N, d.F, d.F, qdu, w.du8, d.F, w.du8t, Np, Np, (float*)nullptr,
+                                (float*)nullptr, s));
+        LL_HIP(wgrad_e4m3(w.dm8t, sv.r8t, Np, d.D, d.F, ew2.C, ew2.dq, acc, s));
+        LL_HIP(wgrad_e4m3(w.du8t, sv.hn8t, Np, d.F, d.D, ew1.C, ew1.dq, acc, s));
+        LL_HIP(launch_gemm_nt(w.du8, d.F, sv.w18t, d.F, (int)N, d.D, d.F, edh, s));
       }
       done = true;
     }

@@ -123,7 +123,7 @@ int run_lce(const T* H, const T* W, const int32_t* y, int64_t n, int d, int64_t 
     // bf16 runs dH_c and dW's GEMM in one grid, dH's long-K tiles first.
     auto grads_gemms = [&](auto ew) -> hipError_t {
       if constexpr (kBf16) {
-        if (gemm_pair_ok(p.vpad, p.vpad, rows_pad, rows_pad)) {
+        if (gemm_pair_ok<bf16>(p.vpad, p.vpad, rows_pad, rows_pad)) {
           EpiLceGrads<T, decltype(ew)> e{};
           e.e0 = eh;
           e.e1 = ew;
