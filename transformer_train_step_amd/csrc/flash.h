@@ -101,6 +101,53 @@ __device__ __forceinline__ void fa_store4(bf16* p, const floatx4& v, float s) {
   *reinterpret_cast<uint2*>(p) = make_uint2(fa_pack(v[0] * s, v[1] * s), fa_pack(v[2] * s, v[3] * s));
 }
 
+// Backward of x^ = RoPE(x / rms(x)) (QK-norm without a gain, then the rotation of channel pairs
+// (i, i + 64) by the position's angles) for one 128-element head row held by the 4 lanes
+// g = 0..3 of one column c16 of an MFMA result: a[t][r] is the gradient of x^ at channel
+// 16 t + 4 g + r, before the factor sc. With dr = RoPE^T(sc a) and rr = 1 / rms(x):
+// dx = rr dr - x rr^3 mean(x . dr) [hn.213312.xyz translation, 设置 / Setup: QK-norm and RoPE].
+// xr: the raw row (bf16), csr: its position's (cos, sin) of pairs 0..63, dst: where dx goes (bf16);
+// every lane takes part in the row sum, only lanes with `store` write.
+__device__ __forceinline__ void fa_norm_rope_bwd(const floatx4 (&a)[8], float sc, const bf16* __restrict__ xr,
+                                                 const float2* __restrict__ csr, float rr, bf16* __restrict__ dst,
+                                                 int g, bool store) {
+  float t0[4][4], t1[4][4], x0[4][4], x1[4][4];
+  float dot = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int i = 16 * t + 4 * g;
+    const uint2 u0 = *reinterpret_cast<const uint2*>(xr + i);
+    const uint2 u1 = *reinterpret_cast<const uint2*>(xr + i + 64);
+    const float4 c01 = *reinterpret_cast<const float4*>(csr + i);
+    const float4 c23 = *reinterpret_cast<const float4*>(csr + i + 2);
+    const float cv[4] = {c01.x, c01.z, c23.x, c23.z}, sv[4] = {c01.y, c01.w, c23.y, c23.w};
+    const uint32_t w0[2] = {u0.x, u0.y}, w1[2] = {u1.x, u1.y};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x0[t][r] = __uint_as_float(r & 1 ? (w0[r >> 1] & 0xffff0000u) : (w0[r >> 1] << 16));
+      x1[t][r] = __uint_as_float(r & 1 ? (w1[r >> 1] & 0xffff0000u) : (w1[r >> 1] << 16));
+      const float d0 = a[t][r] * sc, d1 = a[t + 4][r] * sc;
+      t0[t][r] = d0 * cv[r] + d1 * sv[r];            // rotation by -angle
+      t1[t][r] = -d0 * sv[r] + d1 * cv[r];
+      dot += x0[t][r] * t0[t][r] + x1[t][r] * t1[t][r];
+    }
+  }
+  dot += __shfl_xor(dot, 16, 64);
+  dot += __shfl_xor(dot, 32, 64);
+  const float k3 = rr * rr * rr * dot * (1.f / 128.f);
+  if (!store) return;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int i = 16 * t + 4 * g;
+    *reinterpret_cast<uint2*>(dst + i) =
+        make_uint2(fa_pack(rr * t0[t][0] - x0[t][0] * k3, rr * t0[t][1] - x0[t][1] * k3),
+                   fa_pack(rr * t0[t][2] - x0[t][2] * k3, rr * t0[t][3] - x0[t][3] * k3));
+    *reinterpret_cast<uint2*>(dst + i + 64) =
+        make_uint2(fa_pack(rr * t1[t][0] - x1[t][0] * k3, rr * t1[t][1] - x1[t][1] * k3),
+                   fa_pack(rr * t1[t][2] - x1[t][2] * k3, rr * t1[t][3] - x1[t][3] * k3));
+  }
+}
+
 // Block (4 waves) -> (b, h, query block qb): query blocks with the most key tiles first, and the
 // Hq/Hkv heads sharing one K/V head on the same XCD (block indices Hkv * B apart).
 struct FaBlock {
@@ -204,6 +251,9 @@ fa_fwd_kernel(const bf16* __restrict__ qkv, int64_t ldqkv, const float2* __restr
   auto compute = [&](const unsigned char* sK, int kt) __attribute__((always_inline)) {
     const unsigned char* sV = sK + 64 * 256;
     const int k0 = kt * 64;
+    // a key tile wholly at or below the diagonal of this wave's queries, and inside T, needs no
+    // mask (wave-uniform: a scalar branch)
+    const bool full = __builtin_amdgcn_readfirstlane((int)(k0 + 63 <= qw && k0 + 64 <= T)) != 0;
     floatx4 s[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -219,15 +269,26 @@ fa_fwd_kernel(const bf16* __restrict__ qkv, int64_t ldqkv, const float2* __restr
     for (int j = 0; j < 2; ++j) {
       const int q = qw + 16 * j + c16;
       float tmax = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = k0 + 16 * i + 4 * g + r;
-          const float x = (key <= q && key < T) ? s[i][j][r] * sl2 : -INFINITY;
-          s[i][j][r] = x;
-          tmax = fmaxf(tmax, x);
-        }
+          for (int r = 0; r < 4; ++r) {
+            const float x = s[i][j][r] * sl2;
+            s[i][j][r] = x;
+            tmax = fmaxf(tmax, x);
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0 + 16 * i + 4 * g + r;
+            const float x = (key <= q && key < T) ? s[i][j][r] * sl2 : -INFINITY;
+            s[i][j][r] = x;
+            tmax = fmaxf(tmax, x);
+          }
+      }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       // key 0 is visible to every query, so m is finite from the first tile on
@@ -310,11 +371,14 @@ fa_fwd_kernel(const bf16* __restrict__ qkv, int64_t ldqkv, const float2* __restr
 // dS = P (dP - Delta); dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from transpose reads.
 // lse and delta are [B, Hq, ldl] with ldl >= T rounded up to 64 (entries past T may hold anything);
 // each lane loads the 16 values of its query rows one tile ahead into registers.
+// The epilogue writes dV and, through the backward of the keys' QK-norm and RoPE, dK straight into
+// their columns of the QKV-projection gradient: kraw (the raw k columns of the QKV projection), dk
+// and dv all have row stride lddv; cs [T, 64] holds the RoPE (cos, sin), rk [N, Hkv] 1 / rms(k).
 __global__ void __launch_bounds__(256, 1)
 fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const bf16* __restrict__ v, int64_t ldv,
                const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
-               int64_t ldl, float* __restrict__ dkh, bf16* __restrict__ dv, int64_t lddv, int B, int T, int Hq,
-               int Hkv) {
+               int64_t ldl, const bf16* __restrict__ kraw, const float2* __restrict__ cs, const float* __restrict__ rk,
+               bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t lddv, int B, int T, int Hq, int Hkv) {
   constexpr int DH = 128;
   constexpr int TILE = 64 * 256, STAGE = 2 * TILE;
   constexpr int NIW = 4 + 4;                           // direct loads per wave per stage
@@ -388,18 +452,34 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
         }
       }
     }
+    // a query tile wholly at or past the diagonal of this wave's keys, and inside T, needs no mask
+    // (wave-uniform: a scalar branch)
+    const bool full = __builtin_amdgcn_readfirstlane((int)(live && q0 >= kw + 31 && q0 + 64 <= T && kw + 32 <= T)) != 0;
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int key = kw + 16 * j + c16;
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = q0 + 16 * i + 4 * g + r;
-          const bool ok = live && key <= q && q < T && key < T;
-          const float p = __builtin_amdgcn_exp2f(s[j][i][r] * sl2 - l4[i][r] * kFaLog2e);
-          s[j][i][r] = ok ? p : 0.f;
-          dp[j][i][r] = ok ? p * (dp[j][i][r] - d4[i][r]) : 0.f;
+          for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(s[j][i][r] * sl2 - l4[i][r] * kFaLog2e);
+            s[j][i][r] = p;
+            dp[j][i][r] = p * (dp[j][i][r] - d4[i][r]);
+          }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int key = kw + 16 * j + c16;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int q = q0 + 16 * i + 4 * g + r;
+            const bool ok = live && key <= q && q < T && key < T;
+            const float p = __builtin_amdgcn_exp2f(s[j][i][r] * sl2 - l4[i][r] * kFaLog2e);
+            s[j][i][r] = ok ? p : 0.f;
+            dp[j][i][r] = ok ? p * (dp[j][i][r] - d4[i][r]) : 0.f;
+          }
         }
       }
     }
@@ -452,16 +532,20 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
   const float sc = 1.f / sqrtf((float)DH);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int key = kw + 16 * j + c16;
-    if (key >= T) continue;
-    bf16* dvr = dv + ((int64_t)b * T + key) * lddv + (int64_t)hk * DH + 4 * g;
-    float* dkr = dkh + (((int64_t)b * T + key) * Hkv + hk) * DH + 4 * g;
+    // the row index passes through an empty asm so that the epilogue's addresses and loads are formed
+    // here, not hoisted above the query loop where they would hold registers the loop needs
+    int kk = kw + 16 * j + c16;
+    asm volatile("" : "+v"(kk));
+    const int key = min(kk, T - 1);
+    const int64_t n = (int64_t)b * T + key;
+    if (kk < T) {
+      bf16* dvr = dv + n * lddv + (int64_t)hk * DH + 4 * g;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      fa_store4(dvr + 16 * t, dva[j][t], 1.f);
-      *reinterpret_cast<float4*>(dkr + 16 * t) =
-          make_float4(dka[j][t][0] * sc, dka[j][t][1] * sc, dka[j][t][2] * sc, dka[j][t][3] * sc);
+      for (int t = 0; t < 8; ++t) fa_store4(dvr + 16 * t, dva[j][t], 1.f);
     }
+    // dk^ -> dk through the backward of the key's QK-norm and RoPE
+    fa_norm_rope_bwd(dka[j], sc, kraw + n * lddv + (int64_t)hk * DH, cs + (int64_t)key * (DH / 2),
+                     rk[n * Hkv + hk], dk + n * lddv + (int64_t)hk * DH, g, kk < T);
   }
 }
 
@@ -469,11 +553,14 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
 // Block: one (b, h) and 128 queries, wave w the 32 queries q0 + 32 w .. (Q and dO in registers as
 // `second` operands). Per 64-key tile up to the diagonal: S^T = K Q^T and dP^T = V dO^T (lane:
 // query column, 4 key rows), dS^T = P^T (dP^T - Delta); dQ^T += K^T dS^T with K^T from transpose
-// reads. Writes dqh fp32 [N, Hq, 128] scaled by 1/sqrt(DH).
+// reads. The epilogue scales dQ^ by 1/sqrt(DH) and takes it through the backward of the queries'
+// QK-norm and RoPE: qraw (the raw q columns of the QKV projection) and dq (their columns of its
+// gradient) have row stride ldv; cs [T, 64] holds the RoPE (cos, sin), rq [N, Hq] 1 / rms(q).
 __global__ void __launch_bounds__(256, 2)
 fa_dq_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const bf16* __restrict__ v, int64_t ldv,
              const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta, int64_t ldl,
-             float* __restrict__ dqh, int B, int T, int Hq, int Hkv) {
+             const bf16* __restrict__ qraw, const float2* __restrict__ cs, const float* __restrict__ rq,
+             bf16* __restrict__ dq, int B, int T, int Hq, int Hkv) {
   constexpr int DH = 128, STAGE = 2 * 64 * 256;
   __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE];
@@ -527,6 +614,8 @@ fa_dq_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const bf1
         }
       }
     }
+    // (a mask-free branch for the tiles below the diagonal, as in the other two kernels, makes
+    // this one spill inside the loop at 2 waves per SIMD)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int q = qw + 16 * j + c16;
@@ -577,13 +666,18 @@ fa_dq_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const bf1
   const float sc = 1.f / sqrtf((float)DH);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int q = qw + 16 * j + c16;
-    if (q >= T) continue;
-    float* dqr = dqh + (((int64_t)b * T + q) * Hq + h) * DH + 4 * g;
+    // the row index passes through an empty asm so that the epilogue's addresses and loads are formed
+    // here, not hoisted above the K loop where they would hold registers the loop needs
+    int qq = qw + 16 * j + c16;
+    asm volatile("" : "+v"(qq));
+    const int q = min(qq, T - 1);
+    const int64_t n = (int64_t)b * T + q;
+    floatx4 a[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      *reinterpret_cast<float4*>(dqr + 16 * t) =
-          make_float4(dqa[t][j][0] * sc, dqa[t][j][1] * sc, dqa[t][j][2] * sc, dqa[t][j][3] * sc);
+    for (int t = 0; t < 8; ++t) a[t] = dqa[t][j];
+    // dq^ -> dq through the backward of the query's QK-norm and RoPE
+    fa_norm_rope_bwd(a, sc, qraw + n * ldv + (int64_t)h * DH, cs + (int64_t)q * (DH / 2), rq[n * Hq + h],
+                     dq + n * ldv + (int64_t)h * DH, g, qq < T);
   }
 }
 

@@ -1234,14 +1234,46 @@ template <class T> struct EpiSwigluBwd {
 };
 
 // qkv = round(acc); on the v columns (n >= vcol0) of value-embedding layers:
-// v = round(v + table[ids[m], n - vcol0]), nothing added for ids outside [0, rows)
+// v = round(v + table[ids[m], n - vcol0]), nothing added for ids outside [0, rows).
+// With kh set (128-wide heads), the k columns [kcol0, vcol0) also leave normalised and rotated
+// [hn.213312.xyz translation, 设置 / Setup: QK-norm, RoPE]: k^ = RoPE(k / rms(k)) with
+// rms(k) = sqrt(mean(k^2) + eps) over the head, the rotation of channel pairs (i, i + 64) by the
+// angles of position m % seq from cs [seq, 64] (cos, sin); k^ goes to kh [M, vcol0 - kcol0] and
+// 1 / rms(k) to rk [M, heads]. A head's 16 segments are 16 aligned consecutive lanes of one row (every
+// block configuration's N tile is 128 or 256 wide), so the sum of squares is a 16-lane reduction and
+// the partner of channel i is 8 lanes away.
 template <class T> struct EpiQkv {
   static constexpr const char* kName = "qkv";
   static constexpr int kKind = kEpiPlain;
   T* C; int64_t ldc; const T* table; int64_t ldt; const int32_t* ids; int vcol0; int64_t rows;
+  T* kh = nullptr; float* rk = nullptr; const float2* cs = nullptr; int kcol0 = 0; int seq = 1; float eps = 0.f;
   __device__ __forceinline__ void seg(int m, int n, float (&v)[8]) const {
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = Elem<T>::rnd(v[k]);
+    if (kh && n >= kcol0 && n < vcol0) {                    // uniform over the head's 16 lanes
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ss += v[k] * v[k];
+      ss = group_sum<16>(ss);
+      const float r = 1.0f / sqrtf(ss / 128.f + eps);
+      const int c = (n - kcol0) & 127, i0 = c & 63;
+      const bool lo = c < 64;                               // channel i (else i + 64) of pairs i0 ..
+      const float4* c4 = reinterpret_cast<const float4*>(cs + (int64_t)(m % seq) * 64 + i0);
+      float y[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 cc = c4[q];                           // (cos, sin) of pairs i0 + 2q, i0 + 2q + 1
+        const float cv[2] = {cc.x, cc.z}, sv[2] = {cc.y, cc.w};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int k = 2 * q + e;
+          const float own = v[k] * r, oth = dpp_move<0x128>(v[k]) * r;   // row_ror:8, lane ^ 8
+          y[k] = lo ? own * cv[e] - oth * sv[e] : oth * sv[e] + own * cv[e];
+        }
+      }
+      Vec8<T>::store(kh + (int64_t)m * (vcol0 - kcol0) + (n - kcol0), y);
+      if (c == 0) rk[(int64_t)m * ((vcol0 - kcol0) >> 7) + ((n - kcol0) >> 7)] = r;
+    }
     if (table && n >= vcol0) {
       const int32_t id = ids[m];
       if (id >= 0 && id < rows) {

@@ -166,8 +166,11 @@ size_t carve_bwd(void* base, const Dims& d, BwdWs& w) {
     w.dot = c.take<char>(d.B * d.QD * d.Tp * e);
   }
   w.delta = c.take<float>(d.B * d.Hq * d.Tp);
-  w.dqh = c.take<float>(d.N * d.QD);
-  w.dkh = c.take<float>(d.N * d.KVD);
+  w.dqh = w.dkh = nullptr;
+  if (!d.bf) {   // fp32 kernels leave dq^, dk^ for qk_post
+    w.dqh = c.take<float>(d.N * d.QD);
+    w.dkh = c.take<float>(d.N * d.KVD);
+  }
   w.dqkv = c.take<char>(d.N * d.QKVD * e);
   w.dxn = c.take<char>(d.N * d.D * e);
   w.dgp = c.take<float>(rmsnorm_bwd_partials(d.N) * d.D + colsum_scratch_floats(d.D) + 1);
@@ -259,20 +262,31 @@ int layer_fwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
   // attention block
   LL_HIP(launch_rmsnorm_fwd(x, g1, P<T>(sv.xn), sv.r1, N, d.D, d.eps, (float*)nullptr, s));
   {
+    // QK-norm + RoPE on the bf16 path: k^ (shared by every query block of its group) and 1/rms(k)
+    // leave the QKV GEMM's epilogue; the attention forward applies them to q as it loads it (and
+    // saves q^ and 1/rms(q) for the backward)
+    constexpr bool kFused = std::is_same<T, bf16>::value;
     EpiQkv<T> e{P<T>(sv.qkv), d.QKVD, d.ve ? CP<T>(p->ve_table) : nullptr, d.KVD, ids, d.vcol0, d.ve_rows};
+    if (kFused) {
+      e.kh = P<T>(sv.kh);
+      e.rk = sv.rk;
+      e.cs = w.cs;
+      e.kcol0 = d.QD;
+      e.seq = (int)d.T;
+      e.eps = d.eps;
+    }
     LL_HIP(launch_gemm_nt(CP<T>(sv.xn), d.D, CP<T>(p->w_qkv), d.D, (int)N, d.QKVD, d.D, e, s));
   }
   if (N > 0) {
-    // QK-norm + RoPE: the bf16 attention forward applies them to q as it loads it (and saves q^
-    // and 1/rms(q) for the backward); k^, shared by every query block of its group, is formed
-    // once here. The fp32 kernels take both from this pass.
-    constexpr bool kFusedQ = std::is_same<T, bf16>::value;
-    const int h0 = kFusedQ ? d.Hq : 0, hp = kFusedQ ? d.Hkv : d.Hq + d.Hkv;
-    const int64_t threads = N * hp * (DH / 16);   // 8 rotation pairs per lane
-    LL_LAUNCH("qk_prep", (qk_prep_kernel<T, DH>), dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, s, CP<T>(sv.qkv),
-                       (int64_t)d.QKVD, w.cs, P<T>(sv.qh), P<T>(sv.kh), sv.rq, sv.rk, N, (int)d.T, d.Hq, d.Hkv, d.eps,
-                       h0, hp);
-    LL_HIP(hipGetLastError());
+    if constexpr (!std::is_same<T, bf16>::value) {
+      // the fp32 kernels take q^ and k^ from this pass
+      const int hp = d.Hq + d.Hkv;
+      const int64_t threads = N * hp * (DH / 16);   // 8 rotation pairs per lane
+      LL_LAUNCH("qk_prep", (qk_prep_kernel<T, DH>), dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, s,
+                CP<T>(sv.qkv), (int64_t)d.QKVD, w.cs, P<T>(sv.qh), P<T>(sv.kh), sv.rq, sv.rk, N, (int)d.T, d.Hq,
+                d.Hkv, d.eps, 0, hp);
+      LL_HIP(hipGetLastError());
+    }
     const int nqb = (int)cdiv(d.T, 128);
     // algorithmic work, traced as 2 M N K: causal (query, key) pairs x head_dim x 2 products
     const int64_t pairs = d.B * d.Hq * d.T * (d.T + 1) / 2;
@@ -480,11 +494,12 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
       const int nb128 = (int)cdiv(d.T, 128);
       LL_LAUNCH_MNK("attn_bwd_dkdv", pairs, DH, 3, fa_dkdv_kernel, dim3((unsigned)(d.B * d.Hkv * nb128)), dim3(256), 0, s,
                 CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), sv.lse,
-                w.delta, ldl, w.dkh, dqkv + d.vcol0, (int64_t)d.QKVD, (int)d.B, (int)d.T, d.Hq, d.Hkv);
+                w.delta, ldl, CP<T>(sv.qkv) + d.QD, w.cs, sv.rk, dqkv + d.QD, dqkv + d.vcol0, (int64_t)d.QKVD,
+                (int)d.B, (int)d.T, d.Hq, d.Hkv);
       LL_HIP(hipGetLastError());
       LL_LAUNCH_MNK("attn_bwd_dq", pairs, DH, 1, fa_dq_kernel, dim3((unsigned)(d.B * d.Hq * nb128)), dim3(256), 0, s, CP<T>(sv.qh),
                 CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), sv.lse, w.delta, ldl,
-                w.dqh, (int)d.B, (int)d.T, d.Hq, d.Hkv);
+                CP<T>(sv.qkv), w.cs, sv.rq, dqkv, (int)d.B, (int)d.T, d.Hq, d.Hkv);
       LL_HIP(hipGetLastError());
     } else {
       LL_HIP(launch_transpose(CP<T>(sv.qh), d.T, DH, (int64_t)d.QD, P<T>(w.qt), d.Tp, d.Tp, (int)(d.B * d.Hq), d.Hq,
@@ -503,11 +518,13 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
                 CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), CP<T>(w.kt),
                 sv.lse, w.delta, w.dqh, (int)d.B, (int)d.T, (int)d.Tp, d.Hq, d.Hkv);
       LL_HIP(hipGetLastError());
+      // the fp32 kernels leave dq^, dk^ in fp32 (the bf16 ones apply the norm and RoPE backward in
+      // their epilogues)
+      const int64_t pthreads = N * (d.Hq + d.Hkv) * (DH / 16);
+      LL_LAUNCH("qk_post", (qk_post_kernel<T, DH>), dim3((unsigned)cdiv(pthreads, 256)), dim3(256), 0, s, w.dqh,
+                w.dkh, CP<T>(sv.qkv), (int64_t)d.QKVD, w.cs, sv.rq, sv.rk, dqkv, N, (int)d.T, d.Hq, d.Hkv);
+      LL_HIP(hipGetLastError());
     }
-    const int64_t pthreads = N * (d.Hq + d.Hkv) * (DH / 16);
-    LL_LAUNCH("qk_post", (qk_post_kernel<T, DH>), dim3((unsigned)cdiv(pthreads, 256)), dim3(256), 0, s, w.dqh, w.dkh,
-                       CP<T>(sv.qkv), (int64_t)d.QKVD, w.cs, sv.rq, sv.rk, dqkv, N, (int)d.T, d.Hq, d.Hkv);
-    LL_HIP(hipGetLastError());
     if (d.ve) {
       const int64_t tot = N * d.KVD;
       if (!acc) LL_HIP(fill_f32(g->ve_table, 0.f, d.ve_rows * d.KVD, s));   // overwrite: scatter-add from zero
