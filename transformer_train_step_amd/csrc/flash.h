@@ -279,12 +279,12 @@ fa_fwd_kernel(const bf16* __restrict__ qkv, int64_t ldqkv, const float2* __restr
             tmax = fmaxf(tmax, x);
           }
       } else {
+        const int lim = min(q, T - 1) - k0 - 4 * g;   // key k0 + 4 g + 16 i + r visible iff 16 i + r <= lim
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int key = k0 + 16 * i + 4 * g + r;
-            const float x = (key <= q && key < T) ? s[i][j][r] * sl2 : -INFINITY;
+            const float x = 16 * i + r <= lim ? s[i][j][r] * sl2 : -INFINITY;
             s[i][j][r] = x;
             tmax = fmaxf(tmax, x);
           }
@@ -530,12 +530,13 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
   wait_vmcnt<0>();
 
   const float sc = 1.f / sqrtf((float)DH);
+  // the row indices pass through an empty asm so that the epilogue's addresses and loads are formed
+  // here, not hoisted above the query loop where they would hold registers the loop needs
+  int kk2[2] = {kw + c16, kw + 16 + c16};
+  asm volatile("" : "+v"(kk2[0]), "+v"(kk2[1]));
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    // the row index passes through an empty asm so that the epilogue's addresses and loads are formed
-    // here, not hoisted above the query loop where they would hold registers the loop needs
-    int kk = kw + 16 * j + c16;
-    asm volatile("" : "+v"(kk));
+    const int kk = kk2[j];
     const int key = min(kk, T - 1);
     const int64_t n = (int64_t)b * T + key;
     if (kk < T) {
@@ -553,14 +554,16 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
 // Block: one (b, h) and 128 queries, wave w the 32 queries q0 + 32 w .. (Q and dO in registers as
 // `second` operands). Per 64-key tile up to the diagonal: S^T = K Q^T and dP^T = V dO^T (lane:
 // query column, 4 key rows), dS^T = P^T (dP^T - Delta); dQ^T += K^T dS^T with K^T from transpose
-// reads. The epilogue scales dQ^ by 1/sqrt(DH) and takes it through the backward of the queries'
+// reads. Delta = rowsum(dO * O) of the block's queries is formed here from the dO rows the waves
+// hold and the O rows (same layout as dO), used, and written to delta for the dK/dV kernel.
+// The epilogue scales dQ^ by 1/sqrt(DH) and takes it through the backward of the queries'
 // QK-norm and RoPE: qraw (the raw q columns of the QKV projection) and dq (their columns of its
 // gradient) have row stride ldv; cs [T, 64] holds the RoPE (cos, sin), rq [N, Hq] 1 / rms(q).
 __global__ void __launch_bounds__(256, 2)
 fa_dq_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const bf16* __restrict__ v, int64_t ldv,
-             const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta, int64_t ldl,
-             const bf16* __restrict__ qraw, const float2* __restrict__ cs, const float* __restrict__ rq,
-             bf16* __restrict__ dq, int B, int T, int Hq, int Hkv) {
+             const bf16* __restrict__ dO, const bf16* __restrict__ O, const float* __restrict__ lse,
+             float* __restrict__ delta, int64_t ldl, const bf16* __restrict__ qraw, const float2* __restrict__ cs,
+             const float* __restrict__ rq, bf16* __restrict__ dq, int B, int T, int Hq, int Hkv) {
   constexpr int DH = 128, STAGE = 2 * 64 * 256;
   __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE];
@@ -583,7 +586,23 @@ fa_dq_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const bf1
       of[j][c] = *reinterpret_cast<const u32x4*>(dO + off + 32 * c);
     }
     l2[j] = lse[((int64_t)b * Hq + h) * ldl + q] * kFaLog2e;
-    dl[j] = delta[((int64_t)b * Hq + h) * ldl + q];
+    // Delta = rowsum(dO * O) of the query, over the 4 lanes g that hold its row (written for the
+    // dK/dV kernel, which runs after this one)
+    float dsum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float o8[8];
+      Vec8<bf16>::load(O + off + 32 * c, o8);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t u = of[j][c][w];
+        dsum += __uint_as_float(u << 16) * o8[2 * w] + __uint_as_float(u & 0xffff0000u) * o8[2 * w + 1];
+      }
+    }
+    dsum += __shfl_xor(dsum, 16, 64);
+    dsum += __shfl_xor(dsum, 32, 64);
+    dl[j] = dsum;
+    if (g == 0 && qw + 16 * j + c16 < T) delta[((int64_t)b * Hq + h) * ldl + q] = dsum;
   }
   const bf16* kb = kh + ((int64_t)b * T * Hkv + hk) * DH;
   const bf16* vb = v + (int64_t)b * T * ldv + (int64_t)hk * DH;
@@ -614,19 +633,18 @@ fa_dq_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const bf1
         }
       }
     }
-    // (a mask-free branch for the tiles below the diagonal, as in the other two kernels, makes
-    // this one spill inside the loop at 2 waves per SIMD)
+    // key k0 + 4 g + (16 i + r) is visible to query q iff 16 i + r <= min(q, T - 1) - k0 - 4 g: one
+    // compare against a constant per element (a mask-free branch for the tiles below the diagonal,
+    // as in the other two kernels, makes this one spill inside the loop at 2 waves per SIMD)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int q = qw + 16 * j + c16;
+      const int lim = min(qw + 16 * j + c16, T - 1) - k0 - 4 * g;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = k0 + 16 * i + 4 * g + r;
-          const bool ok = key <= q && key < T;
           const float p = __builtin_amdgcn_exp2f(s[i][j][r] * sl2 - l2[j]);
-          dp[i][j][r] = ok ? p * (dp[i][j][r] - dl[j]) : 0.f;
+          dp[i][j][r] = 16 * i + r <= lim ? p * (dp[i][j][r] - dl[j]) : 0.f;
         }
     }
 #pragma unroll
@@ -664,12 +682,13 @@ fa_dq_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const bf1
   wait_vmcnt<0>();
 
   const float sc = 1.f / sqrtf((float)DH);
+  // the row indices pass through an empty asm so that the epilogue's addresses and loads are formed
+  // here, not hoisted above the K loop where they would hold registers the loop needs
+  int qq2[2] = {qw + c16, qw + 16 + c16};
+  asm volatile("" : "+v"(qq2[0]), "+v"(qq2[1]));
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    // the row index passes through an empty asm so that the epilogue's addresses and loads are formed
-    // here, not hoisted above the K loop where they would hold registers the loop needs
-    int qq = qw + 16 * j + c16;
-    asm volatile("" : "+v"(qq));
+    const int qq = qq2[j];
     const int q = min(qq, T - 1);
     const int64_t n = (int64_t)b * T + q;
     floatx4 a[8];

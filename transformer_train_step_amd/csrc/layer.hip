@@ -487,21 +487,22 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
     const int64_t ldl = d.bf ? d.Tp : d.T;   // row stride of lse and delta
     // algorithmic work, traced as 2 M N K: dK/dV holds the dP, dV and dK products, dQ the dQ product
     const int64_t pairs = d.B * d.Hq * d.T * (d.T + 1) / 2;
-    LL_LAUNCH("attn_delta", (attn_delta_kernel<T, DH>), dim3((unsigned)cdiv(dthreads, 256)), dim3(256), 0, s,
-                       CP<T>(w.dout), CP<T>(sv.o), w.delta, ldl, N, (int)d.T, d.Hq);
-    LL_HIP(hipGetLastError());
     if constexpr (std::is_same<T, bf16>::value) {
+      // dQ first: it forms Delta = rowsum(dO * O) from the rows it holds and leaves it for dK/dV
       const int nb128 = (int)cdiv(d.T, 128);
+      LL_LAUNCH_MNK("attn_bwd_dq", pairs, DH, 1, fa_dq_kernel, dim3((unsigned)(d.B * d.Hq * nb128)), dim3(256), 0, s, CP<T>(sv.qh),
+                CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), CP<T>(sv.o), sv.lse, w.delta,
+                ldl, CP<T>(sv.qkv), w.cs, sv.rq, dqkv, (int)d.B, (int)d.T, d.Hq, d.Hkv);
+      LL_HIP(hipGetLastError());
       LL_LAUNCH_MNK("attn_bwd_dkdv", pairs, DH, 3, fa_dkdv_kernel, dim3((unsigned)(d.B * d.Hkv * nb128)), dim3(256), 0, s,
                 CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), sv.lse,
                 w.delta, ldl, CP<T>(sv.qkv) + d.QD, w.cs, sv.rk, dqkv + d.QD, dqkv + d.vcol0, (int64_t)d.QKVD,
                 (int)d.B, (int)d.T, d.Hq, d.Hkv);
       LL_HIP(hipGetLastError());
-      LL_LAUNCH_MNK("attn_bwd_dq", pairs, DH, 1, fa_dq_kernel, dim3((unsigned)(d.B * d.Hq * nb128)), dim3(256), 0, s, CP<T>(sv.qh),
-                CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), sv.lse, w.delta, ldl,
-                CP<T>(sv.qkv), w.cs, sv.rq, dqkv, (int)d.B, (int)d.T, d.Hq, d.Hkv);
-      LL_HIP(hipGetLastError());
     } else {
+      LL_LAUNCH("attn_delta", (attn_delta_kernel<T, DH>), dim3((unsigned)cdiv(dthreads, 256)), dim3(256), 0, s,
+                CP<T>(w.dout), CP<T>(sv.o), w.delta, ldl, N, (int)d.T, d.Hq);
+      LL_HIP(hipGetLastError());
       LL_HIP(launch_transpose(CP<T>(sv.qh), d.T, DH, (int64_t)d.QD, P<T>(w.qt), d.Tp, d.Tp, (int)(d.B * d.Hq), d.Hq,
                               d.T * d.QD, (int64_t)DH, (int64_t)DH * d.Tp, s));
       LL_HIP(launch_transpose(CP<T>(sv.kh), d.T, DH, (int64_t)d.KVD, P<T>(w.kt), d.Tp, d.Tp, (int)(d.B * d.Hkv),
