@@ -37,12 +37,13 @@ __device__ __forceinline__ floatx4 fa_mma(floatx4 acc, u32x4 first, u32x4 second
 }
 
 // Issue the direct loads of rows [r0, r0 + R) of a bf16 matrix with 128-element rows at
-// src + row * ld (rows at or past rmax repeat row rmax - 1) into an LDS tile; the 4 waves of the
+// src + row * ld (rows at or past rmax repeat row rmax - 1) into an LDS tile; the NW waves of the
 // block share the R / 4 one-kilobyte instructions.
-template <int R>
+template <int R, int NW = 4>
 __device__ __forceinline__ void fa_issue(const bf16* src, int64_t ld, int r0, int rmax, unsigned char* lds, int wave,
                                          int lane) {
-  constexpr int PW = R / 16;
+  static_assert(R % (4 * NW) == 0, "whole instructions per wave");
+  constexpr int PW = R / (4 * NW);
   const int phys = lane & 15;
 #pragma unroll
   for (int n = 0; n < PW; ++n) {
@@ -364,8 +365,9 @@ fa_fwd_kernel(const bf16* __restrict__ qkv, int64_t ldqkv, const float2* __restr
 }
 
 // ------------------------------------------------------------------ backward: dK, dV
-// Block: one (b, kv head) and 128 keys, wave w the 32 keys k0 + 32 w .. (K and V rows in registers
-// as `second` operands, dK^T and dV^T accumulators). Loops over the Hq/Hkv query heads of the
+// Block: one (b, kv head) and 128 keys, wave w the KPW keys k0 + KPW w .. (K and V rows in
+// registers as `second` operands, dK^T and dV^T accumulators): KPW = 32 is 4 waves (one per SIMD),
+// KPW = 16 is 8 waves (two per SIMD, each reading the whole query tile from LDS for half the MFMAs). Loops over the Hq/Hkv query heads of the
 // group and the 64-query tiles at or after k0, three stages in flight. Per tile: S = Q K^T and
 // dP = dO V^T (lane: key column, 4 query rows), P = exp2(S log2e / sqrt(DH) - lse log2e),
 // dS = P (dP - Delta); dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from transpose reads.
@@ -374,14 +376,17 @@ fa_fwd_kernel(const bf16* __restrict__ qkv, int64_t ldqkv, const float2* __restr
 // The epilogue writes dV and, through the backward of the keys' QK-norm and RoPE, dK straight into
 // their columns of the QKV-projection gradient: kraw (the raw k columns of the QKV projection), dk
 // and dv all have row stride lddv; cs [T, 64] holds the RoPE (cos, sin), rk [N, Hkv] 1 / rms(k).
-__global__ void __launch_bounds__(256, 1)
+template <int KPW>
+__global__ void __launch_bounds__(64 * (128 / KPW), 1)
 fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const bf16* __restrict__ v, int64_t ldv,
                const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
                int64_t ldl, const bf16* __restrict__ kraw, const float2* __restrict__ cs, const float* __restrict__ rk,
                bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t lddv, int B, int T, int Hq, int Hkv) {
   constexpr int DH = 128;
   constexpr int TILE = 64 * 256, STAGE = 2 * TILE;
-  constexpr int NIW = 4 + 4;                           // direct loads per wave per stage
+  static_assert(KPW == 16 || KPW == 32, "16 or 32 keys per wave");
+  constexpr int NWV = 128 / KPW, JN = KPW / 16;
+  constexpr int NIW = 32 / NWV;                         // direct loads per wave per stage (Q and dO)
   __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st2[STAGE];
@@ -389,12 +394,12 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
   const int kblk = idx / bkv, b = (idx % bkv) / Hkv, hk = idx % Hkv;
   const int G = Hq / Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
-  const int k0 = kblk * 128, kw = k0 + 32 * wave;
+  const int k0 = kblk * 128, kw = k0 + KPW * wave;
   const float sl2 = kFaLog2e / sqrtf((float)DH);
 
-  u32x4 kf[2][4], vf[2][4];
+  u32x4 kf[JN][4], vf[JN][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < JN; ++j) {
     const int key = min(kw + 16 * j + c16, T - 1);
     const bf16* kr = kh + (((int64_t)b * T + key) * Hkv + hk) * DH + 8 * g;
     const bf16* vr = v + ((int64_t)b * T + key) * ldv + (int64_t)hk * DH + 8 * g;
@@ -404,9 +409,9 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
       vf[j][c] = *reinterpret_cast<const u32x4*>(vr + 32 * c);
     }
   }
-  floatx4 dka[2][8], dva[2][8];
+  floatx4 dka[JN][8], dva[JN][8];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < JN; ++j)
 #pragma unroll
     for (int t = 0; t < 8; ++t) dka[j][t] = dva[j][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -416,8 +421,8 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
   auto issue = [&](int it, unsigned char* s) __attribute__((always_inline)) {
     const int hi = it / nq, q0 = (qt0 + it % nq) * 64;
     const int64_t hoff = ((int64_t)b * T * Hq + hk * G + hi) * DH;
-    fa_issue<64>(qh + hoff, ldq, q0, T, s, wave, lane);
-    fa_issue<64>(dO + hoff, ldq, q0, T, s + TILE, wave, lane);
+    fa_issue<64, NWV>(qh + hoff, ldq, q0, T, s, wave, lane);
+    fa_issue<64, NWV>(dO + hoff, ldq, q0, T, s + TILE, wave, lane);
   };
   // lse and delta of query rows 16 i + 4 g + r of tile it live in buffer it % 3 (one buffer per
   // step of the unrolled loop, so no register copies wait on loads in flight)
@@ -437,16 +442,17 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
     const unsigned char* sO = sQ + TILE;
     const bool live = it < niter;
     const int q0 = (qt0 + it % nq) * 64;
-    floatx4 s[2][4], dp[2][4];
+    floatx4 s[JN][4], dp[JN][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s[0][i] = s[1][i] = dp[0][i] = dp[1][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < JN; ++j) s[j][i] = dp[j][i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const u32x4 qa = fa_rfrag(sQ, 16 * i + c16, 4 * c + g);
         const u32x4 oa = fa_rfrag(sO, 16 * i + c16, 4 * c + g);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < JN; ++j) {
           s[j][i] = fa_mma(s[j][i], qa, kf[j][c]);
           dp[j][i] = fa_mma(dp[j][i], oa, vf[j][c]);
         }
@@ -454,12 +460,12 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
     }
     // a query tile wholly at or past the diagonal of this wave's keys, and inside T, needs no mask
     // (wave-uniform: a scalar branch)
-    const bool full = __builtin_amdgcn_readfirstlane((int)(live && q0 >= kw + 31 && q0 + 64 <= T && kw + 32 <= T)) != 0;
+    const bool full = __builtin_amdgcn_readfirstlane((int)(live && q0 >= kw + KPW - 1 && q0 + 64 <= T && kw + KPW <= T)) != 0;
     if (full) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < JN; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float p = __builtin_amdgcn_exp2f(s[j][i][r] * sl2 - l4[i][r] * kFaLog2e);
@@ -470,7 +476,7 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < JN; ++j) {
           const int key = kw + 16 * j + c16;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -485,9 +491,9 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
     }
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
-      u32x4 pp[2], ds[2];
+      u32x4 pp[JN], ds[JN];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < JN; ++j) {
         pp[j] = fa_operand(s[j][2 * pr], s[j][2 * pr + 1]);
         ds[j] = fa_operand(dp[j][2 * pr], dp[j][2 * pr + 1]);
       }
@@ -496,7 +502,7 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
         const u32x4 ot = fa_tfrag(sO, 32 * pr, 16 * t, lane);
         const u32x4 qt = fa_tfrag(sQ, 32 * pr, 16 * t, lane);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < JN; ++j) {
           dva[j][t] = fa_mma(dva[j][t], ot, pp[j]);
           dka[j][t] = fa_mma(dka[j][t], qt, ds[j]);
         }
@@ -532,10 +538,14 @@ fa_dkdv_kernel(const bf16* __restrict__ qh, const bf16* __restrict__ kh, const b
   const float sc = 1.f / sqrtf((float)DH);
   // the row indices pass through an empty asm so that the epilogue's addresses and loads are formed
   // here, not hoisted above the query loop where they would hold registers the loop needs
-  int kk2[2] = {kw + c16, kw + 16 + c16};
-  asm volatile("" : "+v"(kk2[0]), "+v"(kk2[1]));
+  int kk2[JN];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < JN; ++j) {
+    kk2[j] = kw + 16 * j + c16;
+    asm volatile("" : "+v"(kk2[j]));
+  }
+#pragma unroll
+  for (int j = 0; j < JN; ++j) {
     const int kk = kk2[j];
     const int key = min(kk, T - 1);
     const int64_t n = (int64_t)b * T + key;

@@ -494,7 +494,11 @@ int layer_bwd_t(const Dims& d, const ll_layer_params* p, const T* x, const int32
                 CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), CP<T>(sv.o), sv.lse, w.delta,
                 ldl, CP<T>(sv.qkv), w.cs, sv.rq, dqkv, (int)d.B, (int)d.T, d.Hq, d.Hkv);
       LL_HIP(hipGetLastError());
-      LL_LAUNCH_MNK("attn_bwd_dkdv", pairs, DH, 3, fa_dkdv_kernel, dim3((unsigned)(d.B * d.Hkv * nb128)), dim3(256), 0, s,
+      // 16 keys per wave: 8 waves, two per SIMD, so one wave's softmax and LDS reads overlap the
+      // other's MFMAs
+      constexpr int kKpw = 16;
+      LL_LAUNCH_MNK("attn_bwd_dkdv", pairs, DH, 3, fa_dkdv_kernel<kKpw>, dim3((unsigned)(d.B * d.Hkv * nb128)),
+                dim3(64 * (128 / kKpw)), 0, s,
                 CP<T>(sv.qh), CP<T>(sv.kh), CP<T>(sv.qkv) + d.vcol0, (int64_t)d.QKVD, CP<T>(w.dout), sv.lse,
                 w.delta, ldl, CP<T>(sv.qkv) + d.QD, w.cs, sv.rk, dqkv + d.QD, dqkv + d.vcol0, (int64_t)d.QKVD,
                 (int)d.B, (int)d.T, d.Hq, d.Hkv);
