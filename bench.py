@@ -44,11 +44,11 @@ SOURCES = ("transformer_train_step_amd/csrc/gemm.h", "transformer_train_step_amd
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated (valid while the sources
 # hash to sha256_16; otherwise the roofline reports traffic null)
 TRAFFIC = {
-    "gemm_bf16_lce_grads_kk": {"sources": SOURCES, "sha256_16": "0a0081ffcbaa4949", "read_bytes": 1.4392e+10,
-                               "write_bytes": 6.2563e+08,
+    "gemm_bf16_lce_grads_kk": {"sources": SOURCES, "sha256_16": "832ac60ae8291f72", "read_bytes": 1.4504e+10,
+                               "write_bytes": 6.256e+08,
                                "profile": "profiles/gemm_bf16_lce_grads_kk_hbm_bytes_layer_lce_40x1024.md"},
-    "gemm_bf16_lce_logits_kk": {"sources": SOURCES, "sha256_16": "0a0081ffcbaa4949", "read_bytes": 5.9201e+09,
-                                "write_bytes": 1.0539e+09,
+    "gemm_bf16_lce_logits_kk": {"sources": SOURCES, "sha256_16": "832ac60ae8291f72", "read_bytes": 5.897e+09,
+                                "write_bytes": 1.054e+09,
                                 "profile": "profiles/gemm_bf16_lce_logits_kk_hbm_bytes_layer_lce_40x1024.md"},
 }
 
