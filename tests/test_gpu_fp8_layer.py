@@ -144,6 +144,20 @@ def test_fp8_layer_takes_the_production_paths(key):
 
 
 @pytest.mark.parametrize("key", sorted(CASES))
+def test_attention_passes_of_the_bf16_layer(key):
+    """QK-norm + RoPE and Delta = rowsum(dO * O) have no pass of their own on the bf16 path: k^
+    leaves the QKV GEMM's epilogue, q^ is formed in the attention forward's Q load, their backward
+    happens in the dQ and dK/dV epilogues, and the dQ kernel (which forms Delta for dK/dV) runs
+    first. Their parity is that of the layer (test_fp8_layer_vs_oracle)."""
+    need_gpu()
+    _, _, _, _, _, launches = run_case(key)
+    tags = [l[0] for l in launches]
+    assert not {"qk_prep", "qk_post", "attn_delta"} & set(tags), tags
+    assert [t for t in tags if t.startswith("attn")] == ["attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"], tags
+    assert tags.index("gemm_bf16_qkv_kk") < tags.index("attn_fwd")
+
+
+@pytest.mark.parametrize("key", sorted(CASES))
 def test_fp8_layer_vs_oracle(key):
     need_gpu()
     _, inp, gpu, ref, _, _ = run_case(key)
