@@ -40,8 +40,8 @@ __global__ void rope_table_kernel(float2* cs, int T, int half, double theta) {
 // A head vector is handled by DH/16 consecutive lanes, each owning 8 consecutive rotation pairs
 // (i, i + DH/2), i = i0 .. i0 + 7: 16-byte loads and stores, the sum of squares reduced across the
 // head's lanes by DPP. Heads 0..Hq-1 of a token are q heads, Hq..Hq+Hkv-1 k heads; the kernel takes
-// the Hp heads h0 .. h0 + Hp - 1 of every token (all of them, or only the k heads when the
-// attention forward normalises and rotates q itself as it loads it).
+// the Hp heads h0 .. h0 + Hp - 1 of every token (the fp32 path passes all of them; the bf16 path
+// forms k^ in the QKV GEMM's epilogue and q^ in the attention forward's Q load instead).
 template <class T, int DH>
 __global__ void __launch_bounds__(256)
 qk_prep_kernel(const T* __restrict__ qkv, int64_t ldqkv, const float2* __restrict__ cs, T* __restrict__ qh,
@@ -96,7 +96,8 @@ qk_prep_kernel(const T* __restrict__ qkv, int64_t ldqkv, const float2* __restric
 
 // ------------------------------------------------------------------ backward of QK-norm + RoPE
 // dq = r * dqt - q * r^3 * mean(q * dqt) with dqt = RoPE^T(dq^); written into the q/k columns of
-// dqkv. dqh [N, Hq DH] and dkh [N, Hkv DH] are fp32. Lane layout as in the forward.
+// dqkv. dqh [N, Hq DH] and dkh [N, Hkv DH] are fp32. Lane layout as in the forward. (fp32 path; the
+// bf16 dQ and dK/dV kernels apply the same backward in their epilogues.)
 template <class T, int DH>
 __global__ void __launch_bounds__(256)
 qk_post_kernel(const float* __restrict__ dqh, const float* __restrict__ dkh, const T* __restrict__ qkv,
